@@ -1,0 +1,342 @@
+/*
+ * CPU ORACLE for the DeepSeek-V4 C128 compress-store path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the bench's
+ * cpu_baseline leg use it.  It shares no code with the HIP library.
+ *
+ * It is a plain, slow, obviously correct statement of what the path
+ * computes, in fp64, token by token, following the vLLM API page
+ * "fused_compress_quant_cache" (DeepSeek-V4 common ops), kernel
+ * `_fused_kv_compress_norm_rope_insert_sparse_attn` and its two-stage twins
+ * `_compress_gather_split_sparse_attn` / `_finalize_norm_rope_quant_store_sparse_attn`:
+ *
+ *   gate    a token is active iff its state slot is >= 0 and (pos+1) % 128 == 0
+ *   gather  window rows q = pos-127 .. pos, row q at state[bt[req][q / bs]][q % bs]
+ *   pool    c_j = sum_i softmax_i(score_ij) * kv_ij          (per column j < 512)
+ *   norm    n_j = c_j / sqrt(mean_j c_j^2 + eps) * w_j
+ *   quant   dims < 448: bf16 round trip, per-64 absmax (floor 1e-4), UE8M0
+ *           exponent e = ceil(log2(absmax / 448)), e4m3fn codes of x * 2^-e
+ *   rope    dims 448..511: interleaved pairs rotated by the table row of the
+ *           window's first position (pos // 128) * 128, stored as bf16
+ *   insert  kv slot s >= 0: block s / kv_bs, offset s % kv_bs;
+ *           576 data bytes at blk*stride0 + off*576,
+ *           8 scale bytes (7 exponents + a zero pad) at blk*stride0 + kv_bs*576 + off*8
+ *
+ * Readings where the pages leave a point open (each one is listed with its
+ * reason in the design notes of the repository):
+ *   - int32 index arrays; fp32 rms weight and cos/sin table;
+ *   - `.to(bfloat16)` and `.to(float8e4nv)` round to nearest, ties to even;
+ *     float8e4nv is the OCP E4M3FN format (bias 7, max 448, no infinities);
+ *   - the exponent is the exact ceil(log2) of the fp32 product absmax * fl32(1/448);
+ *   - the normalised value is held in fp32 before the bf16 round trip (its
+ *     storage type on the page); RoPE rotates the fp64 normalised value and
+ *     rounds once to bf16;
+ *   - a negative position is inactive;
+ *   - an active token with a negative kv slot writes nothing.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define HEAD 512        /* head size = state width */
+#define NOPE 448        /* FP8 dims */
+#define ROPE 64         /* bf16 RoPE dims */
+#define HALF_ROPE 32
+#define CR 128          /* compress ratio: rows per window */
+#define QBLOCK 64       /* quantisation block */
+#define NQ (NOPE / QBLOCK)
+#define RECORD 576      /* 448 fp8 bytes + 64 bf16 */
+#define SCALE_DIM 8     /* 7 UE8M0 bytes + 1 pad */
+#define FP8_MAX 448.0
+
+/* ------------------------------------------------------------------------
+ * Number formats, from their definitions.
+ * --------------------------------------------------------------------- */
+
+/*
+ * bfloat16 is binary32 with its significand cut to 8 bits (1 implicit + 7
+ * stored) and the same exponent range.  Round x (any finite double) to the
+ * nearest such value, ties to an even last bit: scale by the spacing of
+ * bf16 numbers at x's binade, rint (round-half-even), scale back.  Returns
+ * the 16-bit pattern.  Finite inputs below 2^128 only.
+ */
+uint16_t oracle_bf16_bits(double x) {
+  double a = fabs(x);
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int k;
+    frexp(a, &k);             /* a = f * 2^k, f in [0.5, 1) -> binade 2^(k-1) */
+    int q = k - 1 - 7;        /* spacing of 8-bit significands in that binade */
+    if (q < -133) q = -133;   /* subnormal spacing of binary32 (and of bf16) */
+    r = ldexp(rint(ldexp(a, -q)), q);
+  }
+  float f = (float)r;         /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t h = (uint16_t)(u >> 16);
+  if (signbit(x)) h |= 0x8000u;
+  return h;
+}
+
+double oracle_bf16_value(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/*
+ * OCP 8-bit floating point, E4M3FN: sign, 4 exponent bits (bias 7), 3
+ * mantissa bits; subnormals m * 2^-9; largest finite 0x7E = 1.75 * 2^8 = 448.
+ * Round |x| <= 448 to nearest, ties to the even code.
+ */
+uint8_t oracle_e4m3_code(double x) {
+  double a = fabs(x);
+  uint8_t sign = signbit(x) ? 0x80u : 0x00u;
+  unsigned code;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: value = m * 2^-9, m = 0..7; m = 8 is the smallest normal */
+    code = (unsigned)rint(ldexp(a, 9));
+  } else {
+    int k;
+    frexp(a, &k);
+    int E = k - 1;                                          /* a in [2^E, 2^(E+1)) */
+    double m = rint((ldexp(a, -E) - 1.0) * 8.0);            /* 3-bit mantissa, RNE */
+    if (m == 8.0) { m = 0.0; E += 1; }
+    code = ((unsigned)(E + 7) << 3) | (unsigned)m;
+  }
+  return (uint8_t)(sign | code);
+}
+
+double oracle_e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Exact ceil(log2(r)) for a positive finite r. */
+int oracle_ceil_log2(double r) {
+  int k;
+  double f = frexp(r, &k); /* r = f * 2^k, f in [0.5, 1) */
+  return (f == 0.5) ? k - 1 : k;
+}
+
+/*
+ * UE8M0 exponent of one quantisation block from its absmax (of bf16 values):
+ * absmax is floored at fl32(1e-4), multiplied by fl32(1/448) in fp32, and
+ * e = ceil(log2(that product)).  The product of two fp32 values is exact in
+ * fp64, so one cast to float is the fp32 multiply.
+ */
+int oracle_ue8m0_exponent(double absmax) {
+  double floor_ = (double)(float)1e-4;
+  double A = absmax > floor_ ? absmax : floor_;
+  double inv = (double)(float)(1.0 / FP8_MAX);
+  double raw = (double)(float)(A * inv);
+  return oracle_ceil_log2(raw);
+}
+
+/* ------------------------------------------------------------------------
+ * One token.
+ * --------------------------------------------------------------------- */
+
+typedef struct {
+  const float* state;
+  int64_t n_state_blocks, state_bs, s0, s1;    /* element strides */
+  const int32_t* block_table;
+  int64_t bt_rows, bt_cols, bt_stride;
+  const int32_t* token_to_req;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  int64_t T;
+  const float* rms_w;
+  double eps;
+  const float* cos_sin;
+  int64_t cs_rows, cs_stride;
+  uint8_t* k_cache;
+  int64_t kv_bs, kv_stride0, n_kv_blocks;      /* stride in bytes */
+  const int32_t* kv_slot_mapping;
+  double* out_compressed;  /* [T, 512] or NULL */
+  double* out_absnorm;     /* [T, 512] sum_i p_ij |kv_ij|, or NULL */
+  double* out_normed;      /* [T, 512] fp64 normalised value, or NULL */
+  int32_t* out_status;     /* [T]: 0 inactive, 1 written, 2 active/no write, <0 bad index */
+} oracle_args;
+
+enum { ST_INACTIVE = 0, ST_WRITTEN = 1, ST_NO_SLOT = 2, ST_BAD_INDEX = -1 };
+
+static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn, double* n) {
+  /* gate */
+  int32_t slot = a->slot_mapping[t];
+  int64_t pos = a->positions[t];
+  if (slot < 0 || pos < 0 || (pos + 1) % CR != 0) return ST_INACTIVE;
+
+  int64_t req = a->token_to_req[t];
+  if (req < 0 || req >= a->bt_rows) return ST_BAD_INDEX;
+  int64_t start = pos - CR + 1;
+  if ((pos / a->state_bs) >= a->bt_cols) return ST_BAD_INDEX;
+
+  /* gather: row pointers of the window, in window order */
+  const float* row[CR];
+  for (int i = 0; i < CR; ++i) {
+    int64_t q = start + i;
+    int64_t blk = a->block_table[req * a->bt_stride + q / a->state_bs];
+    if (blk < 0 || blk >= a->n_state_blocks) return ST_BAD_INDEX;
+    row[i] = a->state + blk * a->s0 + (q % a->state_bs) * a->s1;
+  }
+
+  /* pool: softmax over the window rows of each score column, weights applied to kv */
+  for (int j = 0; j < HEAD; ++j) {
+    double M = -INFINITY;
+    for (int i = 0; i < CR; ++i) {
+      double s = row[i][HEAD + j];
+      if (s > M) M = s;
+    }
+    double w[CR], L = 0.0;
+    for (int i = 0; i < CR; ++i) {
+      w[i] = exp((double)row[i][HEAD + j] - M);
+      L += w[i];
+    }
+    double num = 0.0, an = 0.0;
+    for (int i = 0; i < CR; ++i) {
+      double p = w[i] / L;
+      num += p * (double)row[i][j];
+      an += p * fabs((double)row[i][j]);
+    }
+    c[j] = num;
+    absn[j] = an;
+  }
+
+  /* RMSNorm */
+  double ss = 0.0;
+  for (int j = 0; j < HEAD; ++j) ss += c[j] * c[j];
+  double rrms = 1.0 / sqrt(ss / HEAD + a->eps);
+  for (int j = 0; j < HEAD; ++j) n[j] = c[j] * rrms * (double)a->rms_w[j];
+
+  int64_t kv_slot = a->kv_slot_mapping[t];
+  if (kv_slot < 0) return ST_NO_SLOT;
+  int64_t kblk = kv_slot / a->kv_bs, koff = kv_slot % a->kv_bs;
+  if (kblk >= a->n_kv_blocks) return ST_BAD_INDEX;
+  int64_t P = (pos / CR) * CR;
+  if (P >= a->cs_rows) return ST_BAD_INDEX;
+
+  uint8_t* blockp = a->k_cache + kblk * a->kv_stride0;
+  uint8_t* data = blockp + koff * RECORD;
+  uint8_t* scales = blockp + a->kv_bs * RECORD + koff * SCALE_DIM;
+
+  /* quant of the nope dims: bf16 round trip of the fp32 normalised value */
+  double u[NOPE];
+  for (int j = 0; j < NOPE; ++j) u[j] = oracle_bf16_value(oracle_bf16_bits((double)(float)n[j]));
+  for (int g = 0; g < NQ; ++g) {
+    double amax = 0.0;
+    for (int j = g * QBLOCK; j < (g + 1) * QBLOCK; ++j)
+      if (fabs(u[j]) > amax) amax = fabs(u[j]);
+    int e = oracle_ue8m0_exponent(amax);
+    for (int j = g * QBLOCK; j < (g + 1) * QBLOCK; ++j) {
+      double x = ldexp(u[j], -e);
+      if (x > FP8_MAX) x = FP8_MAX;
+      if (x < -FP8_MAX) x = -FP8_MAX;
+      data[j] = oracle_e4m3_code(x);
+    }
+    int byte = e + 127;
+    scales[g] = (uint8_t)(byte < 0 ? 0 : (byte > 255 ? 255 : byte));
+  }
+  scales[NQ] = 0;
+
+  /* RoPE: GPT-J interleaved pairs (448+2m, 449+2m), angle row of the window's first position */
+  const float* cs = a->cos_sin + P * a->cs_stride;
+  for (int m = 0; m < HALF_ROPE; ++m) {
+    double x = n[NOPE + 2 * m], y = n[NOPE + 2 * m + 1];
+    double C = cs[m], S = cs[HALF_ROPE + m];
+    uint16_t hx = oracle_bf16_bits(x * C - y * S);
+    uint16_t hy = oracle_bf16_bits(y * C + x * S);
+    uint8_t* o = data + NOPE + 4 * m; /* little-endian bf16 pairs */
+    o[0] = (uint8_t)(hx & 0xFF);
+    o[1] = (uint8_t)(hx >> 8);
+    o[2] = (uint8_t)(hy & 0xFF);
+    o[3] = (uint8_t)(hy >> 8);
+  }
+  return ST_WRITTEN;
+}
+
+typedef struct {
+  const oracle_args* a;
+  int64_t lo, hi;
+} oracle_job;
+
+static void* oracle_worker(void* p) {
+  const oracle_job* jb = (const oracle_job*)p;
+  const oracle_args* a = jb->a;
+  double c[HEAD], absn[HEAD], n[HEAD];
+  for (int64_t t = jb->lo; t < jb->hi; ++t) {
+    for (int j = 0; j < HEAD; ++j) c[j] = absn[j] = n[j] = NAN;
+    int st = oracle_token(a, t, c, absn, n);
+    if (a->out_status) a->out_status[t] = st;
+    if (st == ST_WRITTEN || st == ST_NO_SLOT) {
+      if (a->out_compressed) memcpy(a->out_compressed + t * HEAD, c, sizeof c);
+      if (a->out_absnorm) memcpy(a->out_absnorm + t * HEAD, absn, sizeof absn);
+      if (a->out_normed) memcpy(a->out_normed + t * HEAD, n, sizeof n);
+    }
+  }
+  return NULL;
+}
+
+/*
+ * Run the oracle over tokens [t_lo, t_hi) with `nthreads` threads.  Tokens
+ * are independent; each thread takes a contiguous range.  The k_cache is
+ * modified in place exactly where the path writes.  Diagnostics arrays (may
+ * be NULL) are [T, 512] fp64, rows of tokens that do not pass the gate are
+ * left untouched.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_c128_compress_store(
+    const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
+    const int32_t* block_table, int64_t bt_rows, int64_t bt_cols, int64_t bt_stride,
+    const int32_t* token_to_req, const int32_t* positions, const int32_t* slot_mapping,
+    int64_t T, const float* rms_w, double eps, const float* cos_sin, int64_t cs_rows,
+    int64_t cs_stride, uint8_t* k_cache, int64_t kv_bs, int64_t kv_stride0, int64_t n_kv_blocks,
+    const int32_t* kv_slot_mapping, double* out_compressed, double* out_absnorm,
+    double* out_normed, int32_t* out_status, int64_t t_lo, int64_t t_hi, int nthreads) {
+  if (!state || !block_table || !token_to_req || !positions || !slot_mapping || !rms_w ||
+      !cos_sin || !k_cache || !kv_slot_mapping || state_bs < 1 || kv_bs < 1 || T < 0 ||
+      t_lo < 0 || t_hi > T || t_lo > t_hi || nthreads < 1)
+    return -1;
+  oracle_args a = {state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
+                   bt_stride, token_to_req, positions, slot_mapping, T, rms_w, eps, cos_sin,
+                   cs_rows, cs_stride, k_cache, kv_bs, kv_stride0, n_kv_blocks, kv_slot_mapping,
+                   out_compressed, out_absnorm, out_normed, out_status};
+  if (nthreads > 256) nthreads = 256;
+  int64_t n = t_hi - t_lo;
+  if (nthreads > n) nthreads = n > 0 ? (int)n : 1;
+  pthread_t th[256];
+  int created[256];
+  oracle_job jobs[256];
+  int64_t per = (n + nthreads - 1) / nthreads;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i].a = &a;
+    jobs[i].lo = t_lo + (int64_t)i * per < t_hi ? t_lo + (int64_t)i * per : t_hi;
+    jobs[i].hi = jobs[i].lo + per < t_hi ? jobs[i].lo + per : t_hi;
+    created[i] = 0;
+    if (jobs[i].lo >= jobs[i].hi) continue;
+    if (nthreads > 1 && pthread_create(&th[i], NULL, oracle_worker, &jobs[i]) == 0)
+      created[i] = 1;
+    else
+      oracle_worker(&jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i)
+    if (created[i]) pthread_join(th[i], NULL);
+  return 0;
+}
+
+/* Array forms of the format helpers, for exhaustive tests. */
+void oracle_bf16_bits_array(const double* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_bits(x[i]);
+}
+void oracle_e4m3_code_array(const double* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_code(x[i]);
+}
+void oracle_ue8m0_exponent_array(const double* absmax, int32_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_ue8m0_exponent(absmax[i]);
+}
