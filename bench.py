@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Throughput of the C128 compress-store path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--sweep PATH] [--no-cpu-baseline]
+
+A step is one call of the fused kernel over the whole batch: 16384 boundary
+tokens (one per request, position 128k-1, k ~ U{1..64}), each gathering 16
+distinct blocks of a 262144-block fp32 state pool (8.59 GB, every block read
+once per call), then RMSNorm, UE8M0/E4M3 quantisation, RoPE and the paged
+insert into a KV-block-size-64 k_cache.  Inputs are resident in HBM before
+timing starts.
+
+Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
+``--sweep PATH`` also writes per-workload JSONL (decode sweep 1..4096 tokens,
+single-token, decode batch, varlen prefill) with warm and cold timings.
+``--mode copy`` times a plain device-to-device copy (streaming reference line
+and the counter-calibration kernel for rocprofv3).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("µs/call + achieved HBM GB/s (% peak) for C128 compress-store at 1..16384 tokens")
+PEAK_GBS = 8000.0  # MI355X HBM3E peak
+# algorithmic bytes per active token: state 128 rows x 4 KiB, 16 block ids, token_to_req +
+# kv slot, one RoPE row of 64 fp32, the 584-byte k_cache record
+ACTIVE_TOKEN_BYTES = 128 * 1024 * 4 + 64 + 8 + 256 + 584
+ANY_TOKEN_BYTES = 8          # positions + slot_mapping, read for every token
+CALL_BYTES = 512 * 4         # rms weight
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c128_cfg4_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc", "c128_kernel.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> int:
+    act = int(wl.active_mask().sum())
+    return act * ACTIVE_TOKEN_BYTES + wl.num_tokens * ANY_TOKEN_BYTES + CALL_BYTES
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_params.h")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_unused=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the launch stream: one pair around the whole timed region and one pair
+    around every launch."""
+
+    def __init__(self, torch, stream, n):
+        self.torch = torch
+        self.stream = stream
+        E = torch.cuda.Event
+        self.begin, self.end = E(enable_timing=True), E(enable_timing=True)
+        self.starts = [E(enable_timing=True) for _ in range(n)]
+        self.stops = [E(enable_timing=True) for _ in range(n)]
+
+    def region_ms(self):
+        return self.begin.elapsed_time(self.end)
+
+    def launch_ms(self):
+        return [a.elapsed_time(b) for a, b in zip(self.starts, self.stops)]
+
+
+def time_calls(torch, stream, calls, steps, warmup, flush=None):
+    """Run ``calls[i % len(calls)]`` warmup + steps times; returns (region ms, per-launch ms)."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream, steps)
+    tm.begin.record(stream)
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        tm.starts[i].record(stream)
+        calls[i % len(calls)]()
+        tm.stops[i].record(stream)
+    tm.end.record(stream)
+    torch.cuda.synchronize()
+    return tm.region_ms(), tm.launch_ms()
+
+
+def main_line(args):
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    import synth
+    from synth.device import DeviceWorkload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    t0 = time.time()
+    wl = synth.config4()
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s")
+    d = DeviceWorkload(wl, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident on {props.name} ({props.multi_processor_count} CUs)")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+
+    def call():
+        c128.compress_store(*d.args(), stream=sid)
+
+    region_ms, per_launch = time_calls(torch, stream, [call], args.steps, args.warmup)
+    nbytes = algorithmic_bytes(wl)
+    ms_per_step = region_ms / args.steps
+    kernel_ms = float(np.mean(per_launch))
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, kernel avg "
+        f"{kernel_ms * 1e3:.1f} us (min {min(per_launch) * 1e3:.1f}, max "
+        f"{max(per_launch) * 1e3:.1f}), {value:.0f} GB/s")
+    traffic = measured_traffic()
+
+    body, guards_ok = d.k_cache_bytes()
+    T = wl.num_tokens
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "C128 compress-store, 16384 boundary tokens (one per request, pos 128k-1, "
+                        "k~U{1..64}), 16 distinct state blocks each from a 262144x[8,1024] fp32 "
+                        "pool (8.59 GB, every block read once per call), KV block size 64",
+            "tokens": T,
+            "active_tokens": int(wl.active_mask().sum()),
+            "algorithmic_bytes_per_call": nbytes,
+            "us_per_call": round(ms_per_step * 1e3, 2),
+            "compressed_tokens_per_s": round(int(wl.active_mask().sum()) / (ms_per_step * 1e-3)),
+            "pct_peak_hbm": round(100.0 * value / PEAK_GBS, 2),
+            "device": props.name,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_avg_us": round(kernel_ms * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not guards_ok:
+        line["error"] = "k_cache guard bands were written"
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, body, nbytes)
+    del d
+    torch.cuda.empty_cache()
+    if args.sweep:
+        sweep(args, args.sweep)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, gpu_body, nbytes):
+    """The oracle on the host cores, on the same resident host inputs; also checks the GPU
+    bytes of this run against it (outside the timer)."""
+    import oracle
+    import synth
+    from oracle.compare import compare
+
+    threads = synth.default_threads()
+    t0 = time.perf_counter()
+    orc = oracle.run(wl, threads)
+    dt = time.perf_counter() - t0
+    act = int(wl.active_mask().sum())
+    rep = compare(wl, gpu_body, orc)
+    log(f"[bench] oracle: {dt:.2f}s on {threads} threads; parity vs GPU: "
+        f"{'ok' if rep.ok() else 'FAIL'} ({rep.summary()})")
+    return {
+        "value": round(nbytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the full workload: all {wl.num_tokens} tokens ({act} active), fp64, "
+                  f"{threads} threads",
+        "seconds": round(dt, 3),
+        "compressed_tokens_per_s": round(act / dt, 1),
+        "parity_vs_gpu": "ok" if rep.ok() else "FAIL",
+    }
+
+
+def sweep(args, path):
+    """Per-workload timings (warm: back-to-back calls rotating over disjoint window sets;
+    cold: a 1 GiB buffer is overwritten before each individually timed call)."""
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    import synth
+    from synth.device import DeviceWorkload
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+
+    def flush():
+        scratch.fill_(1.0)
+
+    out = open(path, "w")
+
+    def measure(name, dws, steps, warm_only=False):
+        calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
+        wl = dws[0].wl
+        nbytes = algorithmic_bytes(wl)
+        reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
+        rec = {"workload": name, "tokens": wl.num_tokens,
+               "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
+               "algorithmic_bytes_per_call": nbytes,
+               "warm_us_median": round(float(np.median(per)) * 1e3, 2),
+               "warm_us_mean": round(float(np.mean(per)) * 1e3, 2)}
+        rec["warm_gbs"] = round(nbytes / (rec["warm_us_median"] * 1e-6) / 1e9, 1)
+        if not warm_only:
+            _, percold = time_calls(torch, stream, calls, min(steps, 50), 2, flush=flush)
+            rec["cold_us_median"] = round(float(np.median(percold)) * 1e3, 2)
+            rec["cold_gbs"] = round(nbytes / (rec["cold_us_median"] * 1e-6) / 1e9, 1)
+        rec["pct_peak_hbm_warm"] = round(100 * rec["warm_gbs"] / PEAK_GBS, 2)
+        out.write(json.dumps(rec) + "\n")
+        out.flush()
+        log(f"[sweep] {json.dumps(rec)}")
+
+    measure("cfg0 single boundary token", [DeviceWorkload(synth.config0(), device=dev)], 1000)
+    measure("cfg1 decode batch T=128", [DeviceWorkload(synth.config1(), device=dev)], 1000)
+    d2 = DeviceWorkload(synth.config2(), device=dev)
+    measure("cfg2 varlen prefill", [d2], 1000)
+    del d2
+    _, pool = synth.config3_pool()
+    pool_dev = None
+    for T in [1 << i for i in range(13)]:
+        n_sets = min(64, 65536 // (16 * T))
+        dws = []
+        for s in range(n_sets):
+            wl = synth.config3(T, state=pool, window_set=s)
+            d = DeviceWorkload(wl, device=dev, state=pool_dev)
+            pool_dev = (d.state_buf, d.state)
+            dws.append(d)
+        measure(f"cfg3 decode sweep T={T}", dws, 1000 if T <= 1024 else 100)
+        del dws
+    out.close()
+
+
+def copy_line(args):
+    """Plain device-to-device copy of 4 GiB: the streaming reference and the calibration
+    kernel for the HBM counters (reads 4 GiB, writes 4 GiB per launch)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 30  # floats
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    reg, per = time_calls(torch, stream, [lambda: dst.copy_(src)], args.steps, args.warmup)
+    ms = float(np.mean(per))
+    nbytes = 2 * 4 * n
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n, "kernel_avg_us": round(ms * 1e3, 2),
+                      "gbs_read_plus_write": round(nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["main", "copy"], default="main")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the C128 compress-store path shards by request "
+              "with no exchange between GPUs, and this build runs on a single MI355X. "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+    if args.mode == "copy":
+        copy_line(args)
+    else:
+        main_line(args)
+
+
+if __name__ == "__main__":
+    main()

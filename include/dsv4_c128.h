@@ -1,0 +1,161 @@
+/*
+ * dsv4_c128.h -- C ABI of the DeepSeek-V4 C128 compress-store path on
+ * MI355X (gfx950).
+ *
+ * What it computes (vLLM API page "fused_compress_quant_cache", DeepSeek-V4
+ * common ops: the sparse-attention fused kernel
+ * `_fused_kv_compress_norm_rope_insert_sparse_attn` and its launcher
+ * `compress_norm_rope_store_triton`; vLLM PR 44230 "optimize the compressor
+ * 128 split cutedsl kernel", sections Summary and Changes, for the C128 layout
+ * limits and the wrapper-side validation):
+ *
+ *   For every token t whose state slot is >= 0 and whose position closes a
+ *   128-row window ((pos+1) % 128 == 0):
+ *     1. gather the window's 128 state rows q = pos-127 .. pos, row q at
+ *        state_cache[block_table[token_to_req[t]][q / 8]][q % 8];
+ *        a row is kv[0:512] followed by score[512:1024] (fp32);
+ *     2. compressed[j] = sum_i softmax_i(score[i][j]) * kv[i][j], j < 512;
+ *     3. RMSNorm: n = compressed / sqrt(mean(compressed^2) + eps) * rms_w;
+ *     4. dims 0..447: round n to bf16, split into 7 blocks of 64, block
+ *        exponent e = ceil(log2(max(absmax, 1e-4) / 448)), codes =
+ *        E4M3FN(n * 2^-e) (OCP FP8, max 448), scale byte e + 127;
+ *     5. dims 448..511: rotate interleaved pairs (448+2m, 449+2m), m < 32, by
+ *        cos_sin[(pos / 128) * 128][m] (cos) and [32 + m] (sin); store bf16;
+ *     6. if kv_slot_mapping[t] >= 0: with bs = k_cache.shape[1],
+ *        blk = slot / bs, off = slot % bs, write the 576-byte record
+ *        (448 codes, then 64 little-endian bf16) at byte
+ *        blk*k_cache.stride[0] + off*576 and the 8 scale bytes (7 exponent
+ *        bytes, then a zero pad byte) at blk*k_cache.stride[0] + bs*576 + off*8.
+ *   Every other byte of k_cache stays unchanged.
+ *
+ * Tensor views.  Each argument is a dsv4_tensor: a caller-owned pointer, a
+ * dtype code, a rank and shape/stride arrays.  Strides are in ELEMENTS.
+ * For the compute entry points every `data` pointer is device memory of the
+ * current HIP device; the library never allocates, frees or keeps a pointer
+ * after the call returns.  k_cache is written in place; every other tensor
+ * is only read.
+ *
+ *   state_cache     f32 [S, 8, 1024]   stride[2] == 1, stride[1] >= 1024,
+ *                                      stride[0] >= 8 * stride[1]; data and
+ *                                      both strides 16-byte aligned
+ *   block_table     i32 [R, M]         stride[1] == 1, M >= 16
+ *   token_to_req    i32 [T]            contiguous
+ *   positions       i32 [T]            contiguous
+ *   slot_mapping    i32 [T]            contiguous; only its sign is used
+ *   rms_w           f32 [512]          contiguous, 16-byte aligned
+ *   cos_sin         f32 [P, >= 64]     stride[1] == 1; cos in [0,32), sin in [32,64)
+ *   k_cache         u8  [B, bs, 584]   stride[2] == 1, stride[1] == 584,
+ *                                      stride[0] >= bs*584 and a multiple of
+ *                                      16; data 16-byte aligned.  Only bs and
+ *                                      stride[0] give the layout: the view is a
+ *                                      byte container for the block format above
+ *   kv_slot_mapping i32 [T]            contiguous
+ *
+ * Calls are stream-ordered and asynchronous: no host synchronisation and no
+ * device-to-host reads.  T == 0 is a valid no-op.
+ *
+ * Errors.  Entry points return DSV4_OK (0) or a negative DSV4_ERR_* code.  On
+ * any validation error nothing is launched and k_cache is untouched;
+ * dsv4_last_error() then holds a message (per calling thread).
+ *
+ * Values that live in device memory are not validated by the host (that
+ * would need a synchronisation): block ids, request ids, window columns,
+ * RoPE rows and kv slots.  The kernel range-checks each of them and a token
+ * with any out-of-range index writes nothing.  Two active tokens with the
+ * same kv slot race (the pages leave this undefined too).
+ */
+#ifndef DSV4_C128_H
+#define DSV4_C128_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSV4_ABI_VERSION 1
+
+enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
+
+enum dsv4_status {
+  DSV4_OK = 0,
+  DSV4_ERR_NULL = -1,   /* a required pointer is NULL */
+  DSV4_ERR_DTYPE = -2,  /* wrong dtype code */
+  DSV4_ERR_RANK = -3,   /* wrong number of dimensions */
+  DSV4_ERR_SHAPE = -4,  /* state block != 8, state row != 1024 (head 512 + score 512),
+                           k_cache row != 584, rms_w != 512, cos_sin < 64 columns,
+                           block table < 16 columns, token arrays of different length,
+                           or a size above INT32_MAX */
+  DSV4_ERR_STRIDE = -5, /* inner stride != 1, overlapping rows/blocks, k_cache stride[0]
+                           below bs*584 */
+  DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the 16-byte alignment above */
+  DSV4_ERR_LAUNCH = -7  /* the HIP runtime reported an error at launch */
+};
+
+typedef struct dsv4_tensor {
+  void* data;        /* first element */
+  int32_t dtype;     /* enum dsv4_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4]; /* in elements */
+} dsv4_tensor;
+
+/*
+ * The fused compress-store (steps 1-6 above) for all T tokens, launched on
+ * `stream` (a hipStream_t; NULL means the default stream).
+ * `eps` is the RMSNorm epsilon.
+ */
+int dsv4_c128_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                             const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                             const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                             const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                             const dsv4_tensor* kv_slot_mapping, void* stream);
+
+/*
+ * Same as dsv4_c128_compress_store, and also stores the fp32 `compressed`
+ * vector (step 2) of each token that passes the gate to
+ * compressed_out[t * 512 + j] (device memory, [T, 512] row-major, 16-byte
+ * aligned).  Rows of tokens that do not pass the gate are left unchanged.
+ * For tests; the k_cache bytes are identical to the plain entry point's.
+ */
+int dsv4_c128_compress_store_debug(const dsv4_tensor* state_cache,
+                                   const dsv4_tensor* block_table,
+                                   const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                   const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                   float eps, const dsv4_tensor* cos_sin,
+                                   const dsv4_tensor* k_cache,
+                                   const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                   void* stream);
+
+/*
+ * Host-only validation of the descriptors, exactly as the compute entry
+ * points do it.  Makes no HIP call and dereferences no `data` pointer, so it
+ * runs without a GPU.  Returns DSV4_OK or the DSV4_ERR_* the compute entry
+ * point would return.
+ */
+int dsv4_c128_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                       const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                       const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                       const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                       const dsv4_tensor* kv_slot_mapping);
+
+/*
+ * The E4M3FN encoder of step 4 as the kernel runs it (clamp to [-448, 448],
+ * then round to nearest even), applied to n fp32 values: out[i] =
+ * code(in[i]).  Device pointers, no alignment needed beyond 4 bytes for
+ * `in`.  For exhaustive tests of the hardware conversion (OCP FP8 E4M3FN on
+ * gfx950).
+ */
+int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* dsv4_last_error(void);
+
+/* DSV4_ABI_VERSION of the loaded library. */
+int dsv4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV4_C128_H */

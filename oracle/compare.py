@@ -1,0 +1,183 @@
+"""Parity check of a k_cache produced by the HIP path against the oracle.
+
+Test infrastructure (see ``oracle/__init__.py``).  Pass criteria:
+
+* every byte outside the records of written tokens is unchanged (bit-exact);
+* UE8M0 scale bytes bit-exact, the pad byte 0 -- except a quantisation block
+  whose fp64 absmax lies within rel 1e-5 of a bf16 rounding midpoint
+  1.75390625 * 2^k ("knife edge"): there fp32 rounding may legitimately move
+  bf16(absmax) across the power-of-two boundary of absmax/448, so the block is
+  excused, counted, and compared by dequantised value instead;
+* E4M3 codes within 1 code step (ordinal distance, +0 == -0), on at most 0.1%
+  of the compared nope elements;
+* RoPE bf16 within 1 ulp (ordinal distance, +0 == -0);
+* debug fp32 compressed vector: |gpu - oracle| <= 1e-5 * sum_i p_ij |kv_ij|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+RECORD = 576
+SCALE = 8
+SLOT = 584
+KNIFE = 1.75390625
+KNIFE_REL = 1e-5
+CODE_FRAC_MAX = 1e-3
+COMPRESSED_REL = 1e-5
+
+
+def record_offsets(slot: int, bs: int, stride0: int):
+    blk, off = slot // bs, slot % bs
+    rec = blk * stride0 + off * RECORD
+    scl = blk * stride0 + bs * RECORD + off * SCALE
+    return rec, scl
+
+
+def written_byte_mask(total: int, slots, bs: int, stride0: int) -> np.ndarray:
+    m = np.zeros(total, dtype=bool)
+    for s in slots:
+        rec, scl = record_offsets(int(s), bs, stride0)
+        m[rec:rec + RECORD] = True
+        m[scl:scl + SCALE] = True
+    return m
+
+
+def e4m3_ord(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_val(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(c & 0x80, -v, v)
+
+
+def bf16_ord(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def knife_edge(absmax: float) -> bool:
+    if absmax <= 0:
+        return False
+    k = np.floor(np.log2(absmax / KNIFE))
+    for kk in (k - 1, k, k + 1):
+        edge = KNIFE * 2.0 ** kk
+        if abs(absmax - edge) <= KNIFE_REL * edge:
+            return True
+    return False
+
+
+class Report(dict):
+    def ok(self) -> bool:
+        return not self["failures"]
+
+    def summary(self) -> str:
+        keys = ["tokens", "written", "untouched_mismatch", "scale_mismatch", "excused_blocks",
+                "code_diff1", "code_diff1_frac", "code_fail", "rope_max_ulp", "compressed_max_ratio",
+                "compressed_max_rel"]
+        return ", ".join(f"{k}={self.get(k)}" for k in keys) + (
+            "" if self.ok() else f"; FAIL: {self['failures'][:5]}")
+
+
+def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
+            initial_kc_base: np.ndarray | None = None) -> Report:
+    """Compare the GPU k_cache bytes (the whole underlying buffer of the workload's
+    k_cache view) with the oracle's, on ``tokens`` (indices; default all) and check
+    that every byte outside the written records equals the initial buffer."""
+    kc = wl.k_cache
+    bs = kc.shape[1]
+    stride0 = kc.strides[0]
+    init = wl.k_cache_base if initial_kc_base is None else initial_kc_base
+    assert gpu_kc_base.shape == init.shape
+    T = wl.num_tokens
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    written = wl.written_mask()
+    rep = Report(tokens=int(len(toks)), failures=[])
+
+    # 1. untouched bytes (all tokens, from the workload alone)
+    wmask = written_byte_mask(init.size, wl.kv_slot_mapping[written], bs, stride0)
+    diff = (gpu_kc_base != init) & ~wmask
+    rep["untouched_mismatch"] = int(diff.sum())
+    if rep["untouched_mismatch"]:
+        rep["failures"].append(f"{rep['untouched_mismatch']} bytes outside written records changed")
+
+    # 2-4. records of the compared written tokens
+    n_code = n_diff1 = n_scale_bad = n_excused = 0
+    rope_max = 0
+    for t in toks:
+        t = int(t)
+        if not written[t]:
+            continue
+        rec, scl = record_offsets(int(wl.kv_slot_mapping[t]), bs, stride0)
+        g_codes = gpu_kc_base[rec:rec + 448]
+        o_codes = orc.k_cache_base[rec:rec + 448]
+        g_rope = gpu_kc_base[rec + 448:rec + RECORD].view("<u2")
+        o_rope = orc.k_cache_base[rec + 448:rec + RECORD].view("<u2")
+        g_sc = gpu_kc_base[scl:scl + SCALE]
+        o_sc = orc.k_cache_base[scl:scl + SCALE]
+        if g_sc[7] != 0 or o_sc[7] != 0:
+            rep["failures"].append(f"token {t}: pad byte not zero")
+        n64 = orc.normed[t] if orc.normed is not None else None
+        for g in range(7):
+            gc, oc = g_codes[64 * g:64 * (g + 1)], o_codes[64 * g:64 * (g + 1)]
+            n_code += 64
+            if g_sc[g] != o_sc[g]:
+                amax = float(np.abs(n64[64 * g:64 * (g + 1)]).max()) if n64 is not None else 0.0
+                if knife_edge(amax):
+                    n_excused += 1
+                    gv = e4m3_val(gc) * 2.0 ** (int(g_sc[g]) - 127)
+                    ov = e4m3_val(oc) * 2.0 ** (int(o_sc[g]) - 127)
+                    step = 2.0 ** (max(int(g_sc[g]), int(o_sc[g])) - 127 + 8 - 3)
+                    if np.any(np.abs(gv - ov) > step):
+                        rep["failures"].append(f"token {t} block {g}: excused block values differ")
+                    continue
+                n_scale_bad += 1
+                rep["failures"].append(
+                    f"token {t} block {g}: scale byte {int(g_sc[g])} != {int(o_sc[g])}")
+                continue
+            d = np.abs(e4m3_ord(gc) - e4m3_ord(oc))
+            n_diff1 += int((d == 1).sum())
+            if np.any(d > 1):
+                rep["failures"].append(f"token {t} block {g}: code differs by {int(d.max())}")
+        rd = np.abs(bf16_ord(g_rope) - bf16_ord(o_rope))
+        rope_max = max(rope_max, int(rd.max()))
+    rep["written"] = int(written[toks].sum())
+    rep["scale_mismatch"] = n_scale_bad
+    rep["excused_blocks"] = n_excused
+    rep["code_diff1"] = n_diff1
+    rep["code_diff1_frac"] = (n_diff1 / n_code) if n_code else 0.0
+    rep["code_fail"] = rep["code_diff1_frac"] > CODE_FRAC_MAX
+    if rep["code_fail"]:
+        rep["failures"].append(f"code diff-1 fraction {rep['code_diff1_frac']:.2e} > 1e-3")
+    rep["rope_max_ulp"] = rope_max
+    if rope_max > 1:
+        rep["failures"].append(f"rope differs by {rope_max} bf16 ulp")
+
+    # 5. compressed fp32 (debug export)
+    if gpu_compressed is not None and orc.compressed is not None:
+        act = wl.active_mask()
+        worst = 0.0
+        worst_rel = 0.0
+        for t in toks:
+            t = int(t)
+            if not act[t] or not np.isfinite(orc.compressed[t]).all():
+                continue
+            g = gpu_compressed[t].astype(np.float64)
+            o = orc.compressed[t]
+            ratio = np.abs(g - o) / np.maximum(orc.absnorm[t], 1e-300)
+            worst = max(worst, float(ratio.max()))
+            big = np.abs(o) > 1e-3 * np.abs(o).max()
+            if big.any():
+                worst_rel = max(worst_rel, float((np.abs(g - o)[big] / np.abs(o[big])).max()))
+        rep["compressed_max_ratio"] = worst
+        rep["compressed_max_rel"] = worst_rel
+        if worst > COMPRESSED_REL:
+            rep["failures"].append(f"compressed error {worst:.3e} > 1e-5 of sum p|kv|")
+    return rep

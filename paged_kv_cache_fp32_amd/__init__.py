@@ -1,0 +1,187 @@
+"""MI355X (gfx950) C128 compress-store for the DeepSeek-V4 sparse-attention compressor.
+
+Thin ctypes binding of ``libdsv4_c128.so`` (C ABI in ``include/dsv4_c128.h``).
+The binding only marshals torch tensors into descriptors and passes torch's
+current HIP stream; every step of the computation runs in the HIP kernel.
+Loading fails loudly when the library is missing -- there is no fallback.
+
+    import paged_kv_cache_fp32_amd as c128
+    c128.compress_store(state_cache, block_table, token_to_req, positions,
+                        slot_mapping, rms_w, eps, cos_sin, k_cache, kv_slot_mapping)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libdsv4_c128.so")
+
+DSV4_F32, DSV4_I32, DSV4_U8 = 1, 2, 3
+DSV4_OK = 0
+ERRORS = {
+    -1: "DSV4_ERR_NULL",
+    -2: "DSV4_ERR_DTYPE",
+    -3: "DSV4_ERR_RANK",
+    -4: "DSV4_ERR_SHAPE",
+    -5: "DSV4_ERR_STRIDE",
+    -6: "DSV4_ERR_ALIGN",
+    -7: "DSV4_ERR_LAUNCH",
+}
+_DTYPES = {torch.float32: DSV4_F32, torch.int32: DSV4_I32, torch.uint8: DSV4_U8}
+
+
+class Dsv4Error(RuntimeError):
+    """A call into the library returned a negative status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+class Tensor(ctypes.Structure):
+    """dsv4_tensor: pointer, dtype code, rank, shape and strides in elements."""
+
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+def describe(t: torch.Tensor) -> Tensor:
+    """Descriptor of a torch tensor (any device; the library never reads host data)."""
+    d = Tensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = _DTYPES.get(t.dtype, 0)
+    d.ndim = t.dim()
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+_lib = None
+
+
+def library():
+    """The loaded ``libdsv4_c128.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise ImportError(
+                f"{LIBRARY_PATH} is missing: build it with "
+                "`python -m paged_kv_cache_fp32_amd.build` (there is no fallback path)")
+        lib = ctypes.CDLL(LIBRARY_PATH)
+        P = ctypes.POINTER(Tensor)
+        args10 = [P, P, P, P, P, P, ctypes.c_float, P, P, P]
+        lib.dsv4_c128_compress_store.argtypes = args10 + [ctypes.c_void_p]
+        lib.dsv4_c128_compress_store.restype = ctypes.c_int
+        lib.dsv4_c128_compress_store_debug.argtypes = args10 + [ctypes.c_void_p, ctypes.c_void_p]
+        lib.dsv4_c128_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_c128_validate.argtypes = args10
+        lib.dsv4_c128_validate.restype = ctypes.c_int
+        lib.dsv4_e4m3_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p]
+        lib.dsv4_e4m3_encode.restype = ctypes.c_int
+        lib.dsv4_last_error.argtypes = []
+        lib.dsv4_last_error.restype = ctypes.c_char_p
+        lib.dsv4_abi_version.argtypes = []
+        lib.dsv4_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().dsv4_last_error().decode()
+
+
+def abi_version() -> int:
+    return library().dsv4_abi_version()
+
+
+def _check(rc: int):
+    if rc != DSV4_OK:
+        raise Dsv4Error(rc, last_error())
+
+
+def _descriptors(tensors):
+    descs = [describe(t) for t in tensors]
+    return descs, [ctypes.byref(d) for d in descs]
+
+
+def _require_cuda(tensors):
+    dev = None
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("compress_store needs device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def compress_store(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                   cos_sin, k_cache, kv_slot_mapping, stream: int | None = None) -> None:
+    """Fused C128 compress -> RMSNorm -> FP8/UE8M0 quant -> RoPE -> paged insert (in place
+    on ``k_cache``), enqueued on ``stream`` (default: torch's current stream)."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping)
+    dev = _require_cuda(ts)
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    _check(library().dsv4_c128_compress_store(*refs[:6], float(eps), *refs[6:], s))
+
+
+def compress_store_debug(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                         eps, cos_sin, k_cache, kv_slot_mapping, compressed_out,
+                         stream: int | None = None) -> None:
+    """``compress_store`` that also writes the fp32 pooled vector of each token passing the
+    gate into ``compressed_out`` ([T, 512] fp32, contiguous, on the device)."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping, compressed_out)
+    dev = _require_cuda(ts)
+    if compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or \
+            tuple(compressed_out.shape) != (positions.shape[0], 512):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    _, refs = _descriptors(ts[:-1])
+    s = _stream(dev) if stream is None else stream
+    _check(library().dsv4_c128_compress_store_debug(*refs[:6], float(eps), *refs[6:],
+                                                    compressed_out.data_ptr(), s))
+
+
+def validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+             cos_sin, k_cache, kv_slot_mapping) -> int:
+    """Host-only validation of the descriptors (no HIP call); returns the status code."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping)
+    _, refs = _descriptors(ts)
+    return library().dsv4_c128_validate(*refs[:6], float(eps), *refs[6:])
+
+
+def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
+    """The kernel's E4M3FN encoder (clamp to +-448, round to nearest even) on a float32
+    device tensor; returns the uint8 codes."""
+    if x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a float32 device tensor")
+    x = x.contiguous()
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = _stream(x.device) if stream is None else stream
+    _check(library().dsv4_e4m3_encode(x.data_ptr(), out.data_ptr(), x.numel(), s))
+    return out
+
+
+__all__ = ["compress_store", "compress_store_debug", "validate", "e4m3_encode", "last_error",
+           "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

@@ -1,0 +1,241 @@
+// C ABI of the C128 compress-store library: descriptor validation (host
+// only), launch, error codes and the per-thread error message.  The contract
+// is documented in include/dsv4_c128.h.
+//
+// The validation mirrors the layout limits of the DeepSeek-V4 C128 path
+// (vLLM PR 44230, "Summary" and "Changes": head 512, state width 512,
+// compress ratio 128, state block 8, KV block size taken from
+// k_cache.shape[1]; the wrapper rejects unsupported layouts up front) and
+// the argument list of the page's launcher `compress_norm_rope_store_triton`
+// (block table row stride, cos/sin row stride, k_cache.stride(0) as the
+// block stride in bytes).
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "c128_params.h"
+#include "dsv4_c128.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_tensor(const dsv4_tensor* t, const char* name, int dtype, int ndim) {
+  if (!t) return fail(DSV4_ERR_NULL, "%s: descriptor is NULL", name);
+  if (t->ndim != ndim)
+    return fail(DSV4_ERR_RANK, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
+  if (t->dtype != dtype)
+    return fail(DSV4_ERR_DTYPE, "%s: wrong dtype code %d (expected %d)", name, t->dtype, dtype);
+  for (int d = 0; d < ndim; ++d) {
+    if (t->shape[d] < 0 || t->shape[d] > kI32Max)
+      return fail(DSV4_ERR_SHAPE, "%s: shape[%d] = %lld out of range", name, d,
+                  static_cast<long long>(t->shape[d]));
+  }
+  int64_t numel = 1;
+  for (int d = 0; d < ndim; ++d) numel *= t->shape[d];
+  if (numel > 0 && !t->data) return fail(DSV4_ERR_NULL, "%s: data pointer is NULL", name);
+  return DSV4_OK;
+}
+
+int check_token_array(const dsv4_tensor* t, const char* name, int64_t T) {
+  int rc = check_tensor(t, name, DSV4_I32, 1);
+  if (rc) return rc;
+  if (t->shape[0] != T)
+    return fail(DSV4_ERR_SHAPE, "%s: length %lld differs from positions (%lld)", name,
+                static_cast<long long>(t->shape[0]), static_cast<long long>(T));
+  if (T > 1 && t->stride[0] != 1)
+    return fail(DSV4_ERR_STRIDE, "%s: must be contiguous (stride %lld)", name,
+                static_cast<long long>(t->stride[0]));
+  return DSV4_OK;
+}
+
+int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_tensor* t2r,
+                 const dsv4_tensor* pos, const dsv4_tensor* slot, const dsv4_tensor* w, float eps,
+                 const dsv4_tensor* cs, const dsv4_tensor* kc, const dsv4_tensor* kvs,
+                 dsv4::C128Params* out) {
+  using namespace dsv4;
+  int rc;
+  // positions defines T; every other token array must match it
+  if ((rc = check_tensor(pos, "positions", DSV4_I32, 1))) return rc;
+  const int64_t T = pos->shape[0];
+  if ((rc = check_token_array(pos, "positions", T))) return rc;
+  if ((rc = check_token_array(t2r, "token_to_req", T))) return rc;
+  if ((rc = check_token_array(slot, "slot_mapping", T))) return rc;
+  if ((rc = check_token_array(kvs, "kv_slot_mapping", T))) return rc;
+
+  // state cache f32 [S, 8, 1024]
+  if ((rc = check_tensor(state, "state_cache", DSV4_F32, 3))) return rc;
+  if (state->shape[1] != kStateBlock)
+    return fail(DSV4_ERR_SHAPE, "state_cache: block size %lld, the C128 path needs 8",
+                static_cast<long long>(state->shape[1]));
+  if (state->shape[2] != kRowFloats)
+    return fail(DSV4_ERR_SHAPE,
+                "state_cache: row of %lld floats, the C128 path needs 1024 (kv 512 | score 512)",
+                static_cast<long long>(state->shape[2]));
+  if (state->stride[2] != 1) return fail(DSV4_ERR_STRIDE, "state_cache: stride[2] must be 1");
+  if (state->stride[1] < kRowFloats)
+    return fail(DSV4_ERR_STRIDE, "state_cache: stride[1] = %lld < 1024 (rows overlap)",
+                static_cast<long long>(state->stride[1]));
+  if (state->stride[0] < kStateBlock * state->stride[1])
+    return fail(DSV4_ERR_STRIDE, "state_cache: stride[0] = %lld < 8 * stride[1] (blocks overlap)",
+                static_cast<long long>(state->stride[0]));
+  if (!aligned16(state->data) || (state->stride[1] & 3) || (state->stride[0] & 3))
+    return fail(DSV4_ERR_ALIGN, "state_cache: data and strides must be 16-byte aligned");
+
+  // block table i32 [R, M]
+  if ((rc = check_tensor(bt, "block_table", DSV4_I32, 2))) return rc;
+  if (bt->shape[1] < kWindowBlocks)
+    return fail(DSV4_ERR_SHAPE, "block_table: %lld columns, a C128 window needs 16",
+                static_cast<long long>(bt->shape[1]));
+  if (bt->stride[1] != 1) return fail(DSV4_ERR_STRIDE, "block_table: stride[1] must be 1");
+  if (bt->shape[0] > 1 && bt->stride[0] < bt->shape[1])
+    return fail(DSV4_ERR_STRIDE, "block_table: stride[0] < shape[1] (rows overlap)");
+
+  // rms weight f32 [512]
+  if ((rc = check_tensor(w, "rms_w", DSV4_F32, 1))) return rc;
+  if (w->shape[0] != kHead)
+    return fail(DSV4_ERR_SHAPE, "rms_w: %lld entries, head size is 512",
+                static_cast<long long>(w->shape[0]));
+  if (w->stride[0] != 1) return fail(DSV4_ERR_STRIDE, "rms_w: must be contiguous");
+  if (!aligned16(w->data)) return fail(DSV4_ERR_ALIGN, "rms_w: data must be 16-byte aligned");
+  if (!(eps >= 0.0f) || eps != eps)
+    return fail(DSV4_ERR_SHAPE, "eps must be a non-negative number");
+
+  // cos/sin f32 [P, >=64]
+  if ((rc = check_tensor(cs, "cos_sin", DSV4_F32, 2))) return rc;
+  if (cs->shape[1] < kRope)
+    return fail(DSV4_ERR_SHAPE, "cos_sin: %lld columns, RoPE needs 64 (cos 32 | sin 32)",
+                static_cast<long long>(cs->shape[1]));
+  if (cs->stride[1] != 1) return fail(DSV4_ERR_STRIDE, "cos_sin: stride[1] must be 1");
+  if (cs->shape[0] > 1 && cs->stride[0] < cs->shape[1])
+    return fail(DSV4_ERR_STRIDE, "cos_sin: stride[0] < shape[1] (rows overlap)");
+
+  // k_cache u8 [B, bs, 584]
+  if ((rc = check_tensor(kc, "k_cache", DSV4_U8, 3))) return rc;
+  if (kc->shape[2] != kSlotBytes)
+    return fail(DSV4_ERR_SHAPE, "k_cache: last dimension %lld, the sparse-attention layout "
+                "needs 584 bytes per token (576 data + 8 scale)",
+                static_cast<long long>(kc->shape[2]));
+  if (kc->shape[1] < 1) return fail(DSV4_ERR_SHAPE, "k_cache: block size must be >= 1");
+  if (kc->stride[2] != 1 || kc->stride[1] != kSlotBytes)
+    return fail(DSV4_ERR_STRIDE, "k_cache: stride[2] must be 1 and stride[1] 584");
+  if (kc->stride[0] < kc->shape[1] * kSlotBytes)
+    return fail(DSV4_ERR_STRIDE, "k_cache: stride[0] = %lld < bs*584 = %lld",
+                static_cast<long long>(kc->stride[0]),
+                static_cast<long long>(kc->shape[1] * kSlotBytes));
+  if (!aligned16(kc->data) || (kc->stride[0] & 15))
+    return fail(DSV4_ERR_ALIGN, "k_cache: data and stride[0] must be 16-byte aligned");
+
+  if (out) {
+    out->state = static_cast<const float*>(state->data);
+    out->s0 = state->stride[0];
+    out->s1 = state->stride[1];
+    out->n_state_blocks = static_cast<int32_t>(state->shape[0]);
+    out->block_table = static_cast<const int32_t*>(bt->data);
+    out->bt_stride = bt->stride[0];
+    out->bt_rows = static_cast<int32_t>(bt->shape[0]);
+    out->bt_cols = static_cast<int32_t>(bt->shape[1]);
+    out->token_to_req = static_cast<const int32_t*>(t2r->data);
+    out->positions = static_cast<const int32_t*>(pos->data);
+    out->slot_mapping = static_cast<const int32_t*>(slot->data);
+    out->num_tokens = static_cast<int32_t>(T);
+    out->rms_w = static_cast<const float*>(w->data);
+    out->eps = eps;
+    out->cos_sin = static_cast<const float*>(cs->data);
+    out->cs_stride = cs->stride[0];
+    out->cs_rows = static_cast<int32_t>(cs->shape[0]);
+    out->k_cache = static_cast<uint8_t*>(kc->data);
+    out->kc_stride0 = kc->stride[0];
+    out->kv_bs = static_cast<int32_t>(kc->shape[1]);
+    out->n_kv_slots = kc->shape[0] * kc->shape[1];
+    out->kv_slot_mapping = static_cast<const int32_t*>(kvs->data);
+    out->compressed_out = nullptr;
+  }
+  g_last_error.clear();
+  return DSV4_OK;
+}
+
+int run(const dsv4::C128Params& p, void* stream) {
+  hipError_t err = dsv4::launch_c128_compress_store(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsv4_c128_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                       const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                       const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                       const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                       const dsv4_tensor* kv_slot_mapping) {
+  return validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                      cos_sin, k_cache, kv_slot_mapping, nullptr);
+}
+
+int dsv4_c128_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                             const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                             const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                             const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                             const dsv4_tensor* kv_slot_mapping, void* stream) {
+  dsv4::C128Params p;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p);
+  if (rc) return rc;
+  if (p.num_tokens == 0) return DSV4_OK;
+  return run(p, stream);
+}
+
+int dsv4_c128_compress_store_debug(const dsv4_tensor* state_cache,
+                                   const dsv4_tensor* block_table,
+                                   const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                   const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                   float eps, const dsv4_tensor* cos_sin,
+                                   const dsv4_tensor* k_cache,
+                                   const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                   void* stream) {
+  dsv4::C128Params p;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p);
+  if (rc) return rc;
+  if (p.num_tokens == 0) return DSV4_OK;
+  if (!compressed_out) return fail(DSV4_ERR_NULL, "compressed_out is NULL");
+  if (!aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  p.compressed_out = compressed_out;
+  return run(p, stream);
+}
+
+int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return fail(DSV4_ERR_SHAPE, "n must be >= 0");
+  if (n == 0) return DSV4_OK;
+  if (!in || !out) return fail(DSV4_ERR_NULL, "in/out is NULL");
+  hipError_t err = dsv4::launch_e4m3_encode(in, out, n, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return DSV4_OK;
+}
+
+const char* dsv4_last_error(void) { return g_last_error.c_str(); }
+
+int dsv4_abi_version(void) { return DSV4_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,347 @@
+// C128 compress-store kernel for MI355X (gfx950, wave64).
+//
+// One workgroup per token.  What it computes follows the DeepSeek-V4
+// sparse-attention fused kernel on the vLLM "fused_compress_quant_cache" API
+// page (gate, window gather, per-column softmax pooling, RMSNorm, UE8M0/E4M3
+// quantisation of the 448 nope dims, GPT-J RoPE of the 64 rope dims, paged
+// insert).  How it computes it is specific to this chip:
+//
+//  * Column ownership.  A state row is 4 KiB: kv[0:512] | score[512:1024].
+//    Lane l of a "column half" wave owns the 16-byte kv vector of columns
+//    256*half + 4l .. +3 and the matching score vector 2 KiB further on, so
+//    every wave-wide load is 1 KiB contiguous (fully coalesced).
+//  * Row split.  The workgroup has 2*RG waves: the two column halves times
+//    RG row groups; a row group streams 16/RG of the window's 16 state
+//    blocks.  The window's 16 block ids are contiguous in the block table,
+//    read once with wave-uniform (scalar) loads: no per-row table lookup.
+//  * Online softmax in registers.  Rows are consumed in chunks of 4 with
+//    the next chunk's loads already in flight; per column a lane keeps the
+//    running max (in log2 units), the running sum of weights and the running
+//    weighted sum, rescaled with exp2 when the max grows.
+//  * Cross-wave merge through LDS (RG partial states per column), then the
+//    fused epilogue on the 128 lanes of row group 0: RMSNorm sum of squares
+//    by a wave reduction plus a 2-entry LDS exchange; one 64-column
+//    quantisation block is exactly 16 lanes, so its absmax is a 4-step
+//    in-group shuffle; the UE8M0 exponent comes from the bits of the fp32
+//    product (exact ceil(log2)); codes use gfx950's OCP E4M3FN conversion;
+//    RoPE lanes (columns 448..511) each rotate two pairs and store 8 bytes.
+//
+// This is an HBM-bound gather-reduce (about 0.6 flop per byte), so there is
+// no MFMA: the work is dominated by streaming 512 KiB of state per token.
+
+#include "c128_params.h"
+
+namespace dsv4 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFp8Max = 448.0f;
+constexpr float kInvFp8Max = 1.0f / 448.0f;  // fl32(1/448), as the page's fp32 multiply uses
+constexpr float kAbsmaxFloor = 1e-4f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int C>
+__device__ __forceinline__ float lane_of(const float4& v) {
+  if constexpr (C == 0) return v.x;
+  else if constexpr (C == 1) return v.y;
+  else if constexpr (C == 2) return v.z;
+  else return v.w;
+}
+
+// Clamp to the E4M3FN range and convert four fp32 values to OCP FP8 E4M3FN
+// (round to nearest even) with gfx950's packed conversion; byte k of the
+// result is the code of the k-th argument.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -kFp8Max), kFp8Max);
+  b = __builtin_fminf(__builtin_fmaxf(b, -kFp8Max), kFp8Max);
+  c = __builtin_fminf(__builtin_fmaxf(c, -kFp8Max), kFp8Max);
+  d = __builtin_fminf(__builtin_fmaxf(d, -kFp8Max), kFp8Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+  return __uint_as_float(bf16_bits(x) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Max over the 16-lane group holding one 64-column quantisation block.
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+constexpr int kChunk = 4;  // rows per pipeline stage
+
+__device__ __forceinline__ void load_rows(float4 (&kv)[kChunk], float4 (&sc)[kChunk],
+                                          const float* rp, int64_t s1) {
+#pragma unroll
+  for (int r = 0; r < kChunk; ++r) {
+    kv[r] = *reinterpret_cast<const float4*>(rp + r * s1);
+    sc[r] = *reinterpret_cast<const float4*>(rp + r * s1 + kHead);
+  }
+}
+
+// Online softmax update of one column with kChunk rows.
+template <int C, bool kFirst>
+__device__ __forceinline__ void update_column(const float4 (&kv)[kChunk],
+                                              const float4 (&sc)[kChunk], float& ml, float& l,
+                                              float& acc) {
+  float s[kChunk];
+#pragma unroll
+  for (int r = 0; r < kChunk; ++r) s[r] = lane_of<C>(sc[r]);
+  float cm = s[0];
+#pragma unroll
+  for (int r = 1; r < kChunk; ++r) cm = __builtin_fmaxf(cm, s[r]);
+  cm *= kLog2e;
+  const float mn = kFirst ? cm : __builtin_fmaxf(ml, cm);
+  float psum = 0.0f, a = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kChunk; ++r) {
+    const float pr = exp2_fast(__builtin_fmaf(s[r], kLog2e, -mn));
+    psum += pr;
+    a = __builtin_fmaf(pr, lane_of<C>(kv[r]), a);
+  }
+  if (kFirst) {
+    l = psum;
+    acc = a;
+  } else {
+    const float scale = exp2_fast(ml - mn);
+    l = __builtin_fmaf(l, scale, psum);
+    acc = __builtin_fmaf(acc, scale, a);
+  }
+  ml = mn;
+}
+
+template <bool kFirst>
+__device__ __forceinline__ void update(const float4 (&kv)[kChunk], const float4 (&sc)[kChunk],
+                                       float (&ml)[4], float (&l)[4], float (&acc)[4]) {
+  update_column<0, kFirst>(kv, sc, ml[0], l[0], acc[0]);
+  update_column<1, kFirst>(kv, sc, ml[1], l[1], acc[1]);
+  update_column<2, kFirst>(kv, sc, ml[2], l[2], acc[2]);
+  update_column<3, kFirst>(kv, sc, ml[3], l[3], acc[3]);
+}
+
+template <int RG, bool kDebug>
+__global__ void __launch_bounds__(128 * RG)
+c128_compress_store_kernel(const C128Params p) {
+  static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
+  constexpr int NB = kWindowBlocks / RG;                 // state blocks per wave
+  constexpr int NCH = NB * kStateBlock / kChunk;         // chunks per wave (even)
+  static_assert(NCH % 2 == 0, "ping-pong needs an even chunk count");
+
+  __shared__ float4 lds_ml[RG][2][64];
+  __shared__ float4 lds_l[RG][2][64];
+  __shared__ float4 lds_acc[RG][2][64];
+  __shared__ float lds_ss[2];
+
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int rg = wave >> 1;
+
+  // ---- gate (all values wave-uniform; the whole workgroup takes one path)
+  const int32_t pos = p.positions[t];
+  const int32_t slot = p.slot_mapping[t];
+  if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return;
+  const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
+  const int32_t req = p.token_to_req[t];
+  if (req < 0 || req >= p.bt_rows ||
+      static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
+    return;
+  const int32_t rope_row = win * kRatio;  // (pos // 128) * 128
+  if (rope_row >= p.cs_rows) return;
+  const int32_t* bt =
+      p.block_table + static_cast<int64_t>(req) * p.bt_stride +
+      static_cast<int64_t>(win) * kWindowBlocks;
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < kWindowBlocks; ++i)
+    ok &= static_cast<uint32_t>(bt[i]) < static_cast<uint32_t>(p.n_state_blocks);
+  if (!ok) return;
+
+  // ---- stream this wave's NB blocks x 8 rows, 4 rows per stage
+  const int col = half * 256 + lane * 4;
+  const int32_t* mybt = bt + rg * NB;
+  const float* colbase = p.state + col;
+  const int64_t s0 = p.s0, s1 = p.s1;
+  auto rowptr = [&](int ch) {
+    return colbase + static_cast<int64_t>(mybt[ch >> 1]) * s0 +
+           static_cast<int64_t>((ch & 1) * kChunk) * s1;
+  };
+
+  float ml[4], l[4], acc[4];
+  float4 kvA[kChunk], scA[kChunk], kvB[kChunk], scB[kChunk];
+  load_rows(kvA, scA, rowptr(0), s1);
+#pragma unroll
+  for (int ch = 0; ch < NCH; ch += 2) {
+    load_rows(kvB, scB, rowptr(ch + 1), s1);
+    if (ch == 0)
+      update<true>(kvA, scA, ml, l, acc);
+    else
+      update<false>(kvA, scA, ml, l, acc);
+    if (ch + 2 < NCH) load_rows(kvA, scA, rowptr(ch + 2), s1);
+    update<false>(kvB, scB, ml, l, acc);
+  }
+
+  // ---- merge the RG row groups of each column half
+  if constexpr (RG > 1) {
+    lds_ml[rg][half][lane] = make_float4(ml[0], ml[1], ml[2], ml[3]);
+    lds_l[rg][half][lane] = make_float4(l[0], l[1], l[2], l[3]);
+    lds_acc[rg][half][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+  }
+  float c[4] = {0.f, 0.f, 0.f, 0.f};
+  if (rg == 0) {
+    if constexpr (RG > 1) {
+      float4 gm[RG], gl[RG], ga[RG];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        gm[g] = lds_ml[g][half][lane];
+        gl[g] = lds_l[g][half][lane];
+        ga[g] = lds_acc[g][half][lane];
+      }
+      float M[4] = {gm[0].x, gm[0].y, gm[0].z, gm[0].w};
+#pragma unroll
+      for (int g = 1; g < RG; ++g) {
+        M[0] = __builtin_fmaxf(M[0], gm[g].x);
+        M[1] = __builtin_fmaxf(M[1], gm[g].y);
+        M[2] = __builtin_fmaxf(M[2], gm[g].z);
+        M[3] = __builtin_fmaxf(M[3], gm[g].w);
+      }
+      float L[4] = {0.f, 0.f, 0.f, 0.f}, A[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const float f0 = exp2_fast(gm[g].x - M[0]), f1 = exp2_fast(gm[g].y - M[1]);
+        const float f2 = exp2_fast(gm[g].z - M[2]), f3 = exp2_fast(gm[g].w - M[3]);
+        L[0] = __builtin_fmaf(gl[g].x, f0, L[0]);
+        L[1] = __builtin_fmaf(gl[g].y, f1, L[1]);
+        L[2] = __builtin_fmaf(gl[g].z, f2, L[2]);
+        L[3] = __builtin_fmaf(gl[g].w, f3, L[3]);
+        A[0] = __builtin_fmaf(ga[g].x, f0, A[0]);
+        A[1] = __builtin_fmaf(ga[g].y, f1, A[1]);
+        A[2] = __builtin_fmaf(ga[g].z, f2, A[2]);
+        A[3] = __builtin_fmaf(ga[g].w, f3, A[3]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = A[k] / L[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
+    }
+    // RMSNorm sum of squares: this lane's 4 columns, then the wave
+    float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
+    ss = wave_sum(ss);
+    if (lane == 0) lds_ss[half] = ss;
+  }
+  __syncthreads();
+  if (rg != 0) return;
+
+  // ---- fused epilogue on the 128 lanes of row group 0
+  const float var = (lds_ss[0] + lds_ss[1]) * (1.0f / kHead);
+  const float rrms = 1.0f / __builtin_sqrtf(var + p.eps);
+  const float4 w = *reinterpret_cast<const float4*>(p.rms_w + col);
+  float n[4] = {c[0] * rrms * w.x, c[1] * rrms * w.y, c[2] * rrms * w.z, c[3] * rrms * w.w};
+
+  if constexpr (kDebug)
+    *reinterpret_cast<float4*>(p.compressed_out + static_cast<int64_t>(t) * kHead + col) =
+        make_float4(c[0], c[1], c[2], c[3]);
+
+  // per-64 absmax of the bf16-rounded values (every lane joins the shuffles)
+  float u[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) u[k] = bf16_round(n[k]);
+  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
+                               __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
+  amax = group16_max(amax);
+
+  const int32_t kv_slot = p.kv_slot_mapping[t];
+  if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return;
+  const int32_t kb = kv_slot / p.kv_bs;
+  const int32_t ko = kv_slot - kb * p.kv_bs;
+  uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+  uint8_t* rec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
+  uint8_t* scl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+                 static_cast<int64_t>(ko) * kScaleBytes;
+
+  const bool rope_lane = (half == 1) && (lane >= 48);
+  if (!rope_lane) {
+    // UE8M0 exponent: exact ceil(log2(raw)) from the fp32 bits of the product
+    const float raw = __builtin_fmaxf(amax, kAbsmaxFloor) * kInvFp8Max;
+    const uint32_t rb = __float_as_uint(raw);
+    const int e = static_cast<int>((rb >> 23) & 0xffu) - 127 + ((rb & 0x7fffffu) != 0u);
+    const float inv_scale = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);  // 2^-e
+    const uint32_t codes = e4m3x4(u[0] * inv_scale, u[1] * inv_scale, u[2] * inv_scale,
+                                  u[3] * inv_scale);
+    *reinterpret_cast<uint32_t*>(rec + col) = codes;
+    if ((lane & 15) == 0) {
+      const int byte = e + 127;
+      scl[col >> 6] = static_cast<uint8_t>(byte < 0 ? 0 : (byte > 255 ? 255 : byte));
+    }
+  } else {
+    // GPT-J RoPE: this lane holds pairs m0 = 2j and m0 + 1 (dims 448 + 4j .. + 3)
+    const int j = lane - 48;
+    const float* cs = p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
+    const float c0 = cs[2 * j], c1 = cs[2 * j + 1];
+    const float s0r = cs[kRope / 2 + 2 * j], s1r = cs[kRope / 2 + 2 * j + 1];
+    const float x0 = n[0] * c0 - n[1] * s0r;
+    const float y0 = n[1] * c0 + n[0] * s0r;
+    const float x1 = n[2] * c1 - n[3] * s1r;
+    const float y1 = n[3] * c1 + n[2] * s1r;
+    const uint32_t lo = bf16_bits(x0) | (bf16_bits(y0) << 16);
+    const uint32_t hi = bf16_bits(x1) | (bf16_bits(y1) << 16);
+    *reinterpret_cast<uint2*>(rec + kNope + 8 * j) = make_uint2(lo, hi);
+    if (j == 0) scl[kNumQuant] = 0;  // pad byte
+  }
+}
+
+__global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8_t* out,
+                                                          int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  float v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = (i + k < n) ? in[i + k] : 0.0f;
+  const uint32_t w = e4m3x4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (i + k < n) out[i + k] = static_cast<uint8_t>(w >> (8 * k));
+}
+
+constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
+
+}  // namespace
+
+hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(p.num_tokens));
+  const dim3 block(128 * kRowGroups);
+  if (p.compressed_out)
+    c128_compress_store_kernel<kRowGroups, true><<<grid, block, 0, stream>>>(p);
+  else
+    c128_compress_store_kernel<kRowGroups, false><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  const int64_t blocks = (threads + 255) / 256;
+  e4m3_encode_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace dsv4

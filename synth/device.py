@@ -1,0 +1,77 @@
+"""Place a synth.Workload in device memory (torch tensors; the k_cache view sits between
+guard bands), run the library on it and bring the k_cache bytes back.  Used by the GPU
+tests, the smoke check and the bench."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_fp32_amd as c128
+
+GUARD = 4096
+GUARD_BYTE = 0x5A
+
+
+class DeviceWorkload:
+    def __init__(self, wl, device="cuda", guard=GUARD, state=None):
+        """``state``: an already resident (buffer, view) pair holding the same bytes as
+        ``wl.state`` (several workloads can share one device pool)."""
+        self.wl = wl
+        self.guard = guard
+        st = wl.state
+        if state is not None:
+            self.state_buf, self.state = state
+        else:
+            base = wl.state_base if wl.state_base is not None else \
+                np.ascontiguousarray(st).reshape(-1)
+            self.state_buf = torch.from_numpy(base).to(device)
+            if wl.state_base is not None:
+                s = tuple(x // 4 for x in st.strides)
+                self.state = torch.as_strided(self.state_buf, st.shape, s)
+            else:
+                self.state = self.state_buf.view(st.shape)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(device)
+        self.token_to_req = torch.from_numpy(np.ascontiguousarray(wl.token_to_req)).to(device)
+        self.positions = torch.from_numpy(np.ascontiguousarray(wl.positions)).to(device)
+        self.slot_mapping = torch.from_numpy(np.ascontiguousarray(wl.slot_mapping)).to(device)
+        self.kv_slot_mapping = torch.from_numpy(np.ascontiguousarray(wl.kv_slot_mapping)).to(device)
+        self.rms_w = torch.from_numpy(np.ascontiguousarray(wl.rms_w)).to(device)
+        self.cos_sin = torch.from_numpy(np.ascontiguousarray(wl.cos_sin)).to(device)
+        kb = wl.k_cache_base
+        self.kc_buf = torch.full((kb.size + 2 * guard,), GUARD_BYTE, dtype=torch.uint8,
+                                 device=device)
+        self.kc_buf[guard:guard + kb.size].copy_(torch.from_numpy(kb))
+        kc = wl.k_cache
+        self.k_cache = torch.as_strided(self.kc_buf, kc.shape, kc.strides, guard)
+        self.eps = wl.eps
+
+    def args(self):
+        return (self.state, self.block_table, self.token_to_req, self.positions,
+                self.slot_mapping, self.rms_w, self.eps, self.cos_sin, self.k_cache,
+                self.kv_slot_mapping)
+
+    def run(self, debug=False):
+        comp = None
+        if debug:
+            comp = torch.full((self.wl.num_tokens, 512), float("nan"), dtype=torch.float32,
+                              device=self.state.device)
+            c128.compress_store_debug(*self.args(), comp)
+        else:
+            c128.compress_store(*self.args())
+        torch.cuda.synchronize()
+        return comp
+
+    def k_cache_bytes(self):
+        """(body bytes, guards intact?)"""
+        buf = self.kc_buf.cpu().numpy()
+        g = self.guard
+        guards_ok = bool(np.all(buf[:g] == GUARD_BYTE) and np.all(buf[-g:] == GUARD_BYTE))
+        return buf[g:-g].copy(), guards_ok
+
+
+def run_gpu(wl, debug=True):
+    d = DeviceWorkload(wl)
+    comp = d.run(debug=debug)
+    body, guards_ok = d.k_cache_bytes()
+    return body, (comp.cpu().numpy() if comp is not None else None), guards_ok

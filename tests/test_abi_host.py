@@ -1,0 +1,199 @@
+"""Host-only tests of the C ABI: the library loads without a GPU, exports every function
+the header declares, and its descriptor validation returns each documented error code
+before any HIP call (validation reads descriptors only, never the data)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_fp32_amd as c128
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsv4_c128.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dsv4_\w+)\s*\(", text, re.M)))
+
+
+def header_constant(name):
+    m = re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_library_exports_every_declared_function():
+    lib = c128.library()
+    names = declared_functions()
+    assert {"dsv4_c128_compress_store", "dsv4_c128_compress_store_debug", "dsv4_c128_validate",
+            "dsv4_e4m3_encode", "dsv4_last_error", "dsv4_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header():
+    assert c128.abi_version() == header_constant("DSV4_ABI_VERSION")
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    for code, name in c128.ERRORS.items():
+        m = re.search(rf"{name}\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == code, name
+
+
+def valid_args(T=4, S=32, bs=4):
+    """CPU tensors with valid shapes/strides (validation never reads them)."""
+    return dict(
+        state_cache=torch.zeros(S, 8, 1024, dtype=torch.float32),
+        block_table=torch.zeros(T, 64, dtype=torch.int32),
+        token_to_req=torch.zeros(T, dtype=torch.int32),
+        positions=torch.zeros(T, dtype=torch.int32),
+        slot_mapping=torch.zeros(T, dtype=torch.int32),
+        rms_w=torch.ones(512, dtype=torch.float32),
+        eps=1e-6,
+        cos_sin=torch.zeros(128, 64, dtype=torch.float32),
+        k_cache=torch.zeros(2, bs, 584, dtype=torch.uint8),
+        kv_slot_mapping=torch.zeros(T, dtype=torch.int32),
+    )
+
+
+def call_validate(a):
+    return c128.validate(a["state_cache"], a["block_table"], a["token_to_req"], a["positions"],
+                         a["slot_mapping"], a["rms_w"], a["eps"], a["cos_sin"], a["k_cache"],
+                         a["kv_slot_mapping"])
+
+
+def test_valid_layout_passes():
+    assert call_validate(valid_args()) == 0
+    assert c128.last_error() == ""
+
+
+def padded(shape, dtype, pad_last=0, pad_dim0=0):
+    big = torch.zeros(*[s + (pad_dim0 if i == 0 else 0) for i, s in enumerate(shape[:-1])],
+                      shape[-1] + pad_last, dtype=dtype)
+    return big[tuple(slice(0, s) for s in shape)]
+
+
+def test_padded_views_pass():
+    a = valid_args()
+    a["state_cache"] = torch.zeros(32, 8, 1024 + 64)[:, :, :1024]
+    a["k_cache"] = torch.zeros(2, 4 * 584 + 48, dtype=torch.uint8)[:, :4 * 584].view(
+        2, 4, 584) if False else torch.as_strided(torch.zeros(2 * (4 * 584 + 48), dtype=torch.uint8),
+                                                  (2, 4, 584), (4 * 584 + 48, 584, 1))
+    a["cos_sin"] = torch.zeros(128, 96)[:, :64]
+    a["block_table"] = torch.zeros(4, 80, dtype=torch.int32)[:, :64]
+    assert call_validate(a) == 0, c128.last_error()
+
+
+CASES = [
+    # (name, mutation, expected code)
+    ("state dtype", lambda a: a.update(state_cache=a["state_cache"].double()), -2),
+    ("state rank", lambda a: a.update(state_cache=a["state_cache"].view(32, 8192)), -3),
+    ("state block 16", lambda a: a.update(state_cache=torch.zeros(16, 16, 1024)), -4),
+    ("state row 512", lambda a: a.update(state_cache=torch.zeros(32, 8, 512)), -4),
+    ("state row 2048", lambda a: a.update(state_cache=torch.zeros(32, 8, 2048)), -4),
+    ("state transposed", lambda a: a.update(
+        state_cache=torch.zeros(1024, 8, 32).permute(2, 1, 0)), -5),
+    ("state rows overlap", lambda a: a.update(
+        state_cache=torch.as_strided(torch.zeros(40000), (32, 8, 1024), (1024, 512, 1))), -5),
+    ("state misaligned", lambda a: a.update(
+        state_cache=torch.zeros(32 * 8 * 1024 + 1)[1:].view(32, 8, 1024)), -6),
+    ("state stride not x4", lambda a: a.update(
+        state_cache=torch.zeros(32, 8, 1026)[:, :, :1024]), -6),
+    ("block table rank", lambda a: a.update(block_table=torch.zeros(256, dtype=torch.int32)), -3),
+    ("block table dtype", lambda a: a.update(block_table=torch.zeros(4, 64, dtype=torch.int64)), -2),
+    ("block table narrow", lambda a: a.update(block_table=torch.zeros(4, 8, dtype=torch.int32)), -4),
+    ("block table col-major", lambda a: a.update(
+        block_table=torch.zeros(64, 4, dtype=torch.int32).t()), -5),
+    ("T mismatch", lambda a: a.update(token_to_req=torch.zeros(5, dtype=torch.int32)), -4),
+    ("slot T mismatch", lambda a: a.update(slot_mapping=torch.zeros(3, dtype=torch.int32)), -4),
+    ("kv slot T mismatch", lambda a: a.update(kv_slot_mapping=torch.zeros(2, dtype=torch.int32)),
+     -4),
+    ("positions strided", lambda a: a.update(positions=torch.zeros(8, dtype=torch.int32)[::2]), -5),
+    ("positions int64", lambda a: a.update(positions=torch.zeros(4, dtype=torch.int64)), -2),
+    ("rms 448", lambda a: a.update(rms_w=torch.ones(448)), -4),
+    ("rms strided", lambda a: a.update(rms_w=torch.ones(1024)[::2]), -5),
+    ("rms misaligned", lambda a: a.update(rms_w=torch.ones(513)[1:]), -6),
+    ("cos_sin narrow", lambda a: a.update(cos_sin=torch.zeros(128, 32)), -4),
+    ("cos_sin col-major", lambda a: a.update(cos_sin=torch.zeros(64, 128).t()), -5),
+    ("k_cache dtype", lambda a: a.update(k_cache=torch.zeros(2, 4, 584, dtype=torch.int32)), -2),
+    ("k_cache row 576", lambda a: a.update(k_cache=torch.zeros(2, 4, 576, dtype=torch.uint8)), -4),
+    ("k_cache rank", lambda a: a.update(k_cache=torch.zeros(2, 4 * 584, dtype=torch.uint8)), -3),
+    ("k_cache stride0 small", lambda a: a.update(k_cache=torch.as_strided(
+        torch.zeros(8 * 584, dtype=torch.uint8), (2, 4, 584), (3 * 584, 584, 1))), -5),
+    ("k_cache stride0 unaligned", lambda a: a.update(k_cache=torch.as_strided(
+        torch.zeros(2 * (4 * 584 + 8), dtype=torch.uint8), (2, 4, 584), (4 * 584 + 8, 584, 1))), -6),
+    ("k_cache base unaligned", lambda a: a.update(k_cache=torch.zeros(
+        2 * 4 * 584 + 1, dtype=torch.uint8)[1:].view(2, 4, 584)), -6),
+    ("negative eps", lambda a: a.update(eps=-1.0), -4),
+    ("nan eps", lambda a: a.update(eps=float("nan")), -4),
+]
+
+
+@pytest.mark.parametrize("name,mut,code", CASES, ids=[c[0] for c in CASES])
+def test_validation_error_codes(name, mut, code):
+    a = valid_args()
+    mut(a)
+    assert call_validate(a) == code, c128.last_error()
+    assert c128.last_error() != ""
+
+
+def test_null_descriptor():
+    a = valid_args()
+    lib = c128.library()
+    d = [c128.describe(a[k]) for k in ("state_cache", "block_table", "token_to_req", "positions",
+                                       "slot_mapping", "rms_w")]
+    rest = [c128.describe(a[k]) for k in ("cos_sin", "k_cache", "kv_slot_mapping")]
+    refs = [ctypes.byref(x) for x in d]
+    rc = lib.dsv4_c128_validate(None, *refs[1:], 1e-6, *[ctypes.byref(x) for x in rest])
+    assert rc == -1
+    # a null data pointer on a non-empty tensor
+    d[0].data = None
+    rc = lib.dsv4_c128_validate(*[ctypes.byref(x) for x in d], 1e-6,
+                                *[ctypes.byref(x) for x in rest])
+    assert rc == -1
+
+
+def test_compute_entry_points_reject_before_any_hip_call():
+    """The compute entry points validate first: with an invalid layout they return the error
+    code without launching (safe with host pointers and no GPU)."""
+    a = valid_args()
+    a["state_cache"] = torch.zeros(32, 8, 512)
+    lib = c128.library()
+    ts = [a[k] for k in ("state_cache", "block_table", "token_to_req", "positions",
+                         "slot_mapping", "rms_w")]
+    rest = [a[k] for k in ("cos_sin", "k_cache", "kv_slot_mapping")]
+    ds = [c128.describe(t) for t in ts]
+    rs = [c128.describe(t) for t in rest]
+    rc = lib.dsv4_c128_compress_store(*[ctypes.byref(x) for x in ds], 1e-6,
+                                      *[ctypes.byref(x) for x in rs], None)
+    assert rc == -4
+    rc = lib.dsv4_c128_compress_store_debug(*[ctypes.byref(x) for x in ds], 1e-6,
+                                            *[ctypes.byref(x) for x in rs], None, None)
+    assert rc == -4
+
+
+def test_empty_batch_returns_before_launch():
+    """T == 0 is a no-op that returns before any HIP call."""
+    a = valid_args(T=0)
+    a["block_table"] = torch.zeros(1, 16, dtype=torch.int32)
+    lib = c128.library()
+    ts = [a[k] for k in ("state_cache", "block_table", "token_to_req", "positions",
+                         "slot_mapping", "rms_w")]
+    rest = [a[k] for k in ("cos_sin", "k_cache", "kv_slot_mapping")]
+    rc = lib.dsv4_c128_compress_store(*[ctypes.byref(c128.describe(t)) for t in ts], 1e-6,
+                                      *[ctypes.byref(c128.describe(t)) for t in rest], None)
+    assert rc == 0
+    assert lib.dsv4_e4m3_encode(None, None, 0, None) == 0
+    assert lib.dsv4_e4m3_encode(None, None, -1, None) == -4
+
+
+def test_python_binding_rejects_host_tensors():
+    a = valid_args()
+    with pytest.raises(ValueError):
+        c128.compress_store(**a)

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Pass criteria (oracle/compare.py): untouched bytes and UE8M0 scale bytes
+bit-exact (knife-edge blocks excused and counted), E4M3 codes within one step
+on <= 0.1% of elements, RoPE bf16 within 1 ulp, fp32 compressed within 1e-5
+of sum_i p_ij |kv_ij|.  Every test prints its case before touching the GPU.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.compare import compare
+from synth.device import DeviceWorkload, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+THREADS = synth.default_threads()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check(wl, debug=True, tokens=None, nthreads=THREADS, label=None):
+    announce(label or wl.name)
+    body, comp, guards_ok = run_gpu(wl, debug=debug)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, nthreads)
+    rep = compare(wl, body, orc, tokens=tokens, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, body, comp, orc
+
+
+# ---------------------------------------------------------------- conversion
+
+def test_e4m3_encoder_exhaustive():
+    """The kernel's E4M3FN encoder on every bf16 value (the quantiser's domain after the
+    power-of-two scale), values beyond +-448 (clamped), fp32 subnormals and signed zeros,
+    against the oracle's encoder (itself pinned by brute force)."""
+    announce("e4m3 encoder exhaustive")
+    b = np.arange(1 << 16, dtype=np.uint32)
+    f = (b << 16).view(np.float32)
+    f = f[np.isfinite(f)]
+    extra = np.array([0.0, -0.0, 1e-40, -1e-40, 2.0 ** -149, 449.0, -449.0, 464.0, 1e30, -1e30,
+                      2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -10 * 1.0000001], np.float32)
+    x = np.concatenate([f, extra]).astype(np.float32)
+    got = c128_encode(x)
+    want = oracle.e4m3_codes(np.clip(x.astype(np.float64), -448.0, 448.0))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+def c128_encode(x):
+    import paged_kv_cache_fp32_amd as c128
+    out = c128.e4m3_encode(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_config0_single_token():
+    rep, _, comp, orc = check(synth.config0())
+    assert rep["written"] == 1
+
+
+def test_handworked_golden_bit_exact():
+    """The hand-derived record (tests/golden/c128_handworked.txt) comes out bit-exact, and the
+    non-boundary token at position 126 leaves its slot at 0xAB."""
+    from tests.golden.handworked import build_handworked, expected_record
+    wl = build_handworked()
+    announce("handworked golden")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    codes = body[0:448]
+    rope = body[448:576].view("<u2")
+    scales = body[2 * 576:2 * 576 + 8]
+    want_codes, want_scales, want_rope = expected_record()
+    assert np.array_equal(codes, want_codes)
+    assert np.array_equal(scales, want_scales)
+    assert np.array_equal(rope, want_rope)
+    assert np.all(body[576:2 * 576] == 0xAB) and np.all(body[2 * 576 + 8:] == 0xAB)
+    sign = np.where(np.arange(512) % 3 == 0, 1.0, -1.0)
+    assert np.array_equal(comp[0], sign.astype(np.float32))
+
+
+def test_config1_decode_batch():
+    rep, *_ = check(synth.config1())
+    assert rep["written"] == 128
+
+
+def test_config2_varlen_prefill():
+    wl = synth.config2()
+    rep, *_ = check(wl)
+    assert rep["written"] == int(wl.written_mask().sum()) > 100
+
+
+@pytest.fixture(scope="module")
+def sweep_pool():
+    return synth.config3_pool()
+
+
+@pytest.mark.parametrize("T", [1, 2, 8, 64, 256, 1024, 4096])
+def test_config3_decode_sweep(sweep_pool, T):
+    wl = synth.config3(T, state=sweep_pool[1])
+    rep, *_ = check(wl)
+    assert rep["written"] == T
+
+
+def test_config3_rotated_window_sets(sweep_pool):
+    """The bench rotates over disjoint window sets of the same pool; each set is correct."""
+    for s in (1, 3):
+        wl = synth.config3(512, state=sweep_pool[1], window_set=s)
+        check(wl, label=f"cfg3 T=512 window set {s}")
+
+
+def test_config4_full_size():
+    """16384 boundary tokens over the 8.59 GB pool, in the bench's launch configuration;
+    every token compared against the oracle."""
+    wl = synth.config4()
+    rep, *_ = check(wl, debug=False)
+    assert rep["written"] == 16384
+
+
+# ---------------------------------------------------------------- edge cases
+
+def small(T=8, seed=5, **kw):
+    kv_bs = kw.pop("kv_bs", 4)
+    return synth.decode_batch("edge", seed, T, kw.pop("n_blocks", 16 * T + 16), kw.pop("k_max", 8),
+                              kw.pop("table_cols", 128), kv_bs=kv_bs,
+                              kv_blocks=kw.pop("kv_blocks", -(-2 * T // kv_bs)),
+                              cs_rows=kw.pop("cs_rows", 1024), **kw)
+
+
+def test_non_boundary_and_negative_slots():
+    """Positions 126, 128, 255 (boundary), 254, 383 (boundary); slot -1 on a boundary; kv slot -1
+    on a boundary: only real boundary tokens with both slots >= 0 write."""
+    wl = small(T=6, seed=7)
+    wl.positions[:] = np.array([126, 128, 255, 254, 383, 511], np.int32)
+    wl.slot_mapping[:] = np.array([3, 3, 3, 3, -1, 9], np.int32)
+    wl.kv_slot_mapping[5] = -1
+    rep, body, comp, orc = check(wl, label="non-boundary / negative slots")
+    assert list(np.nonzero(wl.written_mask())[0]) == [2]
+    assert np.isfinite(comp[5]).all() and np.isnan(comp[4]).all() and np.isnan(comp[0]).all()
+
+
+def test_all_zero_window():
+    wl = small(T=2, seed=9)
+    wl.state[:, :, :512] = 0.0
+    rep, body, *_ = check(wl, label="all-zero window")
+
+
+@pytest.mark.parametrize("kv_bs", [1, 2, 64])
+def test_kv_block_sizes(kv_bs):
+    check(small(T=16, seed=11, kv_bs=kv_bs, kv_blocks=-(-40 // kv_bs)), label=f"kv bs {kv_bs}")
+
+
+def test_padded_strides():
+    """Padded state rows and blocks and a padded k_cache block stride."""
+    wl = small(T=12, seed=13, row_pad=32, block_pad=64, kc_block_pad=48)
+    check(wl, label="padded strides")
+
+
+def test_peaky_and_near_constant_scores():
+    wl = small(T=16, seed=17, score_std=8.0)
+    check(wl, label="peaky scores std 8")
+    wl = small(T=16, seed=18, score_std=1.0, score_mix=True)
+    check(wl, label="near-constant windows")
+
+
+def test_out_of_range_device_indices_write_nothing():
+    """Indices that live in device memory and are out of range (request, block id, kv slot,
+    RoPE row) make the kernel skip the token: nothing is written, no fault."""
+    wl = small(T=6, seed=19, cs_rows=1024)
+    wl.token_to_req[0] = wl.block_table.shape[0]        # request out of range
+    r1 = int(wl.positions[1]) // 8
+    wl.block_table[1, r1] = wl.state.shape[0] + 5       # a window block id out of range
+    wl.kv_slot_mapping[2] = wl.k_cache.shape[0] * wl.k_cache.shape[1]  # kv slot out of range
+    wl.cos_sin = wl.cos_sin[:128].copy()                # RoPE rows 0..127 only
+    wl.positions[3] = 127
+    wl.positions[4] = 1023                              # needs RoPE row 896: out of range
+    wl.positions[5] = 127
+    announce("out-of-range device indices")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [-1, -1, -1, 1, -1, 1]
+    # the oracle's k_cache has exactly the two valid tokens' records; so must the GPU's
+    keep = np.array([False, False, False, True, False, True])
+    wl.kv_slot_mapping[~keep] = -1                      # compare as if only they write
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    # tokens rejected on the state side produce no pooled vector; an out-of-range kv slot
+    # behaves like a negative one (pooled, nothing stored)
+    assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
+
+
+def test_empty_batch_is_a_noop():
+    import paged_kv_cache_fp32_amd as c128
+    announce("T = 0")
+    d = DeviceWorkload(small(T=1, seed=23))
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    before = d.kc_buf.clone()
+    c128.compress_store(d.state, d.block_table, e, e, e, d.rms_w, 1e-6, d.cos_sin, d.k_cache, e)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d.kc_buf)
+
+
+def test_repeatable_and_debug_matches_plain():
+    """Two runs give identical bytes; the debug entry point writes the same k_cache bytes."""
+    wl = small(T=32, seed=29)
+    announce("determinism")
+    a, _, ga = run_gpu(wl, debug=False)
+    b, _, gb = run_gpu(wl, debug=False)
+    c, _, gc = run_gpu(wl, debug=True)
+    assert ga and gb and gc
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_stream_argument_is_used():
+    """Launch on a side stream; the result is there after that stream synchronises."""
+    import paged_kv_cache_fp32_amd as c128
+    wl = small(T=8, seed=31)
+    announce("side stream")
+    d = DeviceWorkload(wl)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c128.compress_store(*d.args())
+    s.synchronize()
+    body, ok = d.k_cache_bytes()
+    orc = oracle.run(wl, 2)
+    rep = compare(wl, body, orc)
+    assert ok and rep.ok(), rep.summary()
