@@ -10,7 +10,12 @@ Test infrastructure (see ``oracle/__init__.py``).  Pass criteria:
   excused, counted, and compared by dequantised value instead;
 * E4M3 codes within 1 code step (ordinal distance, +0 == -0), on at most 0.1%
   of the compared nope elements;
-* RoPE bf16 within 1 ulp (ordinal distance, +0 == -0);
+* RoPE bf16 within 1 ulp (ordinal distance, +0 == -0).  Under cancellation --
+  a rotated value x*C - y*S much smaller than its inputs -- the fp32 error that
+  the pooled vector may carry (the compressed tolerance below) is worth more
+  than one ulp of the small result; such an element passes if it lies within
+  1 ulp plus that tolerance carried through the norm and the rotation, and is
+  counted ("rope_band");
 * debug fp32 compressed vector: |gpu - oracle| <= 1e-5 * sum_i p_ij |kv_ij|.
 """
 
@@ -63,6 +68,43 @@ def bf16_ord(b: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
+def bf16_val(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def rope_band(wl, orc, t: int) -> tuple[np.ndarray, np.ndarray]:
+    """(exact rotated values, allowed |gpu - exact|) for the 64 RoPE dims of token t:
+    1 bf16 ulp + the compressed tolerance carried through RMSNorm and the rotation +
+    fp32 rounding of the rotation."""
+    c = orc.compressed[t]
+    n = orc.normed[t]
+    A = orc.absnorm[t]
+    r = 1.0 / np.sqrt(np.mean(c * c) + float(wl.eps))
+    w = wl.rms_w.astype(np.float64)
+    dn = r * np.abs(w) * COMPRESSED_REL * A + COMPRESSED_REL * np.abs(n)
+    P = (int(wl.positions[t]) // 128) * 128
+    cs = wl.cos_sin[P].astype(np.float64)
+    C, S = cs[:32], cs[32:64]
+    x, y = n[448::2], n[449::2]
+    dx, dy = dn[448::2], dn[449::2]
+    zx = x * C - y * S
+    zy = y * C + x * S
+    rnd_x = 2.0 ** -22 * (np.abs(x * C) + np.abs(y * S))
+    rnd_y = 2.0 ** -22 * (np.abs(y * C) + np.abs(x * S))
+    tol_x = bf16_ulp(zx) + np.abs(C) * dx + np.abs(S) * dy + rnd_x
+    tol_y = bf16_ulp(zy) + np.abs(C) * dy + np.abs(S) * dx + rnd_y
+    z = np.empty(64)
+    tol = np.empty(64)
+    z[0::2], z[1::2] = zx, zy
+    tol[0::2], tol[1::2] = tol_x, tol_y
+    return z, tol
+
+
 def knife_edge(absmax: float) -> bool:
     if absmax <= 0:
         return False
@@ -80,7 +122,8 @@ class Report(dict):
 
     def summary(self) -> str:
         keys = ["tokens", "written", "untouched_mismatch", "scale_mismatch", "excused_blocks",
-                "code_diff1", "code_diff1_frac", "code_fail", "rope_max_ulp", "compressed_max_ratio",
+                "code_diff1", "code_diff1_frac", "code_fail", "rope_max_ulp", "rope_band",
+                "compressed_max_ratio",
                 "compressed_max_rel"]
         return ", ".join(f"{k}={self.get(k)}" for k in keys) + (
             "" if self.ok() else f"; FAIL: {self['failures'][:5]}")
@@ -109,7 +152,7 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
         rep["failures"].append(f"{rep['untouched_mismatch']} bytes outside written records changed")
 
     # 2-4. records of the compared written tokens
-    n_code = n_diff1 = n_scale_bad = n_excused = 0
+    n_code = n_diff1 = n_scale_bad = n_excused = n_band = 0
     rope_max = 0
     for t in toks:
         t = int(t)
@@ -148,6 +191,18 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
                 rep["failures"].append(f"token {t} block {g}: code differs by {int(d.max())}")
         rd = np.abs(bf16_ord(g_rope) - bf16_ord(o_rope))
         rope_max = max(rope_max, int(rd.max()))
+        far = rd > 1
+        if far.any():
+            if orc.compressed is None or not np.isfinite(orc.compressed[t]).all():
+                rep["failures"].append(f"token {t}: rope differs by {int(rd.max())} ulp")
+            else:
+                z, tol = rope_band(wl, orc, t)
+                err = np.abs(bf16_val(g_rope) - z)
+                n_band += int(far.sum())
+                if np.any(err[far] > tol[far]):
+                    rep["failures"].append(
+                        f"token {t}: rope beyond 1 ulp + cancellation band "
+                        f"({float((err[far] / tol[far]).max()):.2f} of the band)")
     rep["written"] = int(written[toks].sum())
     rep["scale_mismatch"] = n_scale_bad
     rep["excused_blocks"] = n_excused
@@ -157,8 +212,7 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
     if rep["code_fail"]:
         rep["failures"].append(f"code diff-1 fraction {rep['code_diff1_frac']:.2e} > 1e-3")
     rep["rope_max_ulp"] = rope_max
-    if rope_max > 1:
-        rep["failures"].append(f"rope differs by {rope_max} bf16 ulp")
+    rep["rope_band"] = n_band
 
     # 5. compressed fp32 (debug export)
     if gpu_compressed is not None and orc.compressed is not None:

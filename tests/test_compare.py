@@ -1,0 +1,79 @@
+"""Host tests of the parity checker (oracle/compare.py): it passes the oracle's own output
+and flags each kind of planted mistake."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.compare import compare, record_offsets
+
+
+@pytest.fixture(scope="module")
+def case():
+    wl = synth.decode_batch("cmp", 8, 12, 400, 6, 96, kv_bs=4, kv_blocks=8, cs_rows=768)
+    return wl, oracle.run(wl, 2)
+
+
+def test_identical_output_passes(case):
+    wl, orc = case
+    rep = compare(wl, orc.k_cache_base.copy(), orc, gpu_compressed=orc.compressed.astype(np.float32))
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 12
+
+
+def planted(wl, orc, fn):
+    body = orc.k_cache_base.copy()
+    s = int(wl.kv_slot_mapping[5])
+    rec, scl = record_offsets(s, wl.k_cache.shape[1], wl.k_cache.strides[0])
+    fn(body, rec, scl)
+    return compare(wl, body, orc)
+
+
+def test_flags_code_off_by_two(case):
+    wl, orc = case
+
+    def f(b, rec, scl):
+        c = int(b[rec + 10])
+        b[rec + 10] = (c & 0x80) | ((c & 0x7F) - 2 if (c & 0x7F) >= 2 else (c & 0x7F) + 2)
+    assert not planted(wl, orc, f).ok()
+
+
+def test_flags_scale_byte(case):
+    wl, orc = case
+    assert not planted(wl, orc, lambda b, rec, scl: b.__setitem__(scl + 2, b[scl + 2] + 1)).ok()
+
+
+def test_flags_pad_byte(case):
+    wl, orc = case
+    assert not planted(wl, orc, lambda b, rec, scl: b.__setitem__(scl + 7, 1)).ok()
+
+
+def test_flags_rope_far_off(case):
+    wl, orc = case
+
+    def f(b, rec, scl):
+        v = b[rec + 448:rec + 576].view("<u2")
+        i = int(np.argmax(np.abs((v.astype(np.uint32) << 16).view(np.float32))))
+        v[i] = v[i] + 3 if (v[i] & 0x7FFF) < 0x7F00 else v[i] - 3
+    assert not planted(wl, orc, f).ok()
+
+
+def test_flags_write_outside_records(case):
+    wl, orc = case
+    body = orc.k_cache_base.copy()
+    written = np.zeros(body.size, bool)
+    for s in wl.kv_slot_mapping:
+        rec, scl = record_offsets(int(s), wl.k_cache.shape[1], wl.k_cache.strides[0])
+        written[rec:rec + 576] = True
+        written[scl:scl + 8] = True
+    idx = int(np.nonzero(~written)[0][0])
+    body[idx] ^= 0xFF
+    assert not compare(wl, body, orc).ok()
+
+
+def test_flags_compressed_error(case):
+    wl, orc = case
+    g = orc.compressed.astype(np.float32).copy()
+    g[3, 100] += np.float32(1e-3)
+    assert not compare(wl, orc.k_cache_base.copy(), orc, gpu_compressed=g).ok()
