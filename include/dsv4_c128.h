@@ -46,7 +46,7 @@
  *   cos_sin         f32 [P, >= 64]     stride[1] == 1; cos in [0,32), sin in [32,64)
  *   k_cache         u8  [B, bs, 584]   stride[2] == 1, stride[1] == 584,
  *                                      stride[0] >= bs*584 and a multiple of
- *                                      16; data 16-byte aligned.  Only bs and
+ *                                      8; data 8-byte aligned.  Only bs and
  *                                      stride[0] give the layout: the view is a
  *                                      byte container for the block format above
  *   kv_slot_mapping i32 [T]            contiguous
@@ -88,7 +88,7 @@ enum dsv4_status {
                            or a size above INT32_MAX */
   DSV4_ERR_STRIDE = -5, /* inner stride != 1, overlapping rows/blocks, k_cache stride[0]
                            below bs*584 */
-  DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the 16-byte alignment above */
+  DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the alignment stated above */
   DSV4_ERR_LAUNCH = -7  /* the HIP runtime reported an error at launch */
 };
 

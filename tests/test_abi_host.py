@@ -79,6 +79,12 @@ def padded(shape, dtype, pad_last=0, pad_dim0=0):
     return big[tuple(slice(0, s) for s in shape)]
 
 
+def test_kv_block_size_one_passes():
+    """bs = 1 gives a 584-byte block stride: 8-byte aligned, which is all the stores need."""
+    a = valid_args(bs=1)
+    assert call_validate(a) == 0, c128.last_error()
+
+
 def test_padded_views_pass():
     a = valid_args()
     a["state_cache"] = torch.zeros(32, 8, 1024 + 64)[:, :, :1024]
@@ -127,9 +133,9 @@ CASES = [
     ("k_cache stride0 small", lambda a: a.update(k_cache=torch.as_strided(
         torch.zeros(8 * 584, dtype=torch.uint8), (2, 4, 584), (3 * 584, 584, 1))), -5),
     ("k_cache stride0 unaligned", lambda a: a.update(k_cache=torch.as_strided(
-        torch.zeros(2 * (4 * 584 + 8), dtype=torch.uint8), (2, 4, 584), (4 * 584 + 8, 584, 1))), -6),
+        torch.zeros(2 * (4 * 584 + 4), dtype=torch.uint8), (2, 4, 584), (4 * 584 + 4, 584, 1))), -6),
     ("k_cache base unaligned", lambda a: a.update(k_cache=torch.zeros(
-        2 * 4 * 584 + 1, dtype=torch.uint8)[1:].view(2, 4, 584)), -6),
+        2 * 4 * 584 + 4, dtype=torch.uint8)[4:].view(2, 4, 584)), -6),
     ("negative eps", lambda a: a.update(eps=-1.0), -4),
     ("nan eps", lambda a: a.update(eps=float("nan")), -4),
 ]
