@@ -179,14 +179,12 @@ def test_out_of_range_device_indices_write_nothing():
     """Indices that live in device memory and are out of range (request, block id, kv slot,
     RoPE row) make the kernel skip the token: nothing is written, no fault."""
     wl = small(T=6, seed=19, cs_rows=1024)
+    wl.positions[:] = 127                               # window 0, RoPE row 0 ...
+    wl.positions[4] = 1023                              # ... except token 4: RoPE row 896
     wl.token_to_req[0] = wl.block_table.shape[0]        # request out of range
-    r1 = int(wl.positions[1]) // 8
-    wl.block_table[1, r1] = wl.state.shape[0] + 5       # a window block id out of range
+    wl.block_table[1, 15] = wl.state.shape[0] + 5       # a window block id out of range
     wl.kv_slot_mapping[2] = wl.k_cache.shape[0] * wl.k_cache.shape[1]  # kv slot out of range
     wl.cos_sin = wl.cos_sin[:128].copy()                # RoPE rows 0..127 only
-    wl.positions[3] = 127
-    wl.positions[4] = 1023                              # needs RoPE row 896: out of range
-    wl.positions[5] = 127
     announce("out-of-range device indices")
     body, comp, guards_ok = run_gpu(wl, debug=True)
     assert guards_ok
