@@ -13,8 +13,9 @@ timing starts.
 Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
 ``--sweep PATH`` also writes per-workload JSONL (decode sweep 1..4096 tokens,
 single-token, decode batch, varlen prefill) with warm and cold timings.
-``--mode copy`` times a plain device-to-device copy (streaming reference line
-and the counter-calibration kernel for rocprofv3).
+``--mode copy`` times a plain device-to-device copy (the counter-calibration
+kernel for rocprofv3); ``--mode read`` times a plain streaming read (the
+attainable-bandwidth reference line).
 """
 
 from __future__ import annotations
@@ -226,7 +227,8 @@ def cpu_baseline(wl, gpu_body, nbytes):
 
 def sweep(args, path):
     """Per-workload timings (warm: back-to-back calls rotating over disjoint window sets;
-    cold: a 1 GiB buffer is overwritten before each individually timed call)."""
+    cold: a 1 GiB buffer is read (a sum) before each individually timed call, which evicts the
+    256 MiB MALL and the L2s with clean lines)."""
     import torch
 
     import paged_kv_cache_fp32_amd as c128
@@ -236,10 +238,11 @@ def sweep(args, path):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     sid = stream.cuda_stream
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def flush():
-        scratch.fill_(1.0)
+        torch.sum(scratch, dtype=torch.float32, out=sink)
 
     out = open(path, "w")
 
@@ -283,6 +286,23 @@ def sweep(args, path):
     out.close()
 
 
+def read_line(args):
+    """Plain streaming read of 4 GiB (torch's sum reduction): the attainable read bandwidth
+    reference of this box."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 30  # floats
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    reg, per = time_calls(torch, stream, [lambda: torch.sum(src, dtype=torch.float32, out=sink)],
+                          args.steps, args.warmup)
+    ms = float(np.median(per))
+    print(json.dumps({"mode": "read", "bytes_read_per_launch": 4 * n,
+                      "kernel_median_us": round(ms * 1e3, 2),
+                      "gbs_read": round(4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def copy_line(args):
     """Plain device-to-device copy of 4 GiB: the streaming reference and the calibration
     kernel for the HBM counters (reads 4 GiB, writes 4 GiB per launch)."""
@@ -308,7 +328,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["main", "copy"], default="main")
+    ap.add_argument("--mode", choices=["main", "copy", "read"], default="main")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the C128 compress-store path shards by request "
@@ -319,6 +339,8 @@ def main():
         sys.exit("--steps must be >= 1")
     if args.mode == "copy":
         copy_line(args)
+    elif args.mode == "read":
+        read_line(args)
     else:
         main_line(args)
 
