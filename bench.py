@@ -242,7 +242,7 @@ def sweep(args, path):
     sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def flush():
-        torch.sum(scratch, dtype=torch.float32, out=sink)
+        torch.sum(scratch, dim=0, out=sink)
 
     out = open(path, "w")
 
@@ -295,7 +295,7 @@ def read_line(args):
     src = torch.ones(n, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    reg, per = time_calls(torch, stream, [lambda: torch.sum(src, dtype=torch.float32, out=sink)],
+    reg, per = time_calls(torch, stream, [lambda: torch.sum(src, dim=0, out=sink)],
                           args.steps, args.warmup)
     ms = float(np.median(per))
     print(json.dumps({"mode": "read", "bytes_read_per_launch": 4 * n,
