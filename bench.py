@@ -287,20 +287,55 @@ def sweep(args, path):
 
 
 def read_line(args):
-    """Plain streaming read of 4 GiB (torch's sum reduction): the attainable read bandwidth
-    reference of this box."""
+    """Attainable-bandwidth references on this machine (bench_support probes): a plain
+    sequential streaming read of 4 GiB (best of a few launch shapes), and a read of the
+    16-block windows of the 16384-token workload with the compress kernel's lane mapping
+    but none of its arithmetic."""
+    import ctypes
+
     import torch
+
+    import bench_support
+    import synth
+    from synth.device import DeviceWorkload
+
+    L = bench_support.lib()
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
     n = 1 << 30  # floats
     src = torch.ones(n, dtype=torch.float32, device=dev)
-    sink = torch.empty((), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    reg, per = time_calls(torch, stream, [lambda: torch.sum(src, dim=0, out=sink)],
-                          args.steps, args.warmup)
+    out = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+    rec = {"mode": "read", "stream_bytes": 4 * n}
+    best = None
+    for blocks, threads in ((1024, 512), (2048, 512), (4096, 256), (8192, 256), (2048, 256)):
+        def call(b=blocks, t=threads):
+            assert L.probe_stream_read(src.data_ptr(), 4 * n, out.data_ptr(), b, t, sid) == 0
+        _, per = time_calls(torch, stream, [call], args.steps, args.warmup)
+        gbs = 4 * n / (float(np.median(per)) * 1e-3) / 1e9
+        rec[f"stream_gbs_{blocks}x{threads}"] = round(gbs, 1)
+        best = gbs if best is None else max(best, gbs)
+    rec["stream_gbs_best"] = round(best, 1)
+    del src
+    torch.cuda.empty_cache()
+    wl = synth.config4()
+    d = DeviceWorkload(wl, device=dev)
+    T = wl.num_tokens
+    pos = wl.positions.astype(np.int64)
+    cols = (pos // 128)[:, None] * 16 + np.arange(16)[None, :]
+    ids = np.ascontiguousarray(wl.block_table[np.arange(T)[:, None], cols]).astype(np.int32)
+    ids_d = torch.from_numpy(ids).to(dev)
+    s0 = d.state.stride(0)
+
+    def gather():
+        assert L.probe_block_gather_read(d.state.data_ptr(), s0, ids_d.data_ptr(), T,
+                                         out.data_ptr(), sid) == 0
+    _, per = time_calls(torch, stream, [gather], args.steps, args.warmup)
     ms = float(np.median(per))
-    print(json.dumps({"mode": "read", "bytes_read_per_launch": 4 * n,
-                      "kernel_median_us": round(ms * 1e3, 2),
-                      "gbs_read": round(4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    rec["gather_bytes"] = T * 128 * 4096
+    rec["gather_us"] = round(ms * 1e3, 2)
+    rec["gather_gbs"] = round(T * 128 * 4096 / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(rec), flush=True)
 
 
 def copy_line(args):

@@ -1,0 +1,35 @@
+"""Read-bandwidth reference probes used by bench.py (not part of the C128 library)."""
+import ctypes
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "stream_probe.hip")
+LIB = os.path.join(HERE, "libstream_probe.so")
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIB):
+        from paged_kv_cache_fp32_amd.build import HIPCC_FLAGS, hipcc
+        tmp = LIB + ".tmp"
+        subprocess.check_call([hipcc(), *HIPCC_FLAGS, SRC, "-o", tmp])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise ImportError(f"{LIB} missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.probe_stream_read.argtypes = [vp, i64, vp, ci, ci, vp]
+        L.probe_stream_read.restype = ci
+        L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, vp]
+        L.probe_block_gather_read.restype = ci
+        _lib = L
+    return _lib
