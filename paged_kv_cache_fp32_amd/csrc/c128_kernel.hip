@@ -84,8 +84,6 @@ __device__ __forceinline__ float group16_max(float v) {
   return v;
 }
 
-constexpr int kChunk = 4;  // rows per pipeline stage
-
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // State rows are read exactly once per call: load them with the non-temporal hint
@@ -96,31 +94,31 @@ __device__ __forceinline__ float4 load_stream(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void load_rows(float4 (&kv)[kChunk], float4 (&sc)[kChunk],
-                                          const float* rp, int64_t s1) {
+template <int CH>
+__device__ __forceinline__ void load_rows(float4 (&kv)[CH], float4 (&sc)[CH], const float* rp,
+                                          int64_t s1) {
 #pragma unroll
-  for (int r = 0; r < kChunk; ++r) {
+  for (int r = 0; r < CH; ++r) {
     kv[r] = load_stream(rp + r * s1);
     sc[r] = load_stream(rp + r * s1 + kHead);
   }
 }
 
-// Online softmax update of one column with kChunk rows.
-template <int C, bool kFirst>
-__device__ __forceinline__ void update_column(const float4 (&kv)[kChunk],
-                                              const float4 (&sc)[kChunk], float& ml, float& l,
-                                              float& acc) {
-  float s[kChunk];
+// Online softmax update of one column with CH rows.
+template <int C, bool kFirst, int CH>
+__device__ __forceinline__ void update_column(const float4 (&kv)[CH], const float4 (&sc)[CH],
+                                              float& ml, float& l, float& acc) {
+  float s[CH];
 #pragma unroll
-  for (int r = 0; r < kChunk; ++r) s[r] = lane_of<C>(sc[r]);
+  for (int r = 0; r < CH; ++r) s[r] = lane_of<C>(sc[r]);
   float cm = s[0];
 #pragma unroll
-  for (int r = 1; r < kChunk; ++r) cm = __builtin_fmaxf(cm, s[r]);
+  for (int r = 1; r < CH; ++r) cm = __builtin_fmaxf(cm, s[r]);
   cm *= kLog2e;
   const float mn = kFirst ? cm : __builtin_fmaxf(ml, cm);
   float psum = 0.0f, a = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kChunk; ++r) {
+  for (int r = 0; r < CH; ++r) {
     const float pr = exp2_fast(__builtin_fmaf(s[r], kLog2e, -mn));
     psum += pr;
     a = __builtin_fmaf(pr, lane_of<C>(kv[r]), a);
@@ -136,21 +134,24 @@ __device__ __forceinline__ void update_column(const float4 (&kv)[kChunk],
   ml = mn;
 }
 
-template <bool kFirst>
-__device__ __forceinline__ void update(const float4 (&kv)[kChunk], const float4 (&sc)[kChunk],
+template <bool kFirst, int CH>
+__device__ __forceinline__ void update(const float4 (&kv)[CH], const float4 (&sc)[CH],
                                        float (&ml)[4], float (&l)[4], float (&acc)[4]) {
-  update_column<0, kFirst>(kv, sc, ml[0], l[0], acc[0]);
-  update_column<1, kFirst>(kv, sc, ml[1], l[1], acc[1]);
-  update_column<2, kFirst>(kv, sc, ml[2], l[2], acc[2]);
-  update_column<3, kFirst>(kv, sc, ml[3], l[3], acc[3]);
+  update_column<0, kFirst, CH>(kv, sc, ml[0], l[0], acc[0]);
+  update_column<1, kFirst, CH>(kv, sc, ml[1], l[1], acc[1]);
+  update_column<2, kFirst, CH>(kv, sc, ml[2], l[2], acc[2]);
+  update_column<3, kFirst, CH>(kv, sc, ml[3], l[3], acc[3]);
 }
 
-template <int RG, bool kDebug>
+// RG: row groups (the workgroup has 2*RG waves); CH: rows per pipeline stage.
+template <int RG, int CH, bool kDebug>
 __global__ void __launch_bounds__(128 * RG)
 c128_compress_store_kernel(const C128Params p) {
   static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
+  static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
   constexpr int NB = kWindowBlocks / RG;                 // state blocks per wave
-  constexpr int NCH = NB * kStateBlock / kChunk;         // chunks per wave (even)
+  constexpr int NCH = NB * kStateBlock / CH;             // stages per wave (even)
+  constexpr int kStagesPerBlock = kStateBlock / CH;
   static_assert(NCH % 2 == 0, "ping-pong needs an even chunk count");
 
   __shared__ float4 lds_ml[RG][2][64];
@@ -190,22 +191,22 @@ c128_compress_store_kernel(const C128Params p) {
   const float* colbase = p.state + col;
   const int64_t s0 = p.s0, s1 = p.s1;
   auto rowptr = [&](int ch) {
-    return colbase + static_cast<int64_t>(mybt[ch >> 1]) * s0 +
-           static_cast<int64_t>((ch & 1) * kChunk) * s1;
+    return colbase + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
+           static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
   };
 
   float ml[4], l[4], acc[4];
-  float4 kvA[kChunk], scA[kChunk], kvB[kChunk], scB[kChunk];
-  load_rows(kvA, scA, rowptr(0), s1);
+  float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
+  load_rows<CH>(kvA, scA, rowptr(0), s1);
 #pragma unroll
   for (int ch = 0; ch < NCH; ch += 2) {
-    load_rows(kvB, scB, rowptr(ch + 1), s1);
+    load_rows<CH>(kvB, scB, rowptr(ch + 1), s1);
     if (ch == 0)
-      update<true>(kvA, scA, ml, l, acc);
+      update<true, CH>(kvA, scA, ml, l, acc);
     else
-      update<false>(kvA, scA, ml, l, acc);
-    if (ch + 2 < NCH) load_rows(kvA, scA, rowptr(ch + 2), s1);
-    update<false>(kvB, scB, ml, l, acc);
+      update<false, CH>(kvA, scA, ml, l, acc);
+    if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1);
+    update<false, CH>(kvB, scB, ml, l, acc);
   }
 
   // ---- merge the RG row groups of each column half
@@ -333,6 +334,7 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
 }
 
 constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
+constexpr int kStageRows = 4;  // rows per pipeline stage
 
 }  // namespace
 
@@ -341,9 +343,9 @@ hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.num_tokens));
   const dim3 block(128 * kRowGroups);
   if (p.compressed_out)
-    c128_compress_store_kernel<kRowGroups, true><<<grid, block, 0, stream>>>(p);
+    c128_compress_store_kernel<kRowGroups, kStageRows, true><<<grid, block, 0, stream>>>(p);
   else
-    c128_compress_store_kernel<kRowGroups, false><<<grid, block, 0, stream>>>(p);
+    c128_compress_store_kernel<kRowGroups, kStageRows, false><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
 }
 
