@@ -94,13 +94,16 @@ __device__ __forceinline__ float4 load_stream(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// CH rows starting at the wave-uniform row pointer `row` (SGPRs); the lane adds only its
+// 32-bit column offset, so each load is the saddr + voffset form with no per-row VGPR address.
 template <int CH>
-__device__ __forceinline__ void load_rows(float4 (&kv)[CH], float4 (&sc)[CH], const float* rp,
-                                          int64_t s1) {
+__device__ __forceinline__ void load_rows(float4 (&kv)[CH], float4 (&sc)[CH], const float* row,
+                                          int64_t s1, uint32_t col) {
 #pragma unroll
   for (int r = 0; r < CH; ++r) {
-    kv[r] = load_stream(rp + r * s1);
-    sc[r] = load_stream(rp + r * s1 + kHead);
+    const float* rp = row + r * s1;
+    kv[r] = load_stream(rp + col);
+    sc[r] = load_stream(rp + kHead + col);
   }
 }
 
@@ -143,9 +146,10 @@ __device__ __forceinline__ void update(const float4 (&kv)[CH], const float4 (&sc
   update_column<3, kFirst, CH>(kv, sc, ml[3], l[3], acc[3]);
 }
 
-// RG: row groups (the workgroup has 2*RG waves); CH: rows per pipeline stage.
-template <int RG, int CH, bool kDebug>
-__global__ void __launch_bounds__(128 * RG)
+// RG: row groups (the workgroup has 2*RG waves); CH: rows per pipeline stage; WPE: waves per
+// SIMD the register allocation must allow (it bounds the VGPRs, hence the loads in flight).
+template <int RG, int CH, int WPE, bool kDebug>
+__global__ void __launch_bounds__(128 * RG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 c128_compress_store_kernel(const C128Params p) {
   static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
   static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
@@ -187,25 +191,25 @@ c128_compress_store_kernel(const C128Params p) {
 
   // ---- stream this wave's NB blocks x 8 rows, 4 rows per stage
   const int col = half * 256 + lane * 4;
+  const uint32_t ucol = static_cast<uint32_t>(col);
   const int32_t* mybt = bt + rg * NB;
-  const float* colbase = p.state + col;
   const int64_t s0 = p.s0, s1 = p.s1;
-  auto rowptr = [&](int ch) {
-    return colbase + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
+  auto rowptr = [&](int ch) {  // wave-uniform
+    return p.state + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
            static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
   };
 
   float ml[4], l[4], acc[4];
   float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
-  load_rows<CH>(kvA, scA, rowptr(0), s1);
+  load_rows<CH>(kvA, scA, rowptr(0), s1, ucol);
 #pragma unroll
   for (int ch = 0; ch < NCH; ch += 2) {
-    load_rows<CH>(kvB, scB, rowptr(ch + 1), s1);
+    load_rows<CH>(kvB, scB, rowptr(ch + 1), s1, ucol);
     if (ch == 0)
       update<true, CH>(kvA, scA, ml, l, acc);
     else
       update<false, CH>(kvA, scA, ml, l, acc);
-    if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1);
+    if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1, ucol);
     update<false, CH>(kvB, scB, ml, l, acc);
   }
 
@@ -219,37 +223,26 @@ c128_compress_store_kernel(const C128Params p) {
   float c[4] = {0.f, 0.f, 0.f, 0.f};
   if (rg == 0) {
     if constexpr (RG > 1) {
-      float4 gm[RG], gl[RG], ga[RG];
-#pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        gm[g] = lds_ml[g][half][lane];
-        gl[g] = lds_l[g][half][lane];
-        ga[g] = lds_acc[g][half][lane];
-      }
-      float M[4] = {gm[0].x, gm[0].y, gm[0].z, gm[0].w};
+      // fold the other row groups into this wave's (m, l, acc) one at a time
 #pragma unroll
       for (int g = 1; g < RG; ++g) {
-        M[0] = __builtin_fmaxf(M[0], gm[g].x);
-        M[1] = __builtin_fmaxf(M[1], gm[g].y);
-        M[2] = __builtin_fmaxf(M[2], gm[g].z);
-        M[3] = __builtin_fmaxf(M[3], gm[g].w);
-      }
-      float L[4] = {0.f, 0.f, 0.f, 0.f}, A[4] = {0.f, 0.f, 0.f, 0.f};
+        const float4 gm = lds_ml[g][half][lane];
+        const float4 gl = lds_l[g][half][lane];
+        const float4 ga = lds_acc[g][half][lane];
+        const float om[4] = {gm.x, gm.y, gm.z, gm.w};
+        const float ol[4] = {gl.x, gl.y, gl.z, gl.w};
+        const float oa[4] = {ga.x, ga.y, ga.z, ga.w};
 #pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        const float f0 = exp2_fast(gm[g].x - M[0]), f1 = exp2_fast(gm[g].y - M[1]);
-        const float f2 = exp2_fast(gm[g].z - M[2]), f3 = exp2_fast(gm[g].w - M[3]);
-        L[0] = __builtin_fmaf(gl[g].x, f0, L[0]);
-        L[1] = __builtin_fmaf(gl[g].y, f1, L[1]);
-        L[2] = __builtin_fmaf(gl[g].z, f2, L[2]);
-        L[3] = __builtin_fmaf(gl[g].w, f3, L[3]);
-        A[0] = __builtin_fmaf(ga[g].x, f0, A[0]);
-        A[1] = __builtin_fmaf(ga[g].y, f1, A[1]);
-        A[2] = __builtin_fmaf(ga[g].z, f2, A[2]);
-        A[3] = __builtin_fmaf(ga[g].w, f3, A[3]);
+        for (int k = 0; k < 4; ++k) {
+          const float M = __builtin_fmaxf(ml[k], om[k]);
+          const float fs = exp2_fast(ml[k] - M), fo = exp2_fast(om[k] - M);
+          l[k] = __builtin_fmaf(l[k], fs, ol[k] * fo);
+          acc[k] = __builtin_fmaf(acc[k], fs, oa[k] * fo);
+          ml[k] = M;
+        }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = A[k] / L[k];
+      for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
@@ -335,6 +328,7 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
 
 constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
 constexpr int kStageRows = 4;  // rows per pipeline stage
+constexpr int kWavesPerSimd = 8;
 
 }  // namespace
 
@@ -343,9 +337,11 @@ hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.num_tokens));
   const dim3 block(128 * kRowGroups);
   if (p.compressed_out)
-    c128_compress_store_kernel<kRowGroups, kStageRows, true><<<grid, block, 0, stream>>>(p);
+    c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, true>
+        <<<grid, block, 0, stream>>>(p);
   else
-    c128_compress_store_kernel<kRowGroups, kStageRows, false><<<grid, block, 0, stream>>>(p);
+    c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, false>
+        <<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
 }
 
