@@ -67,13 +67,14 @@
 #ifndef DSV4_C128_H
 #define DSV4_C128_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 1
+#define DSV4_ABI_VERSION 2
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -89,7 +90,8 @@ enum dsv4_status {
   DSV4_ERR_STRIDE = -5, /* inner stride != 1, overlapping rows/blocks, k_cache stride[0]
                            below bs*584 */
   DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the alignment stated above */
-  DSV4_ERR_LAUNCH = -7  /* the HIP runtime reported an error at launch */
+  DSV4_ERR_LAUNCH = -7, /* the HIP runtime reported an error at launch */
+  DSV4_ERR_ARG = -8     /* an argument outside its documented set (splits, workspace size) */
 };
 
 typedef struct dsv4_tensor {
@@ -126,6 +128,41 @@ int dsv4_c128_compress_store_debug(const dsv4_tensor* state_cache,
                                    const dsv4_tensor* k_cache,
                                    const dsv4_tensor* kv_slot_mapping, float* compressed_out,
                                    void* stream);
+
+/*
+ * Small-batch fan-out.  The same computation as dsv4_c128_compress_store, with each token's 16
+ * window blocks split over `splits` workgroups (grid T x splits) that write partial softmax
+ * states to `workspace`; a second, stream-ordered kernel merges them per token and runs the
+ * epilogue.  It exists because one workgroup per token leaves most of the 256 CUs idle when
+ * T is small (decode batches of up to a few hundred tokens); the pages' own split kernel
+ * (vLLM fused_compress_quant_cache page, `_compress_gather_split_sparse_attn` and
+ * `_pick_compress_num_splits`) has the same purpose.
+ *
+ *   splits          0 = the library's choice for T (see dsv4_c128_workspace_bytes), or 1, 2,
+ *                   4, 8, 16.  1 is the single-pass kernel.
+ *   workspace       device memory of at least dsv4_c128_workspace_bytes(T, splits) bytes,
+ *                   16-byte aligned, owned by the caller; its contents need no initialisation
+ *                   and are scratch after the call.  Calls that share a workspace must be
+ *                   ordered on one stream.  With splits == 0 and no (or too small a) workspace
+ *                   the single pass runs; with explicit splits > 1 it is DSV4_ERR_ARG.
+ *   compressed_out  NULL, or as in dsv4_c128_compress_store_debug.
+ *
+ * k_cache results equal the single pass's up to the fp32 summation order of the pooling.
+ */
+int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                void* workspace, size_t workspace_bytes, int splits, void* stream);
+
+/*
+ * Bytes of workspace dsv4_c128_compress_store_ex needs for num_tokens tokens and `splits`
+ * (0 = the library's choice: 1 for num_tokens >= 512, else the smallest power of two up to 16
+ * with num_tokens * splits >= 1024).  0 when no workspace is needed or splits is not valid.
+ * Host-only; no HIP call.
+ */
+size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);
 
 /*
  * Host-only validation of the descriptors, exactly as the compute entry

@@ -30,6 +30,7 @@ ERRORS = {
     -5: "DSV4_ERR_STRIDE",
     -6: "DSV4_ERR_ALIGN",
     -7: "DSV4_ERR_LAUNCH",
+    -8: "DSV4_ERR_ARG",
 }
 _DTYPES = {torch.float32: DSV4_F32, torch.int32: DSV4_I32, torch.uint8: DSV4_U8}
 
@@ -86,6 +87,11 @@ def library():
         lib.dsv4_c128_compress_store.restype = ctypes.c_int
         lib.dsv4_c128_compress_store_debug.argtypes = args10 + [ctypes.c_void_p, ctypes.c_void_p]
         lib.dsv4_c128_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_c128_compress_store_ex.argtypes = args10 + [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+        lib.dsv4_c128_compress_store_ex.restype = ctypes.c_int
+        lib.dsv4_c128_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int]
+        lib.dsv4_c128_workspace_bytes.restype = ctypes.c_size_t
         lib.dsv4_c128_validate.argtypes = args10
         lib.dsv4_c128_validate.restype = ctypes.c_int
         lib.dsv4_e4m3_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -162,6 +168,38 @@ def compress_store_debug(state_cache, block_table, token_to_req, positions, slot
                                                     compressed_out.data_ptr(), s))
 
 
+def workspace_bytes(num_tokens: int, splits: int = 0) -> int:
+    """Workspace bytes ``compress_store_ex`` needs for ``num_tokens`` tokens and ``splits``
+    workgroups per token (0 = the library's choice); 0 when none is needed."""
+    return int(library().dsv4_c128_workspace_bytes(int(num_tokens), int(splits)))
+
+
+def compress_store_ex(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                      cos_sin, k_cache, kv_slot_mapping, compressed_out=None, workspace=None,
+                      splits: int = 0, stream: int | None = None) -> None:
+    """``compress_store`` with the small-batch fan-out: each token's window is split over
+    ``splits`` workgroups (0 = automatic; 1 = single pass) whose partial states go to
+    ``workspace`` (a device tensor of at least ``workspace_bytes(T, splits)`` bytes), then merged
+    per token.  ``compressed_out`` as in ``compress_store_debug``."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    extra = [t for t in (compressed_out, workspace) if t is not None]
+    dev = _require_cuda(ts + extra)
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 512)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_c128_compress_store_ex(*refs[:6], float(eps), *refs[6:], out_ptr,
+                                                 ws_ptr, ws_len, int(splits), s))
+
+
 def validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
              cos_sin, k_cache, kv_slot_mapping) -> int:
     """Host-only validation of the descriptors (no HIP call); returns the status code."""
@@ -183,5 +221,6 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
     return out
 
 
-__all__ = ["compress_store", "compress_store_debug", "validate", "e4m3_encode", "last_error",
+__all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
+           "validate", "e4m3_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

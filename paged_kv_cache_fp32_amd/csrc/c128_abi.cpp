@@ -224,6 +224,50 @@ int dsv4_c128_compress_store_debug(const dsv4_tensor* state_cache,
   return run(p, stream);
 }
 
+size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits) {
+  if (num_tokens <= 0) return 0;
+  if (splits == 0) splits = dsv4::fanout_auto_splits(num_tokens);
+  if (splits != 1 && splits != 2 && splits != 4 && splits != 8 && splits != 16) return 0;
+  return dsv4::fanout_workspace_bytes(num_tokens, splits);
+}
+
+int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                void* workspace, size_t workspace_bytes, int splits,
+                                void* stream) {
+  dsv4::C128Params p;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p);
+  if (rc) return rc;
+  if (splits != 0 && splits != 1 && splits != 2 && splits != 4 && splits != 8 && splits != 16)
+    return fail(DSV4_ERR_ARG, "splits must be 0 (automatic), 1, 2, 4, 8 or 16 (got %d)", splits);
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  int s = splits;
+  if (s == 0) {
+    s = dsv4::fanout_auto_splits(p.num_tokens);
+    if (s > 1 && (!workspace || workspace_bytes < dsv4::fanout_workspace_bytes(p.num_tokens, s)))
+      s = 1;  // automatic mode never fails for want of a workspace: single pass
+  }
+  if (s > 1) {
+    const size_t need = dsv4::fanout_workspace_bytes(p.num_tokens, s);
+    if (!workspace || workspace_bytes < need)
+      return fail(DSV4_ERR_ARG, "workspace of %zu bytes is too small: %d splits need %zu",
+                  workspace_bytes, s, need);
+    if (!aligned16(workspace)) return fail(DSV4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  p.compressed_out = compressed_out;
+  hipError_t err = dsv4::launch_c128_fanout(p, static_cast<float*>(workspace), s,
+                                            static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (n < 0) return fail(DSV4_ERR_SHAPE, "n must be >= 0");
   if (n == 0) return DSV4_OK;

@@ -146,60 +146,54 @@ __device__ __forceinline__ void update(const float4 (&kv)[CH], const float4 (&sc
   update_column<3, kFirst, CH>(kv, sc, ml[3], l[3], acc[3]);
 }
 
-// RG: row groups (the workgroup has 2*RG waves); CH: rows per pipeline stage; WPE: waves per
-// SIMD the register allocation must allow (it bounds the VGPRs, hence the loads in flight).
-template <int RG, int CH, int WPE, bool kDebug>
-__global__ void __launch_bounds__(128 * RG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-c128_compress_store_kernel(const C128Params p) {
-  static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
-  static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
-  constexpr int NB = kWindowBlocks / RG;                 // state blocks per wave
-  constexpr int NCH = NB * kStateBlock / CH;             // stages per wave (even)
-  constexpr int kStagesPerBlock = kStateBlock / CH;
-  static_assert(NCH % 2 == 0, "ping-pong needs an even chunk count");
+// ---------------------------------------------------------------------------------------------
+// Pieces shared by the single-pass kernel and the two fan-out kernels.
 
-  __shared__ float4 lds_ml[RG][2][64];
-  __shared__ float4 lds_l[RG][2][64];
-  __shared__ float4 lds_acc[RG][2][64];
-  __shared__ float lds_ss[2];
+// Gate of token t and its window, all wave-uniform: active iff the state slot is >= 0 and the
+// position closes a window; then request, window columns, RoPE row and the 16 block ids must be
+// in range (device-resident values the host cannot check), else the token is skipped.
+struct Window {
+  bool ok;
+  int32_t rope_row;      // (pos // 128) * 128
+  const int32_t* bt;     // the window's 16 block ids
+};
 
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = wave & 1;
-  const int rg = wave >> 1;
-
-  // ---- gate (all values wave-uniform; the whole workgroup takes one path)
+__device__ __forceinline__ Window gate_and_window(const C128Params& p, int32_t t) {
+  Window w{false, 0, nullptr};
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
-  if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return;
+  if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return w;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
   const int32_t req = p.token_to_req[t];
-  if (req < 0 || req >= p.bt_rows ||
-      static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
-    return;
-  const int32_t rope_row = win * kRatio;  // (pos // 128) * 128
-  if (rope_row >= p.cs_rows) return;
-  const int32_t* bt =
-      p.block_table + static_cast<int64_t>(req) * p.bt_stride +
-      static_cast<int64_t>(win) * kWindowBlocks;
+  if (req < 0 || req >= p.bt_rows || static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
+    return w;
+  w.rope_row = win * kRatio;
+  if (w.rope_row >= p.cs_rows) return w;
+  w.bt = p.block_table + static_cast<int64_t>(req) * p.bt_stride +
+         static_cast<int64_t>(win) * kWindowBlocks;
   bool ok = true;
 #pragma unroll
   for (int i = 0; i < kWindowBlocks; ++i)
-    ok &= static_cast<uint32_t>(bt[i]) < static_cast<uint32_t>(p.n_state_blocks);
-  if (!ok) return;
+    ok &= static_cast<uint32_t>(w.bt[i]) < static_cast<uint32_t>(p.n_state_blocks);
+  w.ok = ok;
+  return w;
+}
 
-  // ---- stream this wave's NB blocks x 8 rows, 4 rows per stage
-  const int col = half * 256 + lane * 4;
-  const uint32_t ucol = static_cast<uint32_t>(col);
-  const int32_t* mybt = bt + rg * NB;
+// Stream NBW state blocks (ids mybt[0..NBW)) x 8 rows, CH rows per stage, into this lane's
+// online-softmax state (m in log2 units, l, acc) for its 4 columns.
+template <int NBW, int CH>
+__device__ __forceinline__ void stream_blocks(const C128Params& p, const int32_t* mybt,
+                                              uint32_t ucol, float (&ml)[4], float (&l)[4],
+                                              float (&acc)[4]) {
+  constexpr int kStagesPerBlock = kStateBlock / CH;
+  constexpr int NCH = NBW * kStagesPerBlock;  // stages (even)
+  static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
+  static_assert(NCH % 2 == 0, "ping-pong needs an even stage count");
   const int64_t s0 = p.s0, s1 = p.s1;
   auto rowptr = [&](int ch) {  // wave-uniform
     return p.state + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
            static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
   };
-
-  float ml[4], l[4], acc[4];
   float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
   load_rows<CH>(kvA, scA, rowptr(0), s1, ucol);
 #pragma unroll
@@ -212,51 +206,53 @@ c128_compress_store_kernel(const C128Params p) {
     if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1, ucol);
     update<false, CH>(kvB, scB, ml, l, acc);
   }
+}
 
-  // ---- merge the RG row groups of each column half
+// Fold another partial (m, l, acc) of the same 4 columns into this one.
+__device__ __forceinline__ void fold(float (&ml)[4], float (&l)[4], float (&acc)[4],
+                                     const float4& gm, const float4& gl, const float4& ga) {
+  const float om[4] = {gm.x, gm.y, gm.z, gm.w};
+  const float ol[4] = {gl.x, gl.y, gl.z, gl.w};
+  const float oa[4] = {ga.x, ga.y, ga.z, ga.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float M = __builtin_fmaxf(ml[k], om[k]);
+    const float fs = exp2_fast(ml[k] - M), fo = exp2_fast(om[k] - M);
+    l[k] = __builtin_fmaf(l[k], fs, ol[k] * fo);
+    acc[k] = __builtin_fmaf(acc[k], fs, oa[k] * fo);
+    ml[k] = M;
+  }
+}
+
+// Merge the RG row groups of each column half through LDS: on return the rg == 0 waves hold
+// the merged state.  Every wave of the workgroup must call it (it contains a barrier).
+template <int RG>
+__device__ __forceinline__ void merge_row_groups(float4 (&lds_ml)[RG][2][64],
+                                                 float4 (&lds_l)[RG][2][64],
+                                                 float4 (&lds_acc)[RG][2][64], int rg, int half,
+                                                 int lane, float (&ml)[4], float (&l)[4],
+                                                 float (&acc)[4]) {
   if constexpr (RG > 1) {
     lds_ml[rg][half][lane] = make_float4(ml[0], ml[1], ml[2], ml[3]);
     lds_l[rg][half][lane] = make_float4(l[0], l[1], l[2], l[3]);
     lds_acc[rg][half][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
-  }
-  float c[4] = {0.f, 0.f, 0.f, 0.f};
-  if (rg == 0) {
-    if constexpr (RG > 1) {
-      // fold the other row groups into this wave's (m, l, acc) one at a time
+    if (rg == 0) {
 #pragma unroll
-      for (int g = 1; g < RG; ++g) {
-        const float4 gm = lds_ml[g][half][lane];
-        const float4 gl = lds_l[g][half][lane];
-        const float4 ga = lds_acc[g][half][lane];
-        const float om[4] = {gm.x, gm.y, gm.z, gm.w};
-        const float ol[4] = {gl.x, gl.y, gl.z, gl.w};
-        const float oa[4] = {ga.x, ga.y, ga.z, ga.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float M = __builtin_fmaxf(ml[k], om[k]);
-          const float fs = exp2_fast(ml[k] - M), fo = exp2_fast(om[k] - M);
-          l[k] = __builtin_fmaf(l[k], fs, ol[k] * fo);
-          acc[k] = __builtin_fmaf(acc[k], fs, oa[k] * fo);
-          ml[k] = M;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
+      for (int g = 1; g < RG; ++g)
+        fold(ml, l, acc, lds_ml[g][half][lane], lds_l[g][half][lane], lds_acc[g][half][lane]);
     }
-    // RMSNorm sum of squares: this lane's 4 columns, then the wave
-    float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
-    ss = wave_sum(ss);
-    if (lane == 0) lds_ss[half] = ss;
   }
-  __syncthreads();
-  if (rg != 0) return;
+}
 
-  // ---- fused epilogue on the 128 lanes of row group 0
-  const float var = (lds_ss[0] + lds_ss[1]) * (1.0f / kHead);
+// Fused epilogue of token t on 128 lanes (2 waves, one per column half; 4 columns per lane):
+// RMSNorm, bf16 round trip, per-64 absmax -> UE8M0 exponent -> E4M3FN codes, GPT-J RoPE ->
+// bf16, paged insert.  sumsq is the sum of squares of all 512 pooled values.
+template <bool kDebug>
+__device__ __forceinline__ void epilogue(const C128Params& p, int32_t t, int32_t rope_row,
+                                         const float (&c)[4], int half, int lane, int col,
+                                         float sumsq) {
+  const float var = sumsq * (1.0f / kHead);
   const float rrms = 1.0f / __builtin_sqrtf(var + p.eps);
   const float4 w = *reinterpret_cast<const float4*>(p.rms_w + col);
   float n[4] = {c[0] * rrms * w.x, c[1] * rrms * w.y, c[2] * rrms * w.z, c[3] * rrms * w.w};
@@ -313,6 +309,126 @@ c128_compress_store_kernel(const C128Params p) {
   }
 }
 
+// c = acc / l, then the RMSNorm sum of squares over both column halves (one barrier), then the
+// epilogue on the 128 lanes of the first two waves.  Every wave must call it.
+template <bool kDebug>
+__device__ __forceinline__ void finish_token(const C128Params& p, int32_t t, int32_t rope_row,
+                                             bool epilogue_wave, int half, int lane, int col,
+                                             const float (&l)[4], const float (&acc)[4],
+                                             float* lds_ss) {
+  float c[4] = {0.f, 0.f, 0.f, 0.f};
+  if (epilogue_wave) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = acc[k] / l[k];
+    float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
+    ss = wave_sum(ss);
+    if (lane == 0) lds_ss[half] = ss;
+  }
+  __syncthreads();
+  if (epilogue_wave) epilogue<kDebug>(p, t, rope_row, c, half, lane, col, lds_ss[0] + lds_ss[1]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Single pass: one workgroup per token.
+// RG: row groups (the workgroup has 2*RG waves); CH: rows per pipeline stage; WPE: waves per
+// SIMD the register allocation must allow (it bounds the VGPRs, hence the loads in flight).
+template <int RG, int CH, int WPE, bool kDebug>
+__global__ void __launch_bounds__(128 * RG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+c128_compress_store_kernel(const C128Params p) {
+  static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
+  constexpr int NB = kWindowBlocks / RG;  // state blocks per wave
+
+  __shared__ float4 lds_ml[RG][2][64];
+  __shared__ float4 lds_l[RG][2][64];
+  __shared__ float4 lds_acc[RG][2][64];
+  __shared__ float lds_ss[2];
+
+  const int32_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int rg = wave >> 1;
+  const int col = half * 256 + lane * 4;
+
+  const Window win = gate_and_window(p, t);  // uniform: the whole workgroup takes one path
+  if (!win.ok) return;
+
+  float ml[4], l[4], acc[4];
+  stream_blocks<NB, CH>(p, win.bt + rg * NB, static_cast<uint32_t>(col), ml, l, acc);
+  merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
+  finish_token<kDebug>(p, t, win.rope_row, rg == 0, half, lane, col, l, acc, lds_ss);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fan-out for small batches: a token's 16 window blocks are split over S = RG*NBW... workgroups
+// (grid = T x S).  Workgroup (t, s) streams window blocks s*RG*NBW .. (s+1)*RG*NBW - 1 and
+// writes its merged partial state to the workspace:
+//   ws[((t * S + s) * 3 + {0: m (log2 units), 1: l, 2: acc}) * 512 + column].
+// The finish kernel then merges the S partials of each token and runs the epilogue.
+template <int RG, int NBW, int CH>
+__global__ void __launch_bounds__(128 * RG) c128_fanout_partial_kernel(const C128Params p,
+                                                                     float* __restrict__ ws) {
+  constexpr int kBlocksPerGroup = RG * NBW;
+  static_assert(kWindowBlocks % kBlocksPerGroup == 0, "splits must divide the window");
+  constexpr int S = kWindowBlocks / kBlocksPerGroup;
+
+  __shared__ float4 lds_ml[RG][2][64];
+  __shared__ float4 lds_l[RG][2][64];
+  __shared__ float4 lds_acc[RG][2][64];
+
+  const int32_t t = blockIdx.x;
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int rg = wave >> 1;
+  const int col = half * 256 + lane * 4;
+
+  const Window win = gate_and_window(p, t);
+  if (!win.ok) return;
+
+  float ml[4], l[4], acc[4];
+  stream_blocks<NBW, CH>(p, win.bt + s * kBlocksPerGroup + rg * NBW, static_cast<uint32_t>(col),
+                         ml, l, acc);
+  merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
+  if (rg == 0) {
+    float* out = ws + (static_cast<int64_t>(t) * S + s) * (3 * kHead) + col;
+    *reinterpret_cast<float4*>(out) = make_float4(ml[0], ml[1], ml[2], ml[3]);
+    *reinterpret_cast<float4*>(out + kHead) = make_float4(l[0], l[1], l[2], l[3]);
+    *reinterpret_cast<float4*>(out + 2 * kHead) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
+// One workgroup of 128 lanes per token: merge the S partials, then the fused epilogue.
+template <int S, bool kDebug>
+__global__ void __launch_bounds__(128) c128_fanout_finish_kernel(const C128Params p,
+                                                               const float* __restrict__ ws) {
+  __shared__ float lds_ss[2];
+  const int32_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = half * 256 + lane * 4;
+
+  const Window win = gate_and_window(p, t);  // the same decision the partial kernel took
+  if (!win.ok) return;
+
+  const float* in = ws + static_cast<int64_t>(t) * S * (3 * kHead) + col;
+  const float4 m0 = *reinterpret_cast<const float4*>(in);
+  const float4 l0 = *reinterpret_cast<const float4*>(in + kHead);
+  const float4 a0 = *reinterpret_cast<const float4*>(in + 2 * kHead);
+  float ml[4] = {m0.x, m0.y, m0.z, m0.w};
+  float l[4] = {l0.x, l0.y, l0.z, l0.w};
+  float acc[4] = {a0.x, a0.y, a0.z, a0.w};
+#pragma unroll
+  for (int s = 1; s < S; ++s) {
+    const float* q = in + s * (3 * kHead);
+    fold(ml, l, acc, *reinterpret_cast<const float4*>(q),
+         *reinterpret_cast<const float4*>(q + kHead),
+         *reinterpret_cast<const float4*>(q + 2 * kHead));
+  }
+  finish_token<kDebug>(p, t, win.rope_row, true, half, lane, col, l, acc, lds_ss);
+}
+
 __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8_t* out,
                                                           int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
@@ -343,6 +459,58 @@ hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
     c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, false>
         <<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+namespace {
+
+// Fan-out shapes: S splits of the 16 window blocks, each streamed by RG row groups of NBW blocks.
+template <int RG, int NBW>
+hipError_t launch_fanout(const C128Params& p, float* ws, hipStream_t stream) {
+  constexpr int S = kWindowBlocks / (RG * NBW);
+  const dim3 grid1(static_cast<unsigned>(p.num_tokens), S);
+  c128_fanout_partial_kernel<RG, NBW, kStageRows><<<grid1, dim3(128 * RG), 0, stream>>>(p, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 grid2(static_cast<unsigned>(p.num_tokens));
+  if (p.compressed_out)
+    c128_fanout_finish_kernel<S, true><<<grid2, dim3(128), 0, stream>>>(p, ws);
+  else
+    c128_fanout_finish_kernel<S, false><<<grid2, dim3(128), 0, stream>>>(p, ws);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fanout_auto_splits(int64_t num_tokens) {
+  // Enough workgroups to occupy the 256 CUs several times over; the single pass once the
+  // batch alone does that.
+  if (num_tokens <= 0 || num_tokens >= 512) return 1;
+  int s = 1;
+  while (s < kWindowBlocks && num_tokens * s < 1024) s *= 2;
+  return s;
+}
+
+size_t fanout_workspace_bytes(int64_t num_tokens, int splits) {
+  if (splits <= 1 || num_tokens <= 0) return 0;
+  return static_cast<size_t>(num_tokens) * static_cast<size_t>(splits) * 3 * kHead * sizeof(float);
+}
+
+hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  switch (splits) {
+    case 1:
+      return launch_c128_compress_store(p, stream);
+    case 2:
+      return launch_fanout<4, 2>(p, ws, stream);
+    case 4:
+      return launch_fanout<4, 1>(p, ws, stream);
+    case 8:
+      return launch_fanout<2, 1>(p, ws, stream);
+    case 16:
+      return launch_fanout<1, 1>(p, ws, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {

@@ -48,6 +48,11 @@ struct C128Params {
 
 // Launchers (c128_kernel.hip).  Return the hipError_t of the launch.
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
+// Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) with a
+// workspace of fanout_workspace_bytes(T, splits) bytes, 16-byte aligned.
+hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream);
+int fanout_auto_splits(int64_t num_tokens);
+size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace dsv4

@@ -51,14 +51,23 @@ class DeviceWorkload:
                 self.slot_mapping, self.rms_w, self.eps, self.cos_sin, self.k_cache,
                 self.kv_slot_mapping)
 
-    def run(self, debug=False):
+    def run(self, debug=False, splits=None):
+        """One call; splits None = the plain entry points, else compress_store_ex with that
+        split count (0 = automatic) and a workspace of the size it needs."""
         comp = None
         if debug:
             comp = torch.full((self.wl.num_tokens, 512), float("nan"), dtype=torch.float32,
                               device=self.state.device)
-            c128.compress_store_debug(*self.args(), comp)
+        if splits is None:
+            if debug:
+                c128.compress_store_debug(*self.args(), comp)
+            else:
+                c128.compress_store(*self.args())
         else:
-            c128.compress_store(*self.args())
+            nbytes = c128.workspace_bytes(self.wl.num_tokens, splits)
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.state.device)
+            c128.compress_store_ex(*self.args(), compressed_out=comp, workspace=ws,
+                                   splits=splits)
         torch.cuda.synchronize()
         return comp
 
@@ -70,8 +79,8 @@ class DeviceWorkload:
         return buf[g:-g].copy(), guards_ok
 
 
-def run_gpu(wl, debug=True):
+def run_gpu(wl, debug=True, splits=None):
     d = DeviceWorkload(wl)
-    comp = d.run(debug=debug)
+    comp = d.run(debug=debug, splits=splits)
     body, guards_ok = d.k_cache_bytes()
     return body, (comp.cpu().numpy() if comp is not None else None), guards_ok

@@ -203,3 +203,49 @@ def test_python_binding_rejects_host_tensors():
     a = valid_args()
     with pytest.raises(ValueError):
         c128.compress_store(**a)
+
+
+def test_workspace_bytes_rules():
+    """Automatic splits: 16 for tiny batches, halving until T*splits >= 1024, 1 (no workspace)
+    from 512 tokens on; explicit splits give T*splits*3*512 floats; invalid splits give 0."""
+    wb = c128.workspace_bytes
+    per = 3 * 512 * 4
+    assert wb(1, 0) == 1 * 16 * per
+    assert wb(64, 0) == 64 * 16 * per
+    assert wb(65, 0) == 65 * 16 * per
+    assert wb(128, 0) == 128 * 8 * per
+    assert wb(256, 0) == 256 * 4 * per
+    assert wb(511, 0) == 511 * 4 * per
+    assert wb(512, 0) == 0 and wb(16384, 0) == 0
+    assert wb(10, 4) == 10 * 4 * per and wb(10, 1) == 0
+    assert wb(10, 3) == 0 and wb(10, 32) == 0 and wb(0, 4) == 0
+
+
+def ex_call(a, splits, workspace=None, nbytes=0, out=None):
+    lib = c128.library()
+    ts = [a[k] for k in ("state_cache", "block_table", "token_to_req", "positions",
+                         "slot_mapping", "rms_w")]
+    rest = [a[k] for k in ("cos_sin", "k_cache", "kv_slot_mapping")]
+    return lib.dsv4_c128_compress_store_ex(*[ctypes.byref(c128.describe(t)) for t in ts], 1e-6,
+                                           *[ctypes.byref(c128.describe(t)) for t in rest], out,
+                                           workspace, nbytes, splits, None)
+
+
+def test_fanout_argument_errors_before_launch():
+    """Invalid splits, or explicit splits > 1 without a big enough workspace, fail with
+    DSV4_ERR_ARG before any HIP call; a bad layout still fails with its own code first."""
+    a = valid_args()
+    assert ex_call(a, 3) == -8 and "splits" in c128.last_error()
+    assert ex_call(a, 32) == -8
+    assert ex_call(a, 4) == -8 and "workspace" in c128.last_error()
+    assert ex_call(a, 4, workspace=16, nbytes=16) == -8
+    bad = valid_args()
+    bad["state_cache"] = torch.zeros(32, 8, 512)
+    assert ex_call(bad, 4) == -4
+
+
+def test_fanout_empty_batch_is_a_noop_on_host():
+    a = valid_args(T=0)
+    a["block_table"] = torch.zeros(1, 16, dtype=torch.int32)
+    assert ex_call(a, 16) == 0
+    assert ex_call(a, 0) == 0

@@ -237,3 +237,62 @@ def test_stream_argument_is_used():
     orc = oracle.run(wl, 2)
     rep = compare(wl, body, orc)
     assert ok and rep.ok(), rep.summary()
+
+
+# ---------------------------------------------------------------- small-batch fan-out
+
+def check_ex(wl, splits, label, debug=True):
+    announce(f"{label} (fan-out splits={splits})")
+    body, comp, guards_ok = run_gpu(wl, debug=debug, splits=splits)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, body, comp
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 7, 64, 130])
+def test_fanout_parity(T, splits):
+    """Every split count on small decode batches (one token, a ragged 7, 64, 130)."""
+    wl = small(T=T, seed=100 + T, kv_bs=16, kv_blocks=-(-2 * T // 16))
+    rep, *_ = check_ex(wl, splits, f"decode T={T}")
+    assert rep["written"] == T
+
+
+def test_fanout_automatic_on_workloads():
+    """Automatic split choice on the single-token and T=128 workloads, and on a 600-token batch
+    (single pass, no workspace needed)."""
+    check_ex(synth.config0(), 0, "cfg0")
+    check_ex(synth.config1(), 0, "cfg1")
+    check_ex(small(T=600, seed=77, kv_bs=64, kv_blocks=20), 0, "decode T=600")
+
+
+def test_fanout_gate_and_bad_indices():
+    """Non-boundary tokens, negative slots and out-of-range device indices take the same
+    decisions in the partial and the finish kernels: nothing is written for them."""
+    wl = small(T=6, seed=7)
+    wl.positions[:] = np.array([126, 128, 255, 254, 383, 511], np.int32)
+    wl.slot_mapping[:] = np.array([3, 3, 3, 3, -1, 9], np.int32)
+    wl.kv_slot_mapping[5] = -1
+    rep, body, comp = check_ex(wl, 8, "fan-out gate")
+    assert list(np.nonzero(wl.written_mask())[0]) == [2]
+    assert np.isfinite(comp[5]).all() and np.isnan(comp[4]).all()
+
+    wl = small(T=6, seed=19, cs_rows=1024)
+    wl.positions[:] = 127
+    wl.positions[4] = 1023
+    wl.token_to_req[0] = wl.block_table.shape[0]
+    wl.block_table[1, 15] = wl.state.shape[0] + 5
+    wl.kv_slot_mapping[2] = wl.k_cache.shape[0] * wl.k_cache.shape[1]
+    wl.cos_sin = wl.cos_sin[:128].copy()
+    announce("fan-out out-of-range indices (splits=16)")
+    body, comp, guards_ok = run_gpu(wl, debug=True, splits=16)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [-1, -1, -1, 1, -1, 1]
+    wl.kv_slot_mapping[[0, 1, 2, 4]] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
