@@ -246,13 +246,23 @@ def sweep(args, path):
 
     out = open(path, "w")
 
-    def measure(name, dws, steps, warm_only=False):
-        calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
+    def measure(name, dws, steps, warm_only=False, splits=None):
+        """splits None: the single-pass entry point; else compress_store_ex with that split
+        count (0 = automatic) and a workspace per window set."""
+        if splits is None:
+            calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
+        else:
+            wss = [torch.empty(max(16, c128.workspace_bytes(d.wl.num_tokens, splits)),
+                               dtype=torch.uint8, device=dev) for d in dws]
+            calls = [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w,
+                                                              splits=splits, stream=sid))
+                     for d, w in zip(dws, wss)]
         wl = dws[0].wl
         nbytes = algorithmic_bytes(wl)
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
         rec = {"workload": name, "tokens": wl.num_tokens,
                "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
+               "entry": "single pass" if splits is None else f"fan-out splits={splits}",
                "algorithmic_bytes_per_call": nbytes,
                "warm_us_median": round(float(np.median(per)) * 1e3, 2),
                "warm_us_mean": round(float(np.mean(per)) * 1e3, 2)}
@@ -266,8 +276,13 @@ def sweep(args, path):
         out.flush()
         log(f"[sweep] {json.dumps(rec)}")
 
-    measure("cfg0 single boundary token", [DeviceWorkload(synth.config0(), device=dev)], 1000)
-    measure("cfg1 decode batch T=128", [DeviceWorkload(synth.config1(), device=dev)], 1000)
+    d0 = DeviceWorkload(synth.config0(), device=dev)
+    measure("cfg0 single boundary token", [d0], 1000)
+    measure("cfg0 single boundary token", [d0], 1000, splits=0)
+    d1 = DeviceWorkload(synth.config1(), device=dev)
+    measure("cfg1 decode batch T=128", [d1], 1000)
+    measure("cfg1 decode batch T=128", [d1], 1000, splits=0)
+    del d0, d1
     d2 = DeviceWorkload(synth.config2(), device=dev)
     measure("cfg2 varlen prefill", [d2], 1000)
     del d2
@@ -282,6 +297,9 @@ def sweep(args, path):
             pool_dev = (d.state_buf, d.state)
             dws.append(d)
         measure(f"cfg3 decode sweep T={T}", dws, 1000 if T <= 1024 else 100)
+        if T < 1024:
+            for sp in ([0, 2, 4, 8, 16] if args.sweep_splits else [0]):
+                measure(f"cfg3 decode sweep T={T}", dws, 1000, splits=sp)
         del dws
     out.close()
 
@@ -363,6 +381,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-splits", action="store_true",
+                    help="with --sweep: time every fan-out split count, not only the automatic one")
     ap.add_argument("--mode", choices=["main", "copy", "read"], default="main")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

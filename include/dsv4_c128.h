@@ -158,8 +158,8 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
 
 /*
  * Bytes of workspace dsv4_c128_compress_store_ex needs for num_tokens tokens and `splits`
- * (0 = the library's choice: 1 for num_tokens >= 512, else the smallest power of two up to 16
- * with num_tokens * splits >= 1024).  0 when no workspace is needed or splits is not valid.
+ * (0 = the library's choice: 8 for num_tokens <= 16, 4 for 17..64, 1 above).  0 when no
+ * workspace is needed or splits is not valid.
  * Host-only; no HIP call.
  */
 size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);

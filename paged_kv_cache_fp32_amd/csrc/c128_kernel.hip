@@ -619,12 +619,11 @@ hipError_t launch_fanout(const C128Params& p, float* ws, hipStream_t stream) {
 }  // namespace
 
 int fanout_auto_splits(int64_t num_tokens) {
-  // Enough workgroups to occupy the 256 CUs several times over; the single pass once the
-  // batch alone does that.
-  if (num_tokens <= 0 || num_tokens >= 512) return 1;
-  int s = 1;
-  while (s < kWindowBlocks && num_tokens * s < 1024) s *= 2;
-  return s;
+  // Measured on MI355X with the window sets rotated (cold HBM): 8 splits are fastest up to 16
+  // tokens, 4 up to 64; from about 100 tokens on the single pass already has enough
+  // workgroups and the extra partial-state traffic and second launch make the fan-out slower.
+  if (num_tokens <= 0 || num_tokens > 64) return 1;
+  return num_tokens <= 16 ? 8 : 4;
 }
 
 size_t fanout_workspace_bytes(int64_t num_tokens, int splits) {

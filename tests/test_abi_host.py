@@ -206,18 +206,16 @@ def test_python_binding_rejects_host_tensors():
 
 
 def test_workspace_bytes_rules():
-    """Automatic splits: 16 for tiny batches, halving until T*splits >= 1024, 1 (no workspace)
-    from 512 tokens on; explicit splits give T*splits*3*512 floats; invalid splits give 0."""
+    """Automatic splits: 8 up to 16 tokens, 4 up to 64, 1 (no workspace) above; explicit
+    splits give T*splits*3*512 floats; invalid splits give 0."""
     wb = c128.workspace_bytes
     per = 3 * 512 * 4
-    assert wb(1, 0) == 1 * 16 * per
-    assert wb(64, 0) == 64 * 16 * per
-    assert wb(65, 0) == 65 * 16 * per
-    assert wb(128, 0) == 128 * 8 * per
-    assert wb(256, 0) == 256 * 4 * per
-    assert wb(511, 0) == 511 * 4 * per
-    assert wb(512, 0) == 0 and wb(16384, 0) == 0
-    assert wb(10, 4) == 10 * 4 * per and wb(10, 1) == 0
+    assert wb(1, 0) == 1 * 8 * per
+    assert wb(16, 0) == 16 * 8 * per
+    assert wb(17, 0) == 17 * 4 * per
+    assert wb(64, 0) == 64 * 4 * per
+    assert wb(65, 0) == 0 and wb(512, 0) == 0 and wb(16384, 0) == 0
+    assert wb(10, 4) == 10 * 4 * per and wb(10, 1) == 0 and wb(100, 16) == 100 * 16 * per
     assert wb(10, 3) == 0 and wb(10, 32) == 0 and wb(0, 4) == 0
 
 

@@ -262,9 +262,10 @@ def test_fanout_parity(T, splits):
 
 
 def test_fanout_automatic_on_workloads():
-    """Automatic split choice on the single-token and T=128 workloads, and on a 600-token batch
-    (single pass, no workspace needed)."""
+    """Automatic split choice on the single-token workload (8 splits), a 40-token batch (4),
+    the T=128 workload and a 600-token batch (single pass, no workspace needed)."""
     check_ex(synth.config0(), 0, "cfg0")
+    check_ex(small(T=40, seed=41, kv_bs=16, kv_blocks=5), 0, "decode T=40")
     check_ex(synth.config1(), 0, "cfg1")
     check_ex(small(T=600, seed=77, kv_bs=64, kv_blocks=20), 0, "decode T=600")
 
