@@ -246,10 +246,17 @@ def sweep(args, path):
 
     out = open(path, "w")
 
-    def measure(name, dws, steps, warm_only=False, splits=None):
+    def measure(name, dws, steps, warm_only=False, splits=None, varlen=False):
         """splits None: the single-pass entry point; else compress_store_ex with that split
-        count (0 = automatic) and a workspace per window set."""
-        if splits is None:
+        count (0 = automatic) and a workspace per window set; varlen: the compacted schedule
+        (compress_store_varlen) with a workspace per window set."""
+        if varlen:
+            wss = [torch.empty(max(16, c128.varlen_workspace_bytes(d.wl.num_tokens)),
+                               dtype=torch.uint8, device=dev) for d in dws]
+            calls = [(lambda d=d, w=w: c128.compress_store_varlen(*d.args(), workspace=w,
+                                                                  stream=sid))
+                     for d, w in zip(dws, wss)]
+        elif splits is None:
             calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
         else:
             wss = [torch.empty(max(16, c128.workspace_bytes(d.wl.num_tokens, splits)),
@@ -262,7 +269,8 @@ def sweep(args, path):
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
         rec = {"workload": name, "tokens": wl.num_tokens,
                "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
-               "entry": "single pass" if splits is None else f"fan-out splits={splits}",
+               "entry": "varlen (compacted)" if varlen else
+                        ("single pass" if splits is None else f"fan-out splits={splits}"),
                "algorithmic_bytes_per_call": nbytes,
                "warm_us_median": round(float(np.median(per)) * 1e3, 2),
                "warm_us_mean": round(float(np.mean(per)) * 1e3, 2)}
@@ -285,7 +293,13 @@ def sweep(args, path):
     del d0, d1
     d2 = DeviceWorkload(synth.config2(), device=dev)
     measure("cfg2 varlen prefill", [d2], 1000)
+    measure("cfg2 varlen prefill", [d2], 1000, varlen=True)
     del d2
+    d5 = DeviceWorkload(synth.scattered_batch("scattered", 61, 262400, 8, 64, 1024, kv_bs=64,
+                                              kv_blocks=64, cs_rows=8192), device=dev)
+    measure("scattered positions T=262400", [d5], 200)
+    measure("scattered positions T=262400", [d5], 200, varlen=True)
+    del d5
     _, pool = synth.config3_pool()
     pool_dev = None
     for T in [1 << i for i in range(13)]:
@@ -297,6 +311,8 @@ def sweep(args, path):
             pool_dev = (d.state_buf, d.state)
             dws.append(d)
         measure(f"cfg3 decode sweep T={T}", dws, 1000 if T <= 1024 else 100)
+        if T in (1, 128, 4096):
+            measure(f"cfg3 decode sweep T={T}", dws, 1000 if T <= 1024 else 100, varlen=True)
         if T < 1024:
             for sp in ([0, 2, 4, 8, 16] if args.sweep_splits else [0]):
                 measure(f"cfg3 decode sweep T={T}", dws, 1000, splits=sp)

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 2
+#define DSV4_ABI_VERSION 3
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -163,6 +163,38 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
  * Host-only; no HIP call.
  */
 size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);
+
+/*
+ * Compacted schedule for long varlen batches (chunked prefill).  The same computation as
+ * dsv4_c128_compress_store.  Only tokens whose position closes a 128-row window do any work
+ * (vLLM fused_compress_quant_cache page, sparse-attention kernel: one program per token that
+ * returns early unless (pos + 1) % 128 == 0), and in a prefill batch that is about one token in
+ * 128.  A first kernel tests the gate on every token and writes the passing token indices,
+ * compacted, to `workspace`; a persistent grid of workgroups then processes only those tokens.
+ * Results are identical to dsv4_c128_compress_store's, bit for bit, and do not depend on the
+ * schedule.  For decode batches, where every token passes, the plain entry point is faster.
+ *
+ *   workspace       device memory of at least dsv4_c128_varlen_workspace_bytes(T) bytes,
+ *                   16-byte aligned, owned by the caller; no initialisation needed, scratch after
+ *                   the call.  Calls that share a workspace must be ordered on one stream.
+ *                   NULL or too small: DSV4_ERR_ARG (unless T == 0).
+ *   compressed_out  NULL, or as in dsv4_c128_compress_store_debug.
+ */
+int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
+                                    const dsv4_tensor* block_table,
+                                    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                    float eps, const dsv4_tensor* cos_sin,
+                                    const dsv4_tensor* k_cache,
+                                    const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace dsv4_c128_compress_store_varlen needs for num_tokens tokens: 4 * (1024 +
+ * num_tokens) rounded up to a multiple of 16 (per-scan-block counts, then the compacted token
+ * list); 0 for num_tokens <= 0.  Host-only; no HIP call.
+ */
+size_t dsv4_c128_varlen_workspace_bytes(int64_t num_tokens);
 
 /*
  * Host-only validation of the descriptors, exactly as the compute entry

@@ -92,6 +92,11 @@ def library():
         lib.dsv4_c128_compress_store_ex.restype = ctypes.c_int
         lib.dsv4_c128_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int]
         lib.dsv4_c128_workspace_bytes.restype = ctypes.c_size_t
+        lib.dsv4_c128_compress_store_varlen.argtypes = args10 + [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.dsv4_c128_compress_store_varlen.restype = ctypes.c_int
+        lib.dsv4_c128_varlen_workspace_bytes.argtypes = [ctypes.c_int64]
+        lib.dsv4_c128_varlen_workspace_bytes.restype = ctypes.c_size_t
         lib.dsv4_c128_validate.argtypes = args10
         lib.dsv4_c128_validate.restype = ctypes.c_int
         lib.dsv4_e4m3_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -200,6 +205,39 @@ def compress_store_ex(state_cache, block_table, token_to_req, positions, slot_ma
                                                  ws_ptr, ws_len, int(splits), s))
 
 
+def varlen_workspace_bytes(num_tokens: int) -> int:
+    """Workspace bytes ``compress_store_varlen`` needs for ``num_tokens`` tokens."""
+    return int(library().dsv4_c128_varlen_workspace_bytes(int(num_tokens)))
+
+
+def compress_store_varlen(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                          eps, cos_sin, k_cache, kv_slot_mapping, compressed_out=None,
+                          workspace=None, stream: int | None = None) -> None:
+    """``compress_store`` on a compacted schedule for long varlen (prefill) batches: a gate scan
+    lists the tokens that close a window, then a persistent grid processes only those.
+    ``workspace``: a contiguous device tensor of at least ``varlen_workspace_bytes(T)`` bytes
+    (allocated here when None).  ``compressed_out`` as in ``compress_store_debug``."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    extra = [t for t in (compressed_out, workspace) if t is not None]
+    dev = _require_cuda(ts + extra)
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 512)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(varlen_workspace_bytes(positions.shape[0]), 16),
+                                dtype=torch.uint8, device=dev)
+    elif not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_c128_compress_store_varlen(
+        *refs[:6], float(eps), *refs[6:], out_ptr, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), s))
+
+
 def validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
              cos_sin, k_cache, kv_slot_mapping) -> int:
     """Host-only validation of the descriptors (no HIP call); returns the status code."""
@@ -222,5 +260,6 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
 
 
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
+           "compress_store_varlen", "varlen_workspace_bytes",
            "validate", "e4m3_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

@@ -268,6 +268,39 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
   return DSV4_OK;
 }
 
+size_t dsv4_c128_varlen_workspace_bytes(int64_t num_tokens) {
+  return dsv4::compacted_workspace_bytes(num_tokens);
+}
+
+int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
+                                    const dsv4_tensor* block_table,
+                                    const dsv4_tensor* token_to_req,
+                                    const dsv4_tensor* positions,
+                                    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                    float eps, const dsv4_tensor* cos_sin,
+                                    const dsv4_tensor* k_cache,
+                                    const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dsv4::C128Params p;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p);
+  if (rc) return rc;
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  const size_t need = dsv4::compacted_workspace_bytes(p.num_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSV4_ERR_ARG, "workspace of %zu bytes is too small: %d tokens need %zu",
+                workspace_bytes, p.num_tokens, need);
+  if (!aligned16(workspace)) return fail(DSV4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  p.compressed_out = compressed_out;
+  hipError_t err =
+      dsv4::launch_c128_compacted(p, workspace, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (n < 0) return fail(DSV4_ERR_SHAPE, "n must be >= 0");
   if (n == 0) return DSV4_OK;

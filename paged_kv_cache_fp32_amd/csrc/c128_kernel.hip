@@ -566,6 +566,141 @@ __global__ void __launch_bounds__(128) c128_fanout_finish_kernel(const C128Param
   finish_token<kDebug>(p, t, win.rope_row, true, half, lane, col, l, acc, lds_ss);
 }
 
+constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
+constexpr int kStageRows = 4;  // rows per pipeline stage
+constexpr int kWavesPerSimd = 8;
+
+// ---------------------------------------------------------------------------------------------
+// Compacted schedule for long varlen batches (chunked prefill), where only about one token in
+// 128 closes a window: a workgroup per token would spend most of the call dispatching
+// workgroups that exit at the gate.  Two stream-ordered kernels, no atomics, deterministic:
+//
+//  1. c128_gate_scan_kernel: scan block b owns tokens [b*chunk, min(T, (b+1)*chunk)).  Its 256
+//     lanes test the gate on 256 tokens at a time and write the tokens that pass, in token
+//     order, to list[b*chunk + k], k < counts[b] (wave ballot, lane rank by mbcnt, per-wave
+//     offsets through LDS).
+//  2. c128_compacted_kernel: a persistent grid of single-pass-shaped workgroups.  Each builds
+//     the exclusive prefix of counts[] in LDS and takes items blockIdx.x, blockIdx.x +
+//     gridDim.x, ... of the compacted list; item i sits in the last scan block b with
+//     prefix[b] <= i, at offset i - prefix[b].  A token then runs the full gate (its indices are
+//     range-checked there), the window stream, the row-group merge and the fused epilogue.
+constexpr int kScanThreads = 256;
+constexpr int kMaxScanBlocks = 1024;
+// The compacted kernel keeps loop-invariant values live across its tokens (about 108 VGPRs), so
+// it runs 4 waves per SIMD: 2 workgroups of 8 waves per CU, a persistent grid of 512 for the
+// 256 CUs.  Each wave still has a full pipeline stage of loads in flight.
+constexpr int kCompactedWavesPerSimd = 4;
+constexpr int kCompactedGrid = 512;
+
+__global__ void __launch_bounds__(kScanThreads) c128_gate_scan_kernel(
+    const C128Params p, int32_t chunk, int32_t* __restrict__ counts, int32_t* __restrict__ list) {
+  __shared__ int32_t wave_count[kScanThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t end = begin + chunk < p.num_tokens ? begin + chunk : p.num_tokens;
+  int32_t found = 0;  // tokens of this scan block that passed so far (uniform)
+  for (int64_t base = begin; base < end; base += kScanThreads) {
+    const int64_t t = base + threadIdx.x;
+    bool act = false;
+    if (t < end) {
+      const int32_t pos = p.positions[t];
+      const int32_t slot = p.slot_mapping[t];
+      act = slot >= 0 && pos >= 0 && (pos & (kRatio - 1)) == kRatio - 1;
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(act);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+    if (lane == 0) wave_count[wave] = __builtin_popcountll(mask);
+    __syncthreads();
+    int32_t off = found, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int32_t c = wave_count[w];
+      if (w < wave) off += c;
+      sum += c;
+    }
+    if (act) list[begin + off + below] = static_cast<int32_t>(t);
+    found += sum;
+    __syncthreads();  // wave_count is rewritten in the next round
+  }
+  if (threadIdx.x == 0) counts[blockIdx.x] = found;
+}
+
+template <bool kDebug>
+__global__ void __launch_bounds__(128 * kRowGroups)
+    __attribute__((amdgpu_waves_per_eu(kCompactedWavesPerSimd, kCompactedWavesPerSimd)))
+    c128_compacted_kernel(const C128Params p, const int32_t* __restrict__ counts,
+                          const int32_t* __restrict__ list, int32_t chunk, int32_t nblocks) {
+  constexpr int RG = kRowGroups;
+  constexpr int NBW = kWindowBlocks / RG;
+  constexpr int kPerLane = kMaxScanBlocks / 64;
+
+  __shared__ int32_t lds_prefix[kMaxScanBlocks];
+  __shared__ int32_t lds_total;
+  __shared__ float4 lds_ml[RG][2][64];
+  __shared__ float4 lds_l[RG][2][64];
+  __shared__ float4 lds_acc[RG][2][64];
+  __shared__ float lds_ss[2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int rg = wave >> 1;
+  const int col = half * 256 + lane * 4;
+
+  // exclusive prefix of the scan-block counts: lane l of wave 0 owns blocks 16l .. 16l + 15
+  if (wave == 0) {
+    int32_t v[kPerLane];
+    int32_t own = 0;
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      const int b = lane * kPerLane + k;
+      v[k] = b < nblocks ? counts[b] : 0;
+      own += v[k];
+    }
+    int32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int32_t run = incl - own;
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      const int b = lane * kPerLane + k;
+      if (b < nblocks) lds_prefix[b] = run;
+      run += v[k];
+    }
+    if (lane == 63) lds_total = incl;
+  }
+  __syncthreads();
+  const int64_t total = __builtin_amdgcn_readfirstlane(lds_total);
+
+  for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
+    int lo = 0, hi = nblocks - 1;  // last b with prefix[b] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(lds_prefix[mid]) <= i)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int64_t at = static_cast<int64_t>(lo) * chunk +
+                       (i - __builtin_amdgcn_readfirstlane(lds_prefix[lo]));
+    const int32_t t = __builtin_amdgcn_readfirstlane(list[at]);
+    const Window win = gate_and_window(p, t);
+    if (win.ok) {
+      float ml[4], l[4], acc[4];
+      stream_blocks<NBW, kStageRows>(p, win.bt + rg * NBW, static_cast<uint32_t>(col), ml, l,
+                                     acc);
+      merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
+      finish_token<kDebug>(p, t, win.rope_row, rg == 0, half, lane, col, l, acc, lds_ss);
+    }
+    __syncthreads();  // LDS is reused by the next token
+  }
+}
+
 __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8_t* out,
                                                           int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
@@ -579,9 +714,6 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
     if (i + k < n) out[i + k] = static_cast<uint8_t>(w >> (8 * k));
 }
 
-constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
-constexpr int kStageRows = 4;  // rows per pipeline stage
-constexpr int kWavesPerSimd = 8;
 
 }  // namespace
 
@@ -647,6 +779,46 @@ hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStr
     default:
       return hipErrorInvalidValue;
   }
+}
+
+namespace {
+
+// Scan blocks of a multiple of 256 tokens, at most kMaxScanBlocks of them.
+void compacted_schedule(int64_t num_tokens, int32_t* chunk, int32_t* nblocks) {
+  int64_t per = (num_tokens + kMaxScanBlocks - 1) / kMaxScanBlocks;
+  if (per < 1) per = 1;
+  const int64_t c = (per + kScanThreads - 1) / kScanThreads * kScanThreads;
+  *chunk = static_cast<int32_t>(c);
+  *nblocks = static_cast<int32_t>((num_tokens + c - 1) / c);
+}
+
+}  // namespace
+
+size_t compacted_workspace_bytes(int64_t num_tokens) {
+  if (num_tokens <= 0) return 0;
+  const size_t ints = kMaxScanBlocks + static_cast<size_t>(num_tokens);
+  return (ints * sizeof(int32_t) + 15) / 16 * 16;
+}
+
+hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  int32_t chunk = 0, nblocks = 0;
+  compacted_schedule(p.num_tokens, &chunk, &nblocks);
+  int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* list = counts + kMaxScanBlocks;
+  c128_gate_scan_kernel<<<dim3(static_cast<unsigned>(nblocks)), dim3(kScanThreads), 0, stream>>>(
+      p, chunk, counts, list);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned grid =
+      static_cast<unsigned>(p.num_tokens < kCompactedGrid ? p.num_tokens : kCompactedGrid);
+  if (p.compressed_out)
+    c128_compacted_kernel<true><<<dim3(grid), dim3(128 * kRowGroups), 0, stream>>>(
+        p, counts, list, chunk, nblocks);
+  else
+    c128_compacted_kernel<false><<<dim3(grid), dim3(128 * kRowGroups), 0, stream>>>(
+        p, counts, list, chunk, nblocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {

@@ -53,6 +53,11 @@ hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
 hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream);
 int fanout_auto_splits(int64_t num_tokens);
 size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
+// Compacted schedule for long varlen batches: a gate scan into a workspace of
+// compacted_workspace_bytes(T) bytes (16-byte aligned), then a persistent grid over the tokens
+// that pass.
+hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stream);
+size_t compacted_workspace_bytes(int64_t num_tokens);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace dsv4

@@ -308,6 +308,37 @@ def varlen_prefill(name: str, seed: int, num_reqs: int, max_chunk: int, max_star
     return wl
 
 
+def scattered_batch(name: str, seed: int, num_tokens: int, num_reqs: int, n_blocks: int,
+                    table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int,
+                    drop_frac: float = 0.1, score_std: float = math.sqrt(2.0)) -> Workload:
+    """Tokens of random requests at uniformly random positions 0 .. 8*table_cols - 1, so about
+    one token in 128 closes a window; block-table entries uniform over the pool (windows may
+    share blocks); a seeded ``drop_frac`` of slot_mapping is -1.  Tokens that close a window
+    with slot >= 0 get distinct kv slots; the others get arbitrary slots."""
+    T = num_tokens
+    req = randint(T, 0, num_reqs - 1, seed, 30).astype(np.int32)
+    positions = randint(T, 0, STATE_BLOCK * table_cols - 1, seed, 31)
+    bt = (bits(num_reqs * table_cols, seed, 32) % np.uint64(n_blocks)).astype(np.int32).reshape(
+        num_reqs, table_cols)
+    blk = bt[req, positions // STATE_BLOCK].astype(np.int64)
+    slot_mapping = blk * STATE_BLOCK + positions % STATE_BLOCK
+    slot_mapping[uniform(T, seed, 33) < drop_frac] = -1
+    n_kv = kv_blocks * kv_bs
+    kv_slots = randint(T, 0, n_kv - 1, seed, 34).astype(np.int32)
+    state_base, state = alloc_state(n_blocks)
+    fill_state(state, seed, 1.0, score_std)
+    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs)
+    wl = Workload(name, state, bt, req, positions.astype(np.int32),
+                  slot_mapping.astype(np.int32), _rms_weight(seed), 1e-6, rope_table(cs_rows),
+                  kc, kv_slots, seed, state_base, kc_base)
+    act = wl.active_mask()
+    if int(act.sum()) > n_kv:
+        raise ValueError("not enough kv slots for the active tokens")
+    wl.kv_slot_mapping[act] = permutation(n_kv, seed, 35)[:int(act.sum())].astype(np.int32)
+    wl.info = {"kind": "scattered", "tokens": T, "requests": num_reqs, "pool_blocks": n_blocks}
+    return wl
+
+
 def config0() -> Workload:
     """Single request, one boundary token at position 127; 16-block pool; KV block size 2,
     kv slot 3; kv ~ N(0,1), score ~ N(0,2); 4096 RoPE rows."""

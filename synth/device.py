@@ -51,14 +51,19 @@ class DeviceWorkload:
                 self.slot_mapping, self.rms_w, self.eps, self.cos_sin, self.k_cache,
                 self.kv_slot_mapping)
 
-    def run(self, debug=False, splits=None):
+    def run(self, debug=False, splits=None, varlen=False):
         """One call; splits None = the plain entry points, else compress_store_ex with that
-        split count (0 = automatic) and a workspace of the size it needs."""
+        split count (0 = automatic) and a workspace of the size it needs; varlen = the
+        compacted schedule (compress_store_varlen)."""
         comp = None
         if debug:
             comp = torch.full((self.wl.num_tokens, 512), float("nan"), dtype=torch.float32,
                               device=self.state.device)
-        if splits is None:
+        if varlen:
+            ws = torch.empty(max(c128.varlen_workspace_bytes(self.wl.num_tokens), 16),
+                             dtype=torch.uint8, device=self.state.device)
+            c128.compress_store_varlen(*self.args(), compressed_out=comp, workspace=ws)
+        elif splits is None:
             if debug:
                 c128.compress_store_debug(*self.args(), comp)
             else:
@@ -79,8 +84,8 @@ class DeviceWorkload:
         return buf[g:-g].copy(), guards_ok
 
 
-def run_gpu(wl, debug=True, splits=None):
+def run_gpu(wl, debug=True, splits=None, varlen=False):
     d = DeviceWorkload(wl)
-    comp = d.run(debug=debug, splits=splits)
+    comp = d.run(debug=debug, splits=splits, varlen=varlen)
     body, guards_ok = d.k_cache_bytes()
     return body, (comp.cpu().numpy() if comp is not None else None), guards_ok

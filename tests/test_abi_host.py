@@ -247,3 +247,37 @@ def test_fanout_empty_batch_is_a_noop_on_host():
     a["block_table"] = torch.zeros(1, 16, dtype=torch.int32)
     assert ex_call(a, 16) == 0
     assert ex_call(a, 0) == 0
+
+
+def varlen_call(a, workspace=None, nbytes=0, out=None):
+    lib = c128.library()
+    ts = [a[k] for k in ("state_cache", "block_table", "token_to_req", "positions",
+                         "slot_mapping", "rms_w")]
+    rest = [a[k] for k in ("cos_sin", "k_cache", "kv_slot_mapping")]
+    return lib.dsv4_c128_compress_store_varlen(
+        *[ctypes.byref(c128.describe(t)) for t in ts], 1e-6,
+        *[ctypes.byref(c128.describe(t)) for t in rest], out, workspace, nbytes, None)
+
+
+def test_varlen_workspace_bytes_rule():
+    """Counts of up to 1024 scan blocks, then one list entry per token; 16-byte granules."""
+    vb = c128.varlen_workspace_bytes
+    assert vb(0) == 0 and vb(-3) == 0
+    assert vb(1) == 4112 and vb(4) == 4112 and vb(5) == 4128
+    assert vb(34323) == (4 * (1024 + 34323) + 15) // 16 * 16
+    assert vb(2 ** 31 - 1) == (4 * (1024 + 2 ** 31 - 1) + 15) // 16 * 16
+
+
+def test_varlen_argument_errors_before_launch():
+    """No or too small a workspace is DSV4_ERR_ARG, a misaligned one DSV4_ERR_ALIGN, both
+    before any HIP call; layout errors keep their own codes; T == 0 needs no workspace."""
+    a = valid_args()
+    assert varlen_call(a) == -8 and "workspace" in c128.last_error()
+    assert varlen_call(a, workspace=16, nbytes=c128.varlen_workspace_bytes(4) - 16) == -8
+    assert varlen_call(a, workspace=24, nbytes=c128.varlen_workspace_bytes(4)) == -6
+    assert varlen_call(a, workspace=16, nbytes=8192, out=8) == -6
+    bad = valid_args()
+    bad["k_cache"] = torch.zeros(2, 4, 576, dtype=torch.uint8)
+    assert varlen_call(bad) == -4
+    e = valid_args(T=0)
+    assert varlen_call(e) == 0

@@ -297,3 +297,100 @@ def test_fanout_gate_and_bad_indices():
     rep = compare(wl, body, orc)
     assert rep.ok(), rep.summary()
     assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
+
+
+# ---------------------------------------------------------------- compacted schedule (varlen)
+
+def check_varlen(wl, label, debug=True):
+    announce(f"{label} (compacted schedule)")
+    body, comp, guards_ok = run_gpu(wl, debug=debug, varlen=True)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, body, comp
+
+
+def test_varlen_config2_and_single_pass_bytes():
+    """The varlen prefill workload on the compacted schedule: parity with the oracle, and the
+    same k_cache bytes as the single pass (the per-token arithmetic is the same)."""
+    wl = synth.config2()
+    rep, body, _ = check_varlen(wl, "cfg2 varlen prefill")
+    assert rep["written"] == int(wl.written_mask().sum()) > 100
+    plain, _, ok = run_gpu(wl, debug=False)
+    assert ok and np.array_equal(body, plain)
+
+
+def test_varlen_decode_batches():
+    """Every token active: a ragged 37 and the T=128 workload; bytes equal the single pass."""
+    for wl in (small(T=37, seed=43, kv_bs=16, kv_blocks=5), synth.config1()):
+        rep, body, _ = check_varlen(wl, wl.name + f" T={wl.num_tokens}")
+        assert rep["written"] == wl.num_tokens
+        plain, _, ok = run_gpu(wl, debug=False)
+        assert ok and np.array_equal(body, plain)
+
+
+def test_varlen_many_scan_blocks():
+    """262,400 tokens at random positions, about 1,850 of them written: 513 scan blocks of 512
+    tokens, so the prefix over scan blocks spans many lanes and the persistent grid of 512
+    workgroups takes several tokens each.  Only tokens that close a window write, so the oracle
+    runs on that sub-batch (its diagnostics for all 262,400 rows would take 3 GB): it fixes
+    every record written and every byte that must stay untouched."""
+    import dataclasses
+    wl = synth.scattered_batch("scattered", 61, 262400, 8, 64, 1024, kv_bs=64, kv_blocks=64,
+                               cs_rows=8192)
+    announce("scattered T=262400 (compacted schedule)")
+    body, _, guards_ok = run_gpu(wl, debug=False, varlen=True)
+    assert guards_ok
+    act = np.nonzero(wl.active_mask())[0]
+    sub = dataclasses.replace(wl, token_to_req=wl.token_to_req[act], positions=wl.positions[act],
+                              slot_mapping=wl.slot_mapping[act],
+                              kv_slot_mapping=wl.kv_slot_mapping[act])
+    rep = compare(sub, body, oracle.run(sub, THREADS))
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == int(wl.written_mask().sum()) > 1500
+
+
+def test_varlen_nothing_active():
+    """3,000 tokens none of which closes a window, and one lone non-boundary token: nothing is
+    written and the compacted list is empty."""
+    wl = synth.scattered_batch("scattered", 67, 3000, 4, 32, 256, kv_bs=16, kv_blocks=4,
+                               cs_rows=2048)
+    wl.positions[wl.active_mask()] -= 1
+    rep, *_ = check_varlen(wl, "no active token")
+    assert rep["written"] == 0
+    wl = small(T=1, seed=3)
+    wl.positions[:] = 126
+    rep, *_ = check_varlen(wl, "one inactive token")
+    assert rep["written"] == 0
+
+
+def test_varlen_gate_and_bad_indices():
+    """Gate decisions and out-of-range device indices on the compacted schedule: the gate scan
+    lists boundary tokens with slot >= 0, and the main kernel still range-checks each one."""
+    wl = small(T=6, seed=7)
+    wl.positions[:] = np.array([126, 128, 255, 254, 383, 511], np.int32)
+    wl.slot_mapping[:] = np.array([3, 3, 3, 3, -1, 9], np.int32)
+    wl.kv_slot_mapping[5] = -1
+    rep, body, comp = check_varlen(wl, "varlen gate")
+    assert list(np.nonzero(wl.written_mask())[0]) == [2]
+    assert np.isfinite(comp[5]).all() and np.isnan(comp[4]).all()
+
+    wl = small(T=6, seed=19, cs_rows=1024)
+    wl.positions[:] = 127
+    wl.positions[4] = 1023
+    wl.token_to_req[0] = wl.block_table.shape[0]
+    wl.block_table[1, 15] = wl.state.shape[0] + 5
+    wl.kv_slot_mapping[2] = wl.k_cache.shape[0] * wl.k_cache.shape[1]
+    wl.cos_sin = wl.cos_sin[:128].copy()
+    announce("varlen out-of-range indices")
+    body, comp, guards_ok = run_gpu(wl, debug=True, varlen=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [-1, -1, -1, 1, -1, 1]
+    wl.kv_slot_mapping[[0, 1, 2, 4]] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
