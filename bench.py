@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,7 +55,8 @@ def algorithmic_bytes(wl) -> int:
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_params.h")):
+    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_device.h"),
+              os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_params.h")):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -264,6 +266,8 @@ def sweep(args, path):
             calls = [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w,
                                                               splits=splits, stream=sid))
                      for d, w in zip(dws, wss)]
+        if args.sweep_steps:
+            steps = min(steps, args.sweep_steps)
         wl = dws[0].wl
         nbytes = algorithmic_bytes(wl)
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
@@ -284,25 +288,35 @@ def sweep(args, path):
         out.flush()
         log(f"[sweep] {json.dumps(rec)}")
 
-    d0 = DeviceWorkload(synth.config0(), device=dev)
-    measure("cfg0 single boundary token", [d0], 1000)
-    measure("cfg0 single boundary token", [d0], 1000, splits=0)
-    d1 = DeviceWorkload(synth.config1(), device=dev)
-    measure("cfg1 decode batch T=128", [d1], 1000)
-    measure("cfg1 decode batch T=128", [d1], 1000, splits=0)
-    del d0, d1
-    d2 = DeviceWorkload(synth.config2(), device=dev)
-    measure("cfg2 varlen prefill", [d2], 1000)
-    measure("cfg2 varlen prefill", [d2], 1000, varlen=True)
-    del d2
-    d5 = DeviceWorkload(synth.scattered_batch("scattered", 61, 262400, 8, 64, 1024, kv_bs=64,
-                                              kv_blocks=64, cs_rows=8192), device=dev)
-    measure("scattered positions T=262400", [d5], 200)
-    measure("scattered positions T=262400", [d5], 200, varlen=True)
-    del d5
-    _, pool = synth.config3_pool()
-    pool_dev = None
+    pattern = re.compile(args.sweep_filter) if args.sweep_filter else None
+    want = (lambda name: bool(pattern.search(name))) if pattern else (lambda name: True)
+    if want("cfg0 single boundary token"):
+        d0 = DeviceWorkload(synth.config0(), device=dev)
+        measure("cfg0 single boundary token", [d0], 1000)
+        measure("cfg0 single boundary token", [d0], 1000, splits=0)
+        del d0
+    if want("cfg1 decode batch T=128"):
+        d1 = DeviceWorkload(synth.config1(), device=dev)
+        measure("cfg1 decode batch T=128", [d1], 1000)
+        measure("cfg1 decode batch T=128", [d1], 1000, splits=0)
+        del d1
+    if want("cfg2 varlen prefill"):
+        d2 = DeviceWorkload(synth.config2(), device=dev)
+        measure("cfg2 varlen prefill", [d2], 1000)
+        measure("cfg2 varlen prefill", [d2], 1000, varlen=True)
+        del d2
+    if want("scattered positions T=262400"):
+        d5 = DeviceWorkload(synth.scattered_batch("scattered", 61, 262400, 8, 64, 1024, kv_bs=64,
+                                                  kv_blocks=64, cs_rows=8192), device=dev)
+        measure("scattered positions T=262400", [d5], 200)
+        measure("scattered positions T=262400", [d5], 200, varlen=True)
+        del d5
+    pool = pool_dev = None
     for T in [1 << i for i in range(13)]:
+        if not want(f"cfg3 decode sweep T={T}"):
+            continue
+        if pool is None:
+            _, pool = synth.config3_pool()
         n_sets = min(64, 65536 // (16 * T))
         dws = []
         for s in range(n_sets):
@@ -397,9 +411,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-filter", default=None,
+                    help="only the sweep workloads whose name matches this regular expression")
+    ap.add_argument("--sweep-steps", type=int, default=0,
+                    help="cap on the timed calls per sweep entry (for counter runs)")
     ap.add_argument("--sweep-splits", action="store_true",
                     help="with --sweep: time every fan-out split count, not only the automatic one")
-    ap.add_argument("--mode", choices=["main", "copy", "read"], default="main")
+    ap.add_argument("--mode", choices=["main", "copy", "read", "sweep"], default="main",
+                    help="main: the large-batch line (plus --sweep if given); sweep: only the "
+                         "--sweep workloads; read / copy: bandwidth references and counter "
+                         "calibration")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the C128 compress-store path shards by request "
@@ -412,6 +433,10 @@ def main():
         copy_line(args)
     elif args.mode == "read":
         read_line(args)
+    elif args.mode == "sweep":
+        if not args.sweep:
+            sys.exit("--mode sweep needs --sweep PATH")
+        sweep(args, args.sweep)
     else:
         main_line(args)
 

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsv4_c128.so")
-SOURCES = [os.path.join(CSRC, "c128_kernel.hip"), os.path.join(CSRC, "c128_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "c128_kernel.hip"), os.path.join(CSRC, "c128_schedules.hip"),
+           os.path.join(CSRC, "c128_abi.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

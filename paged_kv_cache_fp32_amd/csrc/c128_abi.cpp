@@ -14,7 +14,7 @@
 #include <cstdio>
 #include <string>
 
-#include "c128_params.h"
+#include "c128_launch.h"
 #include "dsv4_c128.h"
 
 namespace {

@@ -1,0 +1,127 @@
+// Device helpers of the C128 compress-store kernels: fp8 / bf16 conversions, wave and 16-lane
+// reductions, the non-temporal state-row loads and the per-column online-softmax update, plus
+// the single pass's launch shape (the compacted schedule reuses it).
+#pragma once
+
+#include "c128_params.h"
+
+namespace dsv4 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFp8Max = 448.0f;
+constexpr float kInvFp8Max = 1.0f / 448.0f;  // fl32(1/448), as the page's fp32 multiply uses
+constexpr float kAbsmaxFloor = 1e-4f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int C>
+__device__ __forceinline__ float lane_of(const float4& v) {
+  if constexpr (C == 0) return v.x;
+  else if constexpr (C == 1) return v.y;
+  else if constexpr (C == 2) return v.z;
+  else return v.w;
+}
+
+// Clamp to the E4M3FN range and convert four fp32 values to OCP FP8 E4M3FN
+// (round to nearest even) with gfx950's packed conversion; byte k of the
+// result is the code of the k-th argument.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -kFp8Max), kFp8Max);
+  b = __builtin_fminf(__builtin_fmaxf(b, -kFp8Max), kFp8Max);
+  c = __builtin_fminf(__builtin_fmaxf(c, -kFp8Max), kFp8Max);
+  d = __builtin_fminf(__builtin_fmaxf(d, -kFp8Max), kFp8Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+  return __uint_as_float(bf16_bits(x) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Max over the 16-lane group holding one 64-column quantisation block.
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// State rows are read exactly once per call: load them with the non-temporal hint
+// (global_load_dwordx4 ... nt) so the stream does not allocate in L2 / MALL.  On the
+// 16-block window gather this lifts the attainable read rate from about 6.2 to 7.0 TB/s.
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// CH rows starting at the wave-uniform row pointer `row` (SGPRs); the lane adds only its
+// 32-bit column offset, so each load is the saddr + voffset form with no per-row VGPR address.
+template <int CH>
+__device__ __forceinline__ void load_rows(float4 (&kv)[CH], float4 (&sc)[CH], const float* row,
+                                          int64_t s1, uint32_t col) {
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    const float* rp = row + r * s1;
+    kv[r] = load_stream(rp + col);
+    sc[r] = load_stream(rp + kHead + col);
+  }
+}
+
+// Online softmax update of one column with CH rows.
+template <int C, bool kFirst, int CH>
+__device__ __forceinline__ void update_column(const float4 (&kv)[CH], const float4 (&sc)[CH],
+                                              float& ml, float& l, float& acc) {
+  float s[CH];
+#pragma unroll
+  for (int r = 0; r < CH; ++r) s[r] = lane_of<C>(sc[r]);
+  float cm = s[0];
+#pragma unroll
+  for (int r = 1; r < CH; ++r) cm = __builtin_fmaxf(cm, s[r]);
+  cm *= kLog2e;
+  const float mn = kFirst ? cm : __builtin_fmaxf(ml, cm);
+  float psum = 0.0f, a = 0.0f;
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    const float pr = exp2_fast(__builtin_fmaf(s[r], kLog2e, -mn));
+    psum += pr;
+    a = __builtin_fmaf(pr, lane_of<C>(kv[r]), a);
+  }
+  if (kFirst) {
+    l = psum;
+    acc = a;
+  } else {
+    const float scale = exp2_fast(ml - mn);
+    l = __builtin_fmaf(l, scale, psum);
+    acc = __builtin_fmaf(acc, scale, a);
+  }
+  ml = mn;
+}
+
+template <bool kFirst, int CH>
+__device__ __forceinline__ void update(const float4 (&kv)[CH], const float4 (&sc)[CH],
+                                       float (&ml)[4], float (&l)[4], float (&acc)[4]) {
+  update_column<0, kFirst, CH>(kv, sc, ml[0], l[0], acc[0]);
+  update_column<1, kFirst, CH>(kv, sc, ml[1], l[1], acc[1]);
+  update_column<2, kFirst, CH>(kv, sc, ml[2], l[2], acc[2]);
+  update_column<3, kFirst, CH>(kv, sc, ml[3], l[3], acc[3]);
+}
+
+constexpr int kRowGroups = 4;  // 8 waves (512 lanes) per token
+constexpr int kStageRows = 4;  // rows per pipeline stage
+constexpr int kWavesPerSimd = 8;
+
+}  // namespace
+}  // namespace dsv4

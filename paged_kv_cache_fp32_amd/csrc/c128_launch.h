@@ -1,0 +1,28 @@
+// Host-side launchers of the C128 compress-store kernels (internal; the C ABI in c128_abi.cpp
+// validates the arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "c128_params.h"
+
+namespace dsv4 {
+
+// Single pass and encoder: c128_kernel.hip.  Every launcher returns the hipError_t of its launch.
+hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
+// Fan-out and compacted schedules: c128_schedules.hip.
+// Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) with a
+// workspace of fanout_workspace_bytes(T, splits) bytes, 16-byte aligned.
+hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream);
+int fanout_auto_splits(int64_t num_tokens);
+size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
+// Compacted schedule for long varlen batches: a gate scan into a workspace of
+// compacted_workspace_bytes(T) bytes (16-byte aligned), then a persistent grid over the tokens
+// that pass.
+hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stream);
+size_t compacted_workspace_bytes(int64_t num_tokens);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace dsv4

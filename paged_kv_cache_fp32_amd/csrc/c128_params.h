@@ -1,5 +1,5 @@
-// Internal launch parameters of the C128 compress-store kernel (not part of
-// the public ABI; see include/dsv4_c128.h for the contract).
+// Layout constants and launch parameters of the C128 compress-store kernels (not part of the
+// public ABI; include/dsv4_c128.h holds the contract).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,19 +45,5 @@ struct C128Params {
   const int32_t* kv_slot_mapping;
   float* compressed_out;   // [T, 512] or nullptr
 };
-
-// Launchers (c128_kernel.hip).  Return the hipError_t of the launch.
-hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
-// Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) with a
-// workspace of fanout_workspace_bytes(T, splits) bytes, 16-byte aligned.
-hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream);
-int fanout_auto_splits(int64_t num_tokens);
-size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
-// Compacted schedule for long varlen batches: a gate scan into a workspace of
-// compacted_workspace_bytes(T) bytes (16-byte aligned), then a persistent grid over the tokens
-// that pass.
-hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stream);
-size_t compacted_workspace_bytes(int64_t num_tokens);
-hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace dsv4
