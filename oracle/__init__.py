@@ -1,4 +1,4 @@
-"""CPU oracle of the C128 compress-store path (test infrastructure).
+"""CPU oracle of the sparse-attention compress-store path, C128 and C4 (test infrastructure).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never links or calls
@@ -61,6 +61,8 @@ def lib():
             vp, vp, vp, vp,                  # diagnostics
             i64, i64, ctypes.c_int]          # token range, threads
         L.oracle_c128_compress_store.restype = ctypes.c_int
+        L.oracle_compress_store.argtypes = [i64, i64, i64] + L.oracle_c128_compress_store.argtypes
+        L.oracle_compress_store.restype = ctypes.c_int
         L.oracle_bf16_bits.argtypes = [dbl]
         L.oracle_bf16_bits.restype = ctypes.c_uint16
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
@@ -158,8 +160,10 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
         normd = np.full((T, HEAD), np.nan)
     status = np.full(T, -99, np.int32)
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
-    rc = lib().oracle_c128_compress_store(
-        state.ctypes.data, state.shape[0], sbs, s0, s1,
+    cr = int(getattr(wl, "compress_ratio", 128))
+    overlap = int(getattr(wl, "overlap", 0))
+    rc = lib().oracle_compress_store(
+        cr, overlap, (1 + overlap) * HEAD, state.ctypes.data, state.shape[0], sbs, s0, s1,
         bt.ctypes.data, bt.shape[0], bt.shape[1], bt.strides[0] // 4,
         arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data, T,
         rms_w.ctypes.data, float(wl.eps), cs.ctypes.data, cs.shape[0], cs.strides[0] // 4,

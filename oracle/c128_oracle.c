@@ -1,5 +1,6 @@
 /*
- * CPU ORACLE for the DeepSeek-V4 C128 compress-store path.
+ * CPU ORACLE for the DeepSeek-V4 sparse-attention compress-store path (C128, and the C4
+ * compressor with its overlapping window).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file: only the tests, the smoke check and the bench's
@@ -11,14 +12,18 @@
  * `_fused_kv_compress_norm_rope_insert_sparse_attn` and its two-stage twins
  * `_compress_gather_split_sparse_attn` / `_finalize_norm_rope_quant_store_sparse_attn`:
  *
- *   gate    a token is active iff its state slot is >= 0 and (pos+1) % 128 == 0
- *   gather  window rows q = pos-127 .. pos, row q at state[bt[req][q / bs]][q % bs]
+ *   gate    a token is active iff its state slot is >= 0 and (pos+1) % CR == 0
+ *           (compress ratio CR = 128, or 4 for the C4 compressor)
+ *   gather  window rows q = pos - (1+OV)*CR + 1 .. pos (overlap OV = 0 for C128, 1 for C4),
+ *           row q at state[bt[req][q / bs]][q % bs]; rows with q < 0 take no part;
+ *           window row i reads its kv at column offset h_i = (i >= CR ? 512 : 0) of the state
+ *           row and its score at state_width + h_i (state_width = 512 for C128, 1024 for C4)
  *   pool    c_j = sum_i softmax_i(score_ij) * kv_ij          (per column j < 512)
  *   norm    n_j = c_j / sqrt(mean_j c_j^2 + eps) * w_j
  *   quant   dims < 448: bf16 round trip, per-64 absmax (floor 1e-4), UE8M0
  *           exponent e = ceil(log2(absmax / 448)), e4m3fn codes of x * 2^-e
- *   rope    dims 448..511: interleaved pairs rotated by the table row of the
- *           window's first position (pos // 128) * 128, stored as bf16
+ *   rope    dims 448..511: interleaved pairs rotated by the table row
+ *           (pos // CR) * CR, stored as bf16
  *   insert  kv slot s >= 0: block s / kv_bs, offset s % kv_bs;
  *           576 data bytes at blk*stride0 + off*576,
  *           8 scale bytes (7 exponents + a zero pad) at blk*stride0 + kv_bs*576 + off*8
@@ -41,11 +46,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define HEAD 512        /* head size = state width */
+#define HEAD 512        /* head size */
 #define NOPE 448        /* FP8 dims */
 #define ROPE 64         /* bf16 RoPE dims */
 #define HALF_ROPE 32
-#define CR 128          /* compress ratio: rows per window */
+#define MAX_ROWS 256    /* (1 + overlap) * compress ratio, at most 2 * 128 */
 #define QBLOCK 64       /* quantisation block */
 #define NQ (NOPE / QBLOCK)
 #define RECORD 576      /* 448 fp8 bytes + 64 bf16 */
@@ -145,6 +150,7 @@ int oracle_ue8m0_exponent(double absmax) {
  * --------------------------------------------------------------------- */
 
 typedef struct {
+  int64_t cr, overlap, state_width;            /* compress ratio, 0/1, score column offset */
   const float* state;
   int64_t n_state_blocks, state_bs, s0, s1;    /* element strides */
   const int32_t* block_table;
@@ -169,6 +175,7 @@ typedef struct {
 enum { ST_INACTIVE = 0, ST_WRITTEN = 1, ST_NO_SLOT = 2, ST_BAD_INDEX = -1 };
 
 static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn, double* n) {
+  const int64_t CR = a->cr;
   /* gate */
   int32_t slot = a->slot_mapping[t];
   int64_t pos = a->positions[t];
@@ -176,32 +183,42 @@ static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn
 
   int64_t req = a->token_to_req[t];
   if (req < 0 || req >= a->bt_rows) return ST_BAD_INDEX;
-  int64_t start = pos - CR + 1;
+  int64_t nrows = (1 + a->overlap) * CR;
+  int64_t start = pos - nrows + 1;
   if ((pos / a->state_bs) >= a->bt_cols) return ST_BAD_INDEX;
 
-  /* gather: row pointers of the window, in window order */
-  const float* row[CR];
-  for (int i = 0; i < CR; ++i) {
+  /* gather: row pointers of the window, in window order, already offset to the kv half the
+     row contributes (the score of the same row is state_width further on); rows before
+     position 0 are left out */
+  const float* row[MAX_ROWS];
+  int valid[MAX_ROWS];
+  for (int64_t i = 0; i < nrows; ++i) {
     int64_t q = start + i;
+    valid[i] = q >= 0;
+    if (!valid[i]) continue;
     int64_t blk = a->block_table[req * a->bt_stride + q / a->state_bs];
     if (blk < 0 || blk >= a->n_state_blocks) return ST_BAD_INDEX;
-    row[i] = a->state + blk * a->s0 + (q % a->state_bs) * a->s1;
+    int64_t head_offset = (i >= CR) ? HEAD : 0;
+    row[i] = a->state + blk * a->s0 + (q % a->state_bs) * a->s1 + head_offset;
   }
 
   /* pool: softmax over the window rows of each score column, weights applied to kv */
+  const int64_t SW = a->state_width;
   for (int j = 0; j < HEAD; ++j) {
     double M = -INFINITY;
-    for (int i = 0; i < CR; ++i) {
-      double s = row[i][HEAD + j];
+    for (int64_t i = 0; i < nrows; ++i) {
+      if (!valid[i]) continue;
+      double s = row[i][SW + j];
       if (s > M) M = s;
     }
-    double w[CR], L = 0.0;
-    for (int i = 0; i < CR; ++i) {
-      w[i] = exp((double)row[i][HEAD + j] - M);
+    double w[MAX_ROWS], L = 0.0;
+    for (int64_t i = 0; i < nrows; ++i) {
+      w[i] = valid[i] ? exp((double)row[i][SW + j] - M) : 0.0;
       L += w[i];
     }
     double num = 0.0, an = 0.0;
-    for (int i = 0; i < CR; ++i) {
+    for (int64_t i = 0; i < nrows; ++i) {
+      if (!valid[i]) continue;
       double p = w[i] / L;
       num += p * (double)row[i][j];
       an += p * fabs((double)row[i][j]);
@@ -285,14 +302,16 @@ static void* oracle_worker(void* p) {
 }
 
 /*
- * Run the oracle over tokens [t_lo, t_hi) with `nthreads` threads.  Tokens
+ * Run the oracle over tokens [t_lo, t_hi) with `nthreads` threads, for compress ratio
+ * `compress_ratio`, overlap 0 or 1 and the score column offset `state_width` (>= the kv
+ * columns (1 + overlap) * 512 a row holds).  Tokens
  * are independent; each thread takes a contiguous range.  The k_cache is
  * modified in place exactly where the path writes.  Diagnostics arrays (may
  * be NULL) are [T, 512] fp64, rows of tokens that do not pass the gate are
  * left untouched.  Returns 0, or -1 on bad arguments.
  */
-int oracle_c128_compress_store(
-    const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
+int oracle_compress_store(
+    int64_t compress_ratio, int64_t overlap, int64_t state_width, const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
     const int32_t* block_table, int64_t bt_rows, int64_t bt_cols, int64_t bt_stride,
     const int32_t* token_to_req, const int32_t* positions, const int32_t* slot_mapping,
     int64_t T, const float* rms_w, double eps, const float* cos_sin, int64_t cs_rows,
@@ -301,9 +320,11 @@ int oracle_c128_compress_store(
     double* out_normed, int32_t* out_status, int64_t t_lo, int64_t t_hi, int nthreads) {
   if (!state || !block_table || !token_to_req || !positions || !slot_mapping || !rms_w ||
       !cos_sin || !k_cache || !kv_slot_mapping || state_bs < 1 || kv_bs < 1 || T < 0 ||
-      t_lo < 0 || t_hi > T || t_lo > t_hi || nthreads < 1)
+      t_lo < 0 || t_hi > T || t_lo > t_hi || nthreads < 1 || compress_ratio < 1 ||
+      (overlap != 0 && overlap != 1) || (1 + overlap) * compress_ratio > MAX_ROWS ||
+      state_width < (1 + overlap) * HEAD)
     return -1;
-  oracle_args a = {state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
+  oracle_args a = {compress_ratio, overlap, state_width, state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
                    bt_stride, token_to_req, positions, slot_mapping, T, rms_w, eps, cos_sin,
                    cs_rows, cs_stride, k_cache, kv_bs, kv_stride0, n_kv_blocks, kv_slot_mapping,
                    out_compressed, out_absnorm, out_normed, out_status};
@@ -328,6 +349,23 @@ int oracle_c128_compress_store(
   for (int i = 0; i < nthreads; ++i)
     if (created[i]) pthread_join(th[i], NULL);
   return 0;
+}
+
+
+/* The C128 path: compress ratio 128, no overlap, state width 512. */
+int oracle_c128_compress_store(
+    const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
+    const int32_t* block_table, int64_t bt_rows, int64_t bt_cols, int64_t bt_stride,
+    const int32_t* token_to_req, const int32_t* positions, const int32_t* slot_mapping,
+    int64_t T, const float* rms_w, double eps, const float* cos_sin, int64_t cs_rows,
+    int64_t cs_stride, uint8_t* k_cache, int64_t kv_bs, int64_t kv_stride0, int64_t n_kv_blocks,
+    const int32_t* kv_slot_mapping, double* out_compressed, double* out_absnorm,
+    double* out_normed, int32_t* out_status, int64_t t_lo, int64_t t_hi, int nthreads) {
+  return oracle_compress_store(128, 0, HEAD, state, n_state_blocks, state_bs, s0, s1, block_table,
+                               bt_rows, bt_cols, bt_stride, token_to_req, positions, slot_mapping,
+                               T, rms_w, eps, cos_sin, cs_rows, cs_stride, k_cache, kv_bs,
+                               kv_stride0, n_kv_blocks, kv_slot_mapping, out_compressed,
+                               out_absnorm, out_normed, out_status, t_lo, t_hi, nthreads);
 }
 
 /* Array forms of the format helpers, for exhaustive tests. */

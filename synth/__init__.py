@@ -128,22 +128,26 @@ def permutation(n: int, seed: int, stream: int) -> np.ndarray:
     return np.argsort(keys, kind="stable").astype(np.int64)
 
 
-def alloc_state(n_blocks: int, row_width: int = ROW, row_pad: int = 0, block_pad: int = 0):
-    """fp32 state view ``[n_blocks, 8, row_width]``; padding (in floats) between rows and blocks."""
+def alloc_state(n_blocks: int, row_width: int = ROW, row_pad: int = 0, block_pad: int = 0,
+                rows_per_block: int = STATE_BLOCK):
+    """fp32 state view ``[n_blocks, rows_per_block, row_width]``; padding (in floats) between
+    rows and blocks."""
     stride1 = row_width + row_pad
-    stride0 = STATE_BLOCK * stride1 + block_pad
+    stride0 = rows_per_block * stride1 + block_pad
     base = np.zeros(n_blocks * stride0, dtype=np.float32)
     view = np.lib.stride_tricks.as_strided(
-        base, shape=(n_blocks, STATE_BLOCK, row_width), strides=(stride0 * 4, stride1 * 4, 4))
+        base, shape=(n_blocks, rows_per_block, row_width), strides=(stride0 * 4, stride1 * 4, 4))
     return base, view
 
 
 def fill_state(state: np.ndarray, seed: int, kv_std: float = 1.0, score_std: float = 1.0,
-               score_mean_per_block=None, score_std_per_block=None, threads: int | None = None):
-    """kv columns ~ N(0, kv_std^2); score columns ~ N(mean_b, std_b^2)."""
+               score_mean_per_block=None, score_std_per_block=None, threads: int | None = None,
+               width: int = HEAD):
+    """kv columns [0, width) ~ N(0, kv_std^2); score columns [width, 2*width) ~ N(mean_b, std_b^2)
+    (width = 512 for the C128 state, 1024 for the C4 state with its two overlapping halves)."""
     nb = state.shape[0]
     s0, s1, s2 = (x // 4 for x in state.strides)
-    assert s2 == 1 and state.shape[1] == STATE_BLOCK and state.shape[2] >= ROW
+    assert s2 == 1 and state.shape[2] >= 2 * width
     mean_ptr = std_ptr = None
     if score_mean_per_block is not None:
         score_mean_per_block = np.ascontiguousarray(score_mean_per_block, dtype=np.float64)
@@ -154,7 +158,7 @@ def fill_state(state: np.ndarray, seed: int, kv_std: float = 1.0, score_std: flo
         assert score_std_per_block.shape == (nb,)
         std_ptr = score_std_per_block.ctypes.data
     rc = _load().synth_fill_pool(
-        state.ctypes.data, nb, STATE_BLOCK, s0, s1, HEAD, HEAD, HEAD, seed, kv_std, mean_ptr,
+        state.ctypes.data, nb, state.shape[1], s0, s1, width, width, width, seed, kv_std, mean_ptr,
         std_ptr, 0.0, score_std, threads or default_threads())
     assert rc == 0
 
@@ -195,6 +199,8 @@ class Workload:
     state_base: np.ndarray | None = None
     k_cache_base: np.ndarray | None = None
     info: dict = field(default_factory=dict)
+    compress_ratio: int = 128
+    overlap: int = 0
 
     @property
     def num_tokens(self) -> int:
@@ -202,7 +208,7 @@ class Workload:
 
     def active_mask(self) -> np.ndarray:
         p = self.positions.astype(np.int64)
-        return (self.slot_mapping >= 0) & (p >= 0) & ((p + 1) % WINDOW == 0)
+        return (self.slot_mapping >= 0) & (p >= 0) & ((p + 1) % self.compress_ratio == 0)
 
     def written_mask(self) -> np.ndarray:
         return self.active_mask() & (self.kv_slot_mapping >= 0)
@@ -336,6 +342,84 @@ def scattered_batch(name: str, seed: int, num_tokens: int, num_reqs: int, n_bloc
         raise ValueError("not enough kv slots for the active tokens")
     wl.kv_slot_mapping[act] = permutation(n_kv, seed, 35)[:int(act.sum())].astype(np.int32)
     wl.info = {"kind": "scattered", "tokens": T, "requests": num_reqs, "pool_blocks": n_blocks}
+    return wl
+
+
+C4_RATIO = 4
+C4_ROWS = 2 * C4_RATIO       # window rows: the previous window's 4 and the current 4
+C4_ROW = 4 * HEAD            # kv (2 x 512) | score (2 x 512)
+
+
+def c4_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
+                    table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int, state_bs: int = 8,
+                    score_std: float = math.sqrt(2.0), k_min: int = 1,
+                    threads: int | None = None) -> Workload:
+    """C4 compressor: one boundary token per request at position 4k-1, k ~ U{k_min..k_max}.
+
+    The window is rows pos-7 .. pos (rows before position 0 do not exist when k = 1).  Each
+    request's table columns covering its window get state blocks of their own (consecutive
+    entries of a seeded permutation of the pool), so windows never share a block; other table
+    entries hold arbitrary valid ids.  State rows are [S, state_bs, 2048]: kv of the previous-
+    and current-window projections, then their scores."""
+    T = num_tokens
+    if T > kv_blocks * kv_bs:
+        raise ValueError("not enough kv slots")
+    k = randint(T, k_min, k_max, seed, 40)
+    positions = (C4_RATIO * k - 1).astype(np.int64)
+    if int(positions.max(initial=0)) // state_bs >= table_cols:
+        raise ValueError("block table too narrow for k_max")
+    per_tok = -(-C4_ROWS // state_bs) + 1
+    if T * per_tok > n_blocks:
+        raise ValueError("pool too small for disjoint windows")
+    perm = permutation(n_blocks, seed, 41)
+    bt = (bits(T * table_cols, seed, 42) % np.uint64(n_blocks)).astype(np.int32).reshape(
+        T, table_cols)
+    for r in range(T):
+        lo = max(0, int(positions[r]) - (C4_ROWS - 1)) // state_bs
+        hi = int(positions[r]) // state_bs
+        bt[r, lo:hi + 1] = perm[r * per_tok:r * per_tok + (hi - lo + 1)]
+    last_blk = bt[np.arange(T), positions // state_bs].astype(np.int64)
+    slot_mapping = (last_blk * state_bs + positions % state_bs).astype(np.int32)
+    kv_slots = permutation(kv_blocks * kv_bs, seed, 43)[:T].astype(np.int32)
+    state_base, state = alloc_state(n_blocks, row_width=C4_ROW, rows_per_block=state_bs)
+    fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * HEAD)
+    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs)
+    wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),
+                  slot_mapping, _rms_weight(seed), 1e-6, rope_table(cs_rows), kc, kv_slots, seed,
+                  state_base, kc_base, compress_ratio=C4_RATIO, overlap=1)
+    wl.info = {"kind": "c4 decode", "tokens": T, "pool_blocks": n_blocks, "state_bs": state_bs}
+    return wl
+
+
+def c4_varlen_prefill(name: str, seed: int, num_reqs: int, max_chunk: int, max_start: int,
+                      kv_bs: int, cs_rows: int, state_bs: int = 8, drop_frac: float = 0.1,
+                      score_std: float = math.sqrt(2.0), threads: int | None = None) -> Workload:
+    """C4 chunked prefill: request r holds positions start_r .. start_r + L_r - 1, contiguous,
+    request-major, L ~ U{1..max_chunk}, start ~ U{0..max_start}; every fourth position closes a
+    window.  Each request's table entries are distinct blocks of a pool sized for them; a seeded
+    ``drop_frac`` of slot_mapping is -1; every token gets a distinct kv slot."""
+    L = randint(num_reqs, 1, max_chunk, seed, 50)
+    start = randint(num_reqs, 0, max_start, seed, 51)
+    cols = int(-(-(max_start + max_chunk) // state_bs))
+    n_blocks = num_reqs * cols
+    bt = permutation(n_blocks, seed, 52).reshape(num_reqs, cols).astype(np.int32)
+    token_to_req = np.concatenate([np.full(int(L[r]), r, np.int32) for r in range(num_reqs)])
+    positions = np.concatenate(
+        [np.arange(int(start[r]), int(start[r] + L[r]), dtype=np.int64) for r in range(num_reqs)])
+    T = positions.shape[0]
+    blk = bt[token_to_req, positions // state_bs].astype(np.int64)
+    slot_mapping = blk * state_bs + positions % state_bs
+    slot_mapping[uniform(T, seed, 53) < drop_frac] = -1
+    kv_blocks = int(-(-T // kv_bs))
+    kv_slots = permutation(kv_blocks * kv_bs, seed, 54)[:T].astype(np.int32)
+    state_base, state = alloc_state(n_blocks, row_width=C4_ROW, rows_per_block=state_bs)
+    fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * HEAD)
+    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs)
+    wl = Workload(name, state, bt, token_to_req, positions.astype(np.int32),
+                  slot_mapping.astype(np.int32), _rms_weight(seed), 1e-6, rope_table(cs_rows),
+                  kc, kv_slots, seed, state_base, kc_base, compress_ratio=C4_RATIO, overlap=1)
+    wl.info = {"kind": "c4 varlen", "tokens": T, "requests": num_reqs, "pool_blocks": n_blocks,
+               "state_bs": state_bs}
     return wl
 
 
