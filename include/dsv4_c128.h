@@ -1,6 +1,6 @@
 /*
- * dsv4_c128.h -- C ABI of the DeepSeek-V4 C128 compress-store path on
- * MI355X (gfx950).
+ * dsv4_c128.h -- C ABI of the DeepSeek-V4 sparse-attention compress-store path on
+ * MI355X (gfx950): the C128 compressor (below) and the C4 compressor (dsv4_c4_*).
  *
  * What it computes (vLLM API page "fused_compress_quant_cache", DeepSeek-V4
  * common ops: the sparse-attention fused kernel
@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 3
+#define DSV4_ABI_VERSION 4
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -195,6 +195,50 @@ int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
  * list); 0 for num_tokens <= 0.  Host-only; no HIP call.
  */
 size_t dsv4_c128_varlen_workspace_bytes(int64_t num_tokens);
+
+/*
+ * The C4 compressor: the same fused computation with compress ratio 4 and an overlapping
+ * window (vLLM fused_compress_quant_cache page, sparse-attention fused kernel, with
+ * COMPRESS_RATIO = 4 and OVERLAP = 1; vLLM PR 44230, Summary: C4 keeps its fused path).
+ * For every token t whose state slot is >= 0 and whose position closes a 4-row window
+ * ((pos+1) % 4 == 0):
+ *   1. the window is the 8 rows q = pos-7 .. pos (rows with q < 0, which exist only at
+ *      pos = 3, take no part), row q at state_cache[block_table[token_to_req[t]][q / bs]]
+ *      [q % bs] with bs = state_cache.shape[1];
+ *   2. a state row is kv[0:1024] | score[1024:2048]; window row i < 4 (the previous window)
+ *      contributes kv[j] and score[1024 + j], row i >= 4 (the current window) kv[512 + j] and
+ *      score[1536 + j], for output column j < 512;
+ *   3. compressed[j] = sum_i softmax_i(score) * kv over those rows, then steps 3-6 of the C128
+ *      path with the RoPE table row (pos / 4) * 4, into the same 584-byte k_cache layout.
+ *
+ *   state_cache     f32 [S, bs, 2048]  bs >= 1 (any block size), stride[2] == 1,
+ *                                      stride[1] >= 2048, stride[0] >= bs * stride[1]; data
+ *                                      and both strides 16-byte aligned
+ *   block_table     i32 [R, M]         stride[1] == 1, M >= 1 (a token needs column pos / bs)
+ *   every other argument as for dsv4_c128_compress_store.
+ * Device-resident indices are range-checked as in the C128 path.
+ */
+int dsv4_c4_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                           const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                           const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                           const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                           const dsv4_tensor* kv_slot_mapping, void* stream);
+
+/* dsv4_c4_compress_store that also writes the fp32 pooled vectors, as
+ * dsv4_c128_compress_store_debug does (compressed_out may be NULL). */
+int dsv4_c4_compress_store_debug(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                 const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                 const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                 float eps, const dsv4_tensor* cos_sin,
+                                 const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+                                 float* compressed_out, void* stream);
+
+/* Host-only validation of the C4 descriptors (as dsv4_c128_validate). */
+int dsv4_c4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                     const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                     const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                     const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                     const dsv4_tensor* kv_slot_mapping);
 
 /*
  * Host-only validation of the descriptors, exactly as the compute entry

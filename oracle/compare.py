@@ -87,7 +87,8 @@ def rope_band(wl, orc, t: int) -> tuple[np.ndarray, np.ndarray]:
     r = 1.0 / np.sqrt(np.mean(c * c) + float(wl.eps))
     w = wl.rms_w.astype(np.float64)
     dn = r * np.abs(w) * COMPRESSED_REL * A + COMPRESSED_REL * np.abs(n)
-    P = (int(wl.positions[t]) // 128) * 128
+    cr = int(getattr(wl, "compress_ratio", 128))
+    P = (int(wl.positions[t]) // cr) * cr
     cs = wl.cos_sin[P].astype(np.float64)
     C, S = cs[:32], cs[32:64]
     x, y = n[448::2], n[449::2]

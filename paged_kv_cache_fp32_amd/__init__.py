@@ -97,6 +97,12 @@ def library():
         lib.dsv4_c128_compress_store_varlen.restype = ctypes.c_int
         lib.dsv4_c128_varlen_workspace_bytes.argtypes = [ctypes.c_int64]
         lib.dsv4_c128_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.dsv4_c4_compress_store.argtypes = args10 + [ctypes.c_void_p]
+        lib.dsv4_c4_compress_store.restype = ctypes.c_int
+        lib.dsv4_c4_compress_store_debug.argtypes = args10 + [ctypes.c_void_p, ctypes.c_void_p]
+        lib.dsv4_c4_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_c4_validate.argtypes = args10
+        lib.dsv4_c4_validate.restype = ctypes.c_int
         lib.dsv4_c128_validate.argtypes = args10
         lib.dsv4_c128_validate.restype = ctypes.c_int
         lib.dsv4_e4m3_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -238,6 +244,34 @@ def compress_store_varlen(state_cache, block_table, token_to_req, positions, slo
         workspace.numel() * workspace.element_size(), s))
 
 
+def c4_compress_store(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                      eps, cos_sin, k_cache, kv_slot_mapping, compressed_out=None,
+                      stream: int | None = None) -> None:
+    """The C4 compressor (ratio 4, overlapping 8-row window; state rows kv 2x512 | score 2x512,
+    any state block size) into the same k_cache layout; ``compressed_out`` as in
+    ``compress_store_debug`` (optional)."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    dev = _require_cuda(ts + ([compressed_out] if compressed_out is not None else []))
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 512)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_c4_compress_store_debug(*refs[:6], float(eps), *refs[6:], out_ptr, s))
+
+
+def c4_validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                cos_sin, k_cache, kv_slot_mapping) -> int:
+    """Host-only validation of C4 descriptors; returns the status code."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping)
+    _, refs = _descriptors(ts)
+    return library().dsv4_c4_validate(*refs[:6], float(eps), *refs[6:])
+
+
 def validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
              cos_sin, k_cache, kv_slot_mapping) -> int:
     """Host-only validation of the descriptors (no HIP call); returns the status code."""
@@ -260,6 +294,6 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
 
 
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
-           "compress_store_varlen", "varlen_workspace_bytes",
+           "compress_store_varlen", "varlen_workspace_bytes", "c4_compress_store", "c4_validate",
            "validate", "e4m3_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

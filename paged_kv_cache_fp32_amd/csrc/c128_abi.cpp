@@ -1,6 +1,6 @@
-// C ABI of the C128 compress-store library: descriptor validation (host
-// only), launch, error codes and the per-thread error message.  The contract
-// is documented in include/dsv4_c128.h.
+// C ABI of the compress-store library (C128 and C4): descriptor validation
+// (host only), launch, error codes and the per-thread error message.  The
+// contract is documented in include/dsv4_c128.h.
 //
 // The validation mirrors the layout limits of the DeepSeek-V4 C128 path
 // (vLLM PR 44230, "Summary" and "Changes": head 512, state width 512,
@@ -64,10 +64,25 @@ int check_token_array(const dsv4_tensor* t, const char* name, int64_t T) {
   return DSV4_OK;
 }
 
+// State-cache layout a compressor expects: row width in floats, rows per block (0 = any
+// positive count) and the fewest block-table columns a window can need.
+struct StateLayout {
+  const char* path;
+  int64_t row_floats;
+  int64_t block_rows;
+  int64_t min_bt_cols;
+};
+// C128: kv 512 | score 512, blocks of 8 rows, 16 blocks per window.
+constexpr StateLayout kC128Layout{"C128", dsv4::kRowFloats, dsv4::kStateBlock,
+                                  dsv4::kWindowBlocks};
+// C4 with its overlapping window: kv 2 x 512 | score 2 x 512; any block size.
+constexpr StateLayout kC4Layout{"C4", 4 * dsv4::kHead, 0, 1};
+
 int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_tensor* t2r,
                  const dsv4_tensor* pos, const dsv4_tensor* slot, const dsv4_tensor* w, float eps,
                  const dsv4_tensor* cs, const dsv4_tensor* kc, const dsv4_tensor* kvs,
-                 dsv4::C128Params* out) {
+                 dsv4::C128Params* out, const StateLayout& L = kC128Layout,
+                 int32_t* state_bs = nullptr) {
   using namespace dsv4;
   int rc;
   // positions defines T; every other token array must match it
@@ -78,30 +93,32 @@ int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_ten
   if ((rc = check_token_array(slot, "slot_mapping", T))) return rc;
   if ((rc = check_token_array(kvs, "kv_slot_mapping", T))) return rc;
 
-  // state cache f32 [S, 8, 1024]
+  // state cache f32 [S, rows per block, row floats]
   if ((rc = check_tensor(state, "state_cache", DSV4_F32, 3))) return rc;
-  if (state->shape[1] != kStateBlock)
-    return fail(DSV4_ERR_SHAPE, "state_cache: block size %lld, the C128 path needs 8",
-                static_cast<long long>(state->shape[1]));
-  if (state->shape[2] != kRowFloats)
-    return fail(DSV4_ERR_SHAPE,
-                "state_cache: row of %lld floats, the C128 path needs 1024 (kv 512 | score 512)",
-                static_cast<long long>(state->shape[2]));
+  const int64_t sbs = state->shape[1];
+  if (L.block_rows ? sbs != L.block_rows : sbs < 1)
+    return fail(DSV4_ERR_SHAPE, "state_cache: block size %lld, the %s path needs %s",
+                static_cast<long long>(sbs), L.path, L.block_rows ? "8" : ">= 1");
+  if (state->shape[2] != L.row_floats)
+    return fail(DSV4_ERR_SHAPE, "state_cache: row of %lld floats, the %s path needs %lld",
+                static_cast<long long>(state->shape[2]), L.path,
+                static_cast<long long>(L.row_floats));
   if (state->stride[2] != 1) return fail(DSV4_ERR_STRIDE, "state_cache: stride[2] must be 1");
-  if (state->stride[1] < kRowFloats)
-    return fail(DSV4_ERR_STRIDE, "state_cache: stride[1] = %lld < 1024 (rows overlap)",
-                static_cast<long long>(state->stride[1]));
-  if (state->stride[0] < kStateBlock * state->stride[1])
-    return fail(DSV4_ERR_STRIDE, "state_cache: stride[0] = %lld < 8 * stride[1] (blocks overlap)",
+  if (state->stride[1] < L.row_floats)
+    return fail(DSV4_ERR_STRIDE, "state_cache: stride[1] = %lld < %lld (rows overlap)",
+                static_cast<long long>(state->stride[1]), static_cast<long long>(L.row_floats));
+  if (sbs > 1 ? state->stride[0] < sbs * state->stride[1] : state->stride[0] < L.row_floats)
+    return fail(DSV4_ERR_STRIDE, "state_cache: stride[0] = %lld too small (blocks overlap)",
                 static_cast<long long>(state->stride[0]));
   if (!aligned16(state->data) || (state->stride[1] & 3) || (state->stride[0] & 3))
     return fail(DSV4_ERR_ALIGN, "state_cache: data and strides must be 16-byte aligned");
 
   // block table i32 [R, M]
   if ((rc = check_tensor(bt, "block_table", DSV4_I32, 2))) return rc;
-  if (bt->shape[1] < kWindowBlocks)
-    return fail(DSV4_ERR_SHAPE, "block_table: %lld columns, a C128 window needs 16",
-                static_cast<long long>(bt->shape[1]));
+  if (bt->shape[1] < L.min_bt_cols)
+    return fail(DSV4_ERR_SHAPE, "block_table: %lld columns, a %s window needs %lld",
+                static_cast<long long>(bt->shape[1]), L.path,
+                static_cast<long long>(L.min_bt_cols));
   if (bt->stride[1] != 1) return fail(DSV4_ERR_STRIDE, "block_table: stride[1] must be 1");
   if (bt->shape[0] > 1 && bt->stride[0] < bt->shape[1])
     return fail(DSV4_ERR_STRIDE, "block_table: stride[0] < shape[1] (rows overlap)");
@@ -167,6 +184,7 @@ int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_ten
     out->kv_slot_mapping = static_cast<const int32_t*>(kvs->data);
     out->compressed_out = nullptr;
   }
+  if (state_bs) *state_bs = static_cast<int32_t>(sbs);
   g_last_error.clear();
   return DSV4_OK;
 }
@@ -299,6 +317,46 @@ int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
   if (err != hipSuccess)
     return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
   return DSV4_OK;
+}
+
+int dsv4_c4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                     const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                     const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                     const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                     const dsv4_tensor* kv_slot_mapping) {
+  return validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                      cos_sin, k_cache, kv_slot_mapping, nullptr, kC4Layout);
+}
+
+int dsv4_c4_compress_store_debug(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                 const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                 const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                 float eps, const dsv4_tensor* cos_sin,
+                                 const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+                                 float* compressed_out, void* stream) {
+  dsv4::C128Params p;
+  int32_t sbs = 0;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p, kC4Layout, &sbs);
+  if (rc) return rc;
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  p.compressed_out = compressed_out;
+  hipError_t err = dsv4::launch_c4_compress_store(p, sbs, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
+int dsv4_c4_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                           const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                           const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                           const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                           const dsv4_tensor* kv_slot_mapping, void* stream) {
+  return dsv4_c4_compress_store_debug(state_cache, block_table, token_to_req, positions,
+                                      slot_mapping, rms_w, eps, cos_sin, k_cache,
+                                      kv_slot_mapping, nullptr, stream);
 }
 
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -54,12 +54,15 @@ class DeviceWorkload:
     def run(self, debug=False, splits=None, varlen=False):
         """One call; splits None = the plain entry points, else compress_store_ex with that
         split count (0 = automatic) and a workspace of the size it needs; varlen = the
-        compacted schedule (compress_store_varlen)."""
+        compacted schedule (compress_store_varlen).  A C4 workload (compress ratio 4) always
+        goes to c4_compress_store."""
         comp = None
         if debug:
             comp = torch.full((self.wl.num_tokens, 512), float("nan"), dtype=torch.float32,
                               device=self.state.device)
-        if varlen:
+        if getattr(self.wl, "compress_ratio", 128) == 4:
+            c128.c4_compress_store(*self.args(), compressed_out=comp)
+        elif varlen:
             ws = torch.empty(max(c128.varlen_workspace_bytes(self.wl.num_tokens), 16),
                              dtype=torch.uint8, device=self.state.device)
             c128.compress_store_varlen(*self.args(), compressed_out=comp, workspace=ws)

@@ -281,3 +281,45 @@ def test_varlen_argument_errors_before_launch():
     assert varlen_call(bad) == -4
     e = valid_args(T=0)
     assert varlen_call(e) == 0
+
+
+def c4_args(T=4, S=16, sbs=8, bs=4):
+    a = valid_args(T=T, S=S, bs=bs)
+    a["state_cache"] = torch.zeros(S, sbs, 2048, dtype=torch.float32)
+    a["block_table"] = torch.zeros(T, 4, dtype=torch.int32)
+    return a
+
+
+def c4_validate(a):
+    return c128.c4_validate(a["state_cache"], a["block_table"], a["token_to_req"],
+                            a["positions"], a["slot_mapping"], a["rms_w"], a["eps"],
+                            a["cos_sin"], a["k_cache"], a["kv_slot_mapping"])
+
+
+@pytest.mark.parametrize("sbs", [1, 2, 4, 8, 16, 64])
+def test_c4_accepts_any_state_block_size(sbs):
+    assert c4_validate(c4_args(sbs=sbs)) == 0, c128.last_error()
+
+
+def test_c4_layout_errors():
+    """The C4 state row is 2048 floats (kv 2x512 | score 2x512); the C128 row is rejected and
+    the C4 row is rejected by the C128 entry point; strides and alignment as for C128."""
+    a = c4_args()
+    a["state_cache"] = torch.zeros(16, 8, 1024)
+    assert c4_validate(a) == -4 and "2048" in c128.last_error()
+    a = c4_args()
+    assert call_validate(a) == -4
+    a = c4_args()
+    a["state_cache"] = torch.zeros(16, 8, 4096)[:, :, :2048]
+    assert c4_validate(a) == 0
+    a["state_cache"] = torch.zeros(16, 8, 2049)[:, :, :2048]
+    assert c4_validate(a) == -6
+    a = c4_args()
+    a["state_cache"] = torch.zeros(8, 16, 2048).transpose(0, 1)
+    assert c4_validate(a) == -5
+    a = c4_args()
+    a["block_table"] = torch.zeros(4, 0, dtype=torch.int32)
+    assert c4_validate(a) == -4
+    a = c4_args()
+    a["block_table"] = torch.zeros(4, 1, dtype=torch.int32)
+    assert c4_validate(a) == 0

@@ -1,0 +1,115 @@
+"""GPU parity of the C4 compressor kernel (dsv4_c4_compress_store) against the CPU oracle:
+decode batches over several state block sizes (including windows at position 3, whose
+previous window does not exist), a chunked-prefill batch where every fourth token is active,
+gate decisions and out-of-range device indices, and the 16384-token batch the bench times."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.compare import compare
+from synth.device import run_gpu
+
+pytestmark = pytest.mark.gpu
+
+THREADS = synth.default_threads()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check(wl, label, debug=True):
+    announce(label)
+    body, comp, guards_ok = run_gpu(wl, debug=debug)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, body, comp
+
+
+def c4_batch(T, seed, state_bs=8, k_max=16, kv_bs=16, score_std=2 ** 0.5):
+    return synth.c4_decode_batch(f"c4 decode T={T} bs={state_bs}", seed, T,
+                                 T * (-(-8 // state_bs) + 1) + 8, k_max,
+                                 -(-4 * k_max // state_bs) + 1, kv_bs=kv_bs,
+                                 kv_blocks=-(-2 * T // kv_bs), cs_rows=4 * k_max + 4,
+                                 state_bs=state_bs, score_std=score_std)
+
+
+@pytest.mark.parametrize("state_bs", [8, 4, 16, 1])
+@pytest.mark.parametrize("T", [1, 5, 64, 1000])
+def test_c4_decode_parity(T, state_bs):
+    wl = c4_batch(T, 300 + T + state_bs, state_bs=state_bs, k_max=3 if T == 1 else 16)
+    rep, *_ = check(wl, f"c4 decode T={T} state bs={state_bs}")
+    assert rep["written"] == T
+
+
+def test_c4_first_windows():
+    """Every token at position 3 (only the current window exists) or 7 (first full overlap)."""
+    wl = c4_batch(40, 41, k_max=2)
+    assert set(wl.positions.tolist()) == {3, 7}
+    rep, *_ = check(wl, "c4 positions 3 and 7")
+    assert rep["written"] == 40
+
+
+def test_c4_varlen_prefill():
+    wl = synth.c4_varlen_prefill("c4 varlen prefill", 1202, 16, 512, 1024, kv_bs=64,
+                                 cs_rows=1600)
+    rep, *_ = check(wl, "c4 varlen prefill")
+    assert rep["written"] == int(wl.written_mask().sum()) > 300
+
+
+def test_c4_peaky_scores():
+    wl = c4_batch(256, 53, score_std=4.0)
+    check(wl, "c4 peaky scores (std 4)")
+
+
+def test_c4_gate_and_bad_indices():
+    wl = c4_batch(8, 61, k_max=8)
+    wl.positions[:] = np.array([2, 4, 7, 6, 11, 15, 19, 23], np.int32)
+    wl.slot_mapping[:] = np.array([1, 1, 1, 1, -1, 1, 1, 1], np.int32)
+    wl.kv_slot_mapping[5] = -1
+    wl.token_to_req[6] = wl.block_table.shape[0]          # request out of range
+    wl.kv_slot_mapping[7] = wl.k_cache.shape[0] * wl.k_cache.shape[1]  # kv slot out of range
+    announce("c4 gate / bad indices")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [0, 0, 1, 0, 0, 2, -1, -1]
+    wl.kv_slot_mapping[[6, 7]] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 1
+    assert np.isfinite(comp[2]).all() and np.isfinite(comp[5]).all() and np.isfinite(comp[7]).all()
+    assert np.isnan(comp[[0, 1, 3, 4, 6]]).all()
+
+
+def test_c4_bad_block_id_and_rope_row():
+    wl = c4_batch(4, 67, k_max=8)
+    wl.positions[:] = 31
+    bs = wl.state.shape[1]
+    wl.block_table[1, 31 // bs] = wl.state.shape[0] + 3   # block id out of range
+    wl.cos_sin = wl.cos_sin[:28].copy()                    # rope row 28 missing for pos 31
+    wl.positions[3] = 23                                    # rope row 20: present
+    announce("c4 bad block id / rope row")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [-1, -1, -1, 1]
+    wl.kv_slot_mapping[[0, 1, 2]] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+
+
+def test_c4_large_batch():
+    """The 16384-token C4 decode batch of the bench, every token against the oracle."""
+    wl = synth.c4_decode_batch("c4 decode T=16384", 1005, 16384, 16384 * 2, 1024, 512,
+                               kv_bs=64, kv_blocks=256, cs_rows=4096)
+    rep, *_ = check(wl, "c4 decode T=16384", debug=False)
+    assert rep["written"] == 16384
