@@ -47,9 +47,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# C4 (ratio 4, 8-row overlapping window): per active token 4 KiB for each window row that
+# exists (8, or 4 at position 3: kv half 2 KiB + score half 2 KiB), 4 B per distinct block id
+# of the window, token_to_req + kv slot, one RoPE row, the k_cache record
+C4_ROW_BYTES = 2 * 512 * 4
+C4_TOKEN_BYTES = 8 + 256 + 584
+
+
 def algorithmic_bytes(wl) -> int:
-    act = int(wl.active_mask().sum())
-    return act * ACTIVE_TOKEN_BYTES + wl.num_tokens * ANY_TOKEN_BYTES + CALL_BYTES
+    act = wl.active_mask()
+    if getattr(wl, "compress_ratio", 128) == 4:
+        pos = wl.positions[act].astype(np.int64)
+        bs = wl.state.shape[1]
+        first = np.maximum(pos - 7, 0)
+        rows = pos - first + 1
+        cols = pos // bs - first // bs + 1
+        per = rows * C4_ROW_BYTES + cols * 4 + C4_TOKEN_BYTES
+        return int(per.sum()) + wl.num_tokens * ANY_TOKEN_BYTES + CALL_BYTES
+    return int(act.sum()) * ACTIVE_TOKEN_BYTES + wl.num_tokens * ANY_TOKEN_BYTES + CALL_BYTES
 
 
 def kernel_source_hash() -> str:
@@ -252,7 +267,9 @@ def sweep(args, path):
         """splits None: the single-pass entry point; else compress_store_ex with that split
         count (0 = automatic) and a workspace per window set; varlen: the compacted schedule
         (compress_store_varlen) with a workspace per window set."""
-        if varlen:
+        if getattr(dws[0].wl, "compress_ratio", 128) == 4:
+            calls = [(lambda d=d: c128.c4_compress_store(*d.args(), stream=sid)) for d in dws]
+        elif varlen:
             wss = [torch.empty(max(16, c128.varlen_workspace_bytes(d.wl.num_tokens)),
                                dtype=torch.uint8, device=dev) for d in dws]
             calls = [(lambda d=d, w=w: c128.compress_store_varlen(*d.args(), workspace=w,
@@ -273,8 +290,9 @@ def sweep(args, path):
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
         rec = {"workload": name, "tokens": wl.num_tokens,
                "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
-               "entry": "varlen (compacted)" if varlen else
-                        ("single pass" if splits is None else f"fan-out splits={splits}"),
+               "entry": ("c4" if getattr(wl, "compress_ratio", 128) == 4 else
+                         "varlen (compacted)" if varlen else
+                         "single pass" if splits is None else f"fan-out splits={splits}"),
                "algorithmic_bytes_per_call": nbytes,
                "warm_us_median": round(float(np.median(per)) * 1e3, 2),
                "warm_us_mean": round(float(np.mean(per)) * 1e3, 2)}
@@ -331,7 +349,51 @@ def sweep(args, path):
             for sp in ([0, 2, 4, 8, 16] if args.sweep_splits else [0]):
                 measure(f"cfg3 decode sweep T={T}", dws, 1000, splits=sp)
         del dws
+    del pool, pool_dev
+    torch.cuda.empty_cache()
+    c4_sweep(want, measure, dev)
     out.close()
+
+
+def c4_slices(wl, T, n_sets):
+    """n_sets disjoint T-token slices of a C4 decode batch (each token has its own state
+    blocks and kv slot), sharing the pool."""
+    import dataclasses
+    out = []
+    for s in range(n_sets):
+        sl = slice(s * T, (s + 1) * T)
+        out.append(dataclasses.replace(
+            wl, block_table=wl.block_table[sl], token_to_req=np.arange(T, dtype=np.int32),
+            positions=wl.positions[sl], slot_mapping=wl.slot_mapping[sl],
+            kv_slot_mapping=wl.kv_slot_mapping[sl]))
+    return out
+
+
+def c4_sweep(want, measure, dev):
+    """C4 compressor: decode batches cut from one 16384-token batch (2 GiB pool, disjoint
+    windows), and a chunked prefill."""
+    import synth
+    from synth.device import DeviceWorkload
+    names = [f"c4 decode T={T}" for T in (1, 16, 128, 1024, 4096, 16384)]
+    if any(want(n) for n in names):
+        big = synth.c4_decode_batch("c4 decode T=16384", 1005, 16384, 16384 * 2, 1024, 512,
+                                    kv_bs=64, kv_blocks=256, cs_rows=4096)
+        pool_dev = None
+        for T, name in zip((1, 16, 128, 1024, 4096, 16384), names):
+            if not want(name):
+                continue
+            dws = []
+            for wl in c4_slices(big, T, min(64, 16384 // T)):
+                d = DeviceWorkload(wl, device=dev, state=pool_dev)
+                pool_dev = (d.state_buf, d.state)
+                dws.append(d)
+            measure(name, dws, 1000 if T <= 4096 else 200)
+            del dws
+        del big, pool_dev
+    if want("c4 varlen prefill"):
+        wl = synth.c4_varlen_prefill("c4 varlen prefill", 1202, 64, 1024, 4096, kv_bs=64,
+                                     cs_rows=8192)
+        measure("c4 varlen prefill", [DeviceWorkload(wl, device=dev)], 1000)
 
 
 def read_line(args):

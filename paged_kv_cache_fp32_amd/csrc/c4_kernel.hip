@@ -9,15 +9,21 @@
 // the 64 rope dims at table row (pos // 4) * 4, and the paged insert, all as in the C128 path.
 //
 // A state row is kv[0:1024] | score[1024:2048] (2 x 512 each).  A token reads 8 rows x 4 KiB
-// = 32 KiB, a sixteenth of a C128 token, so the whole token fits one wave:
+// = 32 KiB, a sixteenth of a C128 token, so a token fits one wave:
 //
-//  * One wave per token, four tokens per workgroup; no LDS and no barrier.  Lane l owns
-//    columns 4l .. 4l+3 ("v0") and 256 + 4l .. +3 ("v1"), so each wave-wide load is a 1 KiB
-//    contiguous segment of a row.
-//  * All loads of the window (up to 8 rows x 4 vectors, non-temporal) are issued before any
-//    arithmetic; the per-column softmax is a plain max / exp2-sum over registers.
+//  * Lane l owns columns 4l .. 4l+3 ("v0") and 256 + 4l .. +3 ("v1"), so each wave-wide load
+//    is a 1 KiB contiguous segment of a row.  All loads of a window (up to 8 rows x 4 vectors,
+//    non-temporal) are issued before any arithmetic; the per-column softmax is a plain max /
+//    exp2-sum over registers.  No barrier anywhere: waves are independent.
+//  * A wave takes 1 to 8 consecutive tokens (enough waves for 2 per SIMD first).  Their
+//    metadata is resolved up front with one lane per (token, window row): gate, request, block
+//    column, block id and range checks in two rounds of loads, so the token loop only moves row
+//    offsets from lanes to scalars and streams.
 //  * Epilogue within the wave: RMSNorm by one wave reduction; a 64-column quant block is 16
 //    lanes of v0 (blocks 0..3) or of v1 (blocks 4..6); lanes 48..63 hold the RoPE dims in v1.
+//    Records go to the wave's LDS stage and reach the k_cache after the wave's last state
+//    read: measured on MI355X, the same 584-byte records stored token by token cost about 12%
+//    of the call, because the writes land in the middle of the HBM read stream.
 //
 // HBM-bound gather-reduce again (about 0.6 flop per byte): no MFMA.
 
@@ -30,7 +36,10 @@ namespace {
 constexpr int kC4Ratio = 4;
 constexpr int kC4Rows = 2 * kC4Ratio;       // previous window + current window
 constexpr int kC4ScoreOffset = 2 * kHead;   // score part of a row: 2 x 512 columns in
-constexpr int kC4TokensPerGroup = 4;        // waves (tokens) per workgroup
+constexpr int kC4WavesPerGroup = 4;         // waves per workgroup
+constexpr int kC4MaxTokensPerWave = 8;      // 8 tokens x 8 window rows = the 64 lanes
+constexpr int kC4TargetWaves = 2048;        // 2 waves per SIMD on 256 CUs
+constexpr int kC4WavesPerSimd = 3;          // room for all 32 window loads in flight
 
 // Per-column softmax-weighted sum over NR rows held in registers (scores scaled to log2).
 template <int NR>
@@ -48,34 +57,40 @@ __device__ __forceinline__ float pool_column(const float (&s)[NR], const float (
   return a / l;
 }
 
-// Load NR window rows (row pointers already offset to the row's kv half) and pool the lane's
-// 8 columns into c[0..3] (v0) and c[4..7] (v1).
-template <int NR>
+// Load NR window rows (wave-uniform row pointers, already offset to the row's kv half) and
+// pool the lane's 8 columns into c[0..3] (v0) and c[4..7] (v1); all 4*NR loads are issued
+// before the first use.
+template <int NR, int HALVES = 1>
 __device__ __forceinline__ void pool_rows(const float* const (&rowp)[NR], uint32_t col,
                                           float (&c)[8]) {
-  float4 kv0[NR], kv1[NR], sc0[NR], sc1[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    kv0[r] = load_stream(rowp[r] + col);
-    kv1[r] = load_stream(rowp[r] + 256 + col);
-    sc0[r] = load_stream(rowp[r] + kC4ScoreOffset + col);
-    sc1[r] = load_stream(rowp[r] + kC4ScoreOffset + 256 + col);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float s[NR], v[NR];
+  for (int h = 0; h < HALVES; ++h) {
+    constexpr int NV = 2 / HALVES;  // column vectors per phase
+    float4 kv[NV][NR], sc[NV][NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      s[r] = (k == 0 ? sc0[r].x : k == 1 ? sc0[r].y : k == 2 ? sc0[r].z : sc0[r].w) * kLog2e;
-      v[r] = k == 0 ? kv0[r].x : k == 1 ? kv0[r].y : k == 2 ? kv0[r].z : kv0[r].w;
-    }
-    c[k] = pool_column<NR>(s, v);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      s[r] = (k == 0 ? sc1[r].x : k == 1 ? sc1[r].y : k == 2 ? sc1[r].z : sc1[r].w) * kLog2e;
-      v[r] = k == 0 ? kv1[r].x : k == 1 ? kv1[r].y : k == 2 ? kv1[r].z : kv1[r].w;
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t off = col + 256u * static_cast<uint32_t>(h * NV + v);
+        kv[v][r] = load_stream(rowp[r] + off);
+        sc[v][r] = load_stream(rowp[r] + kC4ScoreOffset + off);
+      }
     }
-    c[4 + k] = pool_column<NR>(s, v);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float s[NR], x[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float4& a = sc[v][r];
+          const float4& b = kv[v][r];
+          s[r] = (k == 0 ? a.x : k == 1 ? a.y : k == 2 ? a.z : a.w) * kLog2e;
+          x[r] = k == 0 ? b.x : k == 1 ? b.y : k == 2 ? b.z : b.w;
+        }
+        c[4 * (h * NV + v) + k] = pool_column<NR>(s, x);
+      }
+    }
   }
 }
 
@@ -97,126 +112,182 @@ __device__ __forceinline__ uint8_t scale_byte(int e) {
   return static_cast<uint8_t>(b < 0 ? 0 : (b > 255 ? 255 : b));
 }
 
-template <bool kDebug>
-__global__ void __launch_bounds__(64 * kC4TokensPerGroup)
-    c4_compress_store_kernel(const C128Params p, int32_t state_bs) {
+template <bool kDebug, int WPE>
+__global__ void __launch_bounds__(64 * kC4WavesPerGroup)
+    __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+    c4_compress_store_kernel(const C128Params p, int32_t state_bs, int32_t state_bs_log2,
+                             int32_t tokens_per_wave) {
+  __shared__ __align__(16) uint8_t stage_all[kC4WavesPerGroup][kC4MaxTokensPerWave * kSlotBytes];
+  __shared__ int32_t slot_all[kC4WavesPerGroup][kC4MaxTokensPerWave];
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kC4TokensPerGroup + wave;
-  if (t >= p.num_tokens) return;
+  uint8_t* stage = stage_all[wave];
+  int32_t* slot_of = slot_all[wave];
+  const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * kC4WavesPerGroup + wave) *
+                        tokens_per_wave;
+  if (lane < kC4MaxTokensPerWave) slot_of[lane] = -1;
 
-  // ---- gate and window (wave-uniform); out-of-range device indices skip the token
-  const int32_t pos = p.positions[t];
-  const int32_t slot = p.slot_mapping[t];
-  if (slot < 0 || pos < 0 || (pos & (kC4Ratio - 1)) != kC4Ratio - 1) return;
-  const int32_t req = p.token_to_req[t];
-  if (req < 0 || req >= p.bt_rows || pos / state_bs >= p.bt_cols) return;
-  const int32_t rope_row = pos & ~(kC4Ratio - 1);  // (pos // 4) * 4
-  if (rope_row >= p.cs_rows) return;
-  const int32_t* bt = p.block_table + static_cast<int64_t>(req) * p.bt_stride;
-  const int32_t start = pos - (kC4Rows - 1);
-  const float* rowp[kC4Rows];
-  bool ok = true;
-#pragma unroll
-  for (int i = 0; i < kC4Rows; ++i) {
-    const int32_t q = start + i;
-    rowp[i] = p.state;
-    if (q < 0) continue;
-    const int32_t b = bt[q / state_bs];
-    ok &= static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks);
-    rowp[i] = p.state + static_cast<int64_t>(b) * p.s0 + static_cast<int64_t>(q % state_bs) * p.s1 +
-              (i >= kC4Ratio ? kHead : 0);
+  // ---- metadata of the wave's tokens, one lane per (token k, window row i): gate, request,
+  // block column, block id and their range checks, all in two rounds of loads.  A token goes
+  // on only if every one of its 8 lanes passes.  Rows before position 0 (pos 3, i < 4) are not
+  // read and need no block.
+  const int mk = lane >> 3, mi = lane & 7;
+  const int64_t mt = tbase + mk;
+  int32_t mpos = -1, mkv = -1;
+  int64_t moff = 0;
+  bool mok = false;
+  if (mk < tokens_per_wave && mt < p.num_tokens) {
+    mpos = p.positions[mt];
+    const int32_t slot = p.slot_mapping[mt];
+    if (slot >= 0 && mpos >= 0 && (mpos & (kC4Ratio - 1)) == kC4Ratio - 1) {
+      const int32_t req = p.token_to_req[mt];
+      mok = req >= 0 && req < p.bt_rows && mpos / state_bs < p.bt_cols &&
+            (mpos & ~(kC4Ratio - 1)) < p.cs_rows;
+      const int32_t q = mpos - (kC4Rows - 1) + mi;
+      if (mok && q >= 0) {
+        const int32_t bcol = state_bs_log2 >= 0 ? q >> state_bs_log2 : q / state_bs;
+        const int32_t boff = q - bcol * state_bs;
+        const int32_t b = p.block_table[static_cast<int64_t>(req) * p.bt_stride + bcol];
+        mok = static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks);
+        moff = static_cast<int64_t>(b) * p.s0 + static_cast<int64_t>(boff) * p.s1 +
+               (mi >= kC4Ratio ? kHead : 0);
+      }
+      if (mi == 0) mkv = p.kv_slot_mapping[mt];
+    }
   }
-  if (!ok) return;
+  const uint64_t good = __builtin_amdgcn_ballot_w64(mok);
 
-  // ---- pool: 8 rows, or only the current window's 4 when the previous one lies before 0
   const uint32_t col = static_cast<uint32_t>(lane) * 4;
-  float c[8];
-  if (start >= 0) {
-    pool_rows<kC4Rows>(rowp, col, c);
-  } else {
-    const float* const cur[kC4Ratio] = {rowp[4], rowp[5], rowp[6], rowp[7]};
-    pool_rows<kC4Ratio>(cur, col, c);
-  }
-
-  // ---- RMSNorm over the 512 columns (one wave)
-  float ss = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ss = __builtin_fmaf(c[k], c[k], ss);
-  ss = wave_sum(ss);
-  const float rrms = 1.0f / __builtin_sqrtf(ss * (1.0f / kHead) + p.eps);
   const float4 w0 = *reinterpret_cast<const float4*>(p.rms_w + col);
   const float4 w1 = *reinterpret_cast<const float4*>(p.rms_w + 256 + col);
-  const float n[8] = {c[0] * rrms * w0.x, c[1] * rrms * w0.y, c[2] * rrms * w0.z,
-                      c[3] * rrms * w0.w, c[4] * rrms * w1.x, c[5] * rrms * w1.y,
-                      c[6] * rrms * w1.z, c[7] * rrms * w1.w};
-  if constexpr (kDebug) {
-    float* out = p.compressed_out + t * kHead;
-    *reinterpret_cast<float4*>(out + col) = make_float4(c[0], c[1], c[2], c[3]);
-    *reinterpret_cast<float4*>(out + 256 + col) = make_float4(c[4], c[5], c[6], c[7]);
-  }
+  const int j = lane & 15;  // RoPE pair index of lanes 48..63
 
-  // ---- per-64 absmax of the bf16-rounded values (every lane joins both shuffles)
-  float u[8];
+  for (int k = 0; k < tokens_per_wave; ++k) {
+    if (((good >> (8 * k)) & 0xffu) != 0xffu) continue;  // inactive or an index out of range
+    const int32_t pos = __builtin_amdgcn_readlane(mpos, 8 * k);
+    const int32_t kv_slot = __builtin_amdgcn_readlane(mkv, 8 * k);
+    const int32_t rope_row = pos & ~(kC4Ratio - 1);  // (pos // 4) * 4
+    const float* rowp[kC4Rows];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) u[k] = bf16_round(n[k]);
-  const float a0 = group16_max(__builtin_fmaxf(
-      __builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
-      __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3]))));
-  const float a1 = group16_max(__builtin_fmaxf(
-      __builtin_fmaxf(__builtin_fabsf(u[4]), __builtin_fabsf(u[5])),
-      __builtin_fmaxf(__builtin_fabsf(u[6]), __builtin_fabsf(u[7]))));
-
-  // ---- paged insert
-  const int32_t kv_slot = p.kv_slot_mapping[t];
-  if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return;
-  const int32_t kb = kv_slot / p.kv_bs;
-  const int32_t ko = kv_slot - kb * p.kv_bs;
-  uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
-  uint8_t* rec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
-  uint8_t* scl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
-                 static_cast<int64_t>(ko) * kScaleBytes;
-  const int group = lane >> 4;
-
-  // v0: columns 0..255, quant blocks 0..3
-  const int e0 = ue8m0_exponent(a0);
-  *reinterpret_cast<uint32_t*>(rec + col) = quant4(u, 0, e0);
-  if ((lane & 15) == 0) scl[group] = scale_byte(e0);
-
-  if (lane < 48) {
-    // v1: columns 256..447, quant blocks 4..6
-    const int e1 = ue8m0_exponent(a1);
-    *reinterpret_cast<uint32_t*>(rec + 256 + col) = quant4(u, 4, e1);
-    if ((lane & 15) == 0) scl[4 + group] = scale_byte(e1);
-  } else {
-    // v1 of lanes 48..63: RoPE dims 448 + 4j .. +3, pairs 2j and 2j + 1
-    const int j = lane - 48;
+    for (int i = 0; i < kC4Rows; ++i) {
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(moff), 8 * k + i);
+      const uint32_t hi =
+          __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(moff) >> 32),
+                                    8 * k + i);
+      rowp[i] = p.state + static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    }
     const float* cs = p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
-    const float c0 = cs[2 * j], c1 = cs[2 * j + 1];
-    const float s0 = cs[kRope / 2 + 2 * j], s1 = cs[kRope / 2 + 2 * j + 1];
-    const float x0 = n[4] * c0 - n[5] * s0;
-    const float y0 = n[5] * c0 + n[4] * s0;
-    const float x1 = n[6] * c1 - n[7] * s1;
-    const float y1 = n[7] * c1 + n[6] * s1;
-    const uint32_t lo = bf16_bits(x0) | (bf16_bits(y0) << 16);
-    const uint32_t hi = bf16_bits(x1) | (bf16_bits(y1) << 16);
-    *reinterpret_cast<uint2*>(rec + kNope + 8 * j) = make_uint2(lo, hi);
-    if (j == 0) scl[kNumQuant] = 0;  // pad byte
+    const float cos0 = cs[2 * j], cos1 = cs[2 * j + 1];
+    const float sin0 = cs[kRope / 2 + 2 * j], sin1 = cs[kRope / 2 + 2 * j + 1];
+
+    // ---- pool: 8 rows, or only the current window's 4 at position 3
+    float c[8];
+    if (pos >= kC4Rows - 1) {
+      pool_rows<kC4Rows>(rowp, col, c);
+    } else {
+      const float* const cur[kC4Ratio] = {rowp[4], rowp[5], rowp[6], rowp[7]};
+      pool_rows<kC4Ratio>(cur, col, c);
+    }
+
+    // ---- RMSNorm over the 512 columns (one wave)
+    float ss = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) ss = __builtin_fmaf(c[m], c[m], ss);
+    ss = wave_sum(ss);
+    const float rrms = 1.0f / __builtin_sqrtf(ss * (1.0f / kHead) + p.eps);
+    const float n[8] = {c[0] * rrms * w0.x, c[1] * rrms * w0.y, c[2] * rrms * w0.z,
+                        c[3] * rrms * w0.w, c[4] * rrms * w1.x, c[5] * rrms * w1.y,
+                        c[6] * rrms * w1.z, c[7] * rrms * w1.w};
+    if constexpr (kDebug) {
+      float* out = p.compressed_out + (tbase + k) * kHead;
+      *reinterpret_cast<float4*>(out + col) = make_float4(c[0], c[1], c[2], c[3]);
+      *reinterpret_cast<float4*>(out + 256 + col) = make_float4(c[4], c[5], c[6], c[7]);
+    }
+    if (kv_slot < 0 || kv_slot >= p.n_kv_slots) continue;
+
+    // ---- per-64 absmax of the bf16-rounded values, UE8M0 / E4M3, RoPE -> this token's
+    // 584-byte slot in the wave's LDS stage
+    float u[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) u[m] = bf16_round(n[m]);
+    const float a0 = group16_max(__builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
+        __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3]))));
+    const float a1 = group16_max(__builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fabsf(u[4]), __builtin_fabsf(u[5])),
+        __builtin_fmaxf(__builtin_fabsf(u[6]), __builtin_fabsf(u[7]))));
+    uint8_t* rec = stage + k * kSlotBytes;
+    uint8_t* scl = rec + kRecordBytes;
+    const int group = lane >> 4;
+    // v0: columns 0..255, quant blocks 0..3
+    const int e0 = ue8m0_exponent(a0);
+    *reinterpret_cast<uint32_t*>(rec + col) = quant4(u, 0, e0);
+    if ((lane & 15) == 0) scl[group] = scale_byte(e0);
+    if (lane < 48) {
+      // v1: columns 256..447, quant blocks 4..6
+      const int e1 = ue8m0_exponent(a1);
+      *reinterpret_cast<uint32_t*>(rec + 256 + col) = quant4(u, 4, e1);
+      if ((lane & 15) == 0) scl[4 + group] = scale_byte(e1);
+    } else {
+      // v1 of lanes 48..63: RoPE dims 448 + 4j .. +3, pairs 2j and 2j + 1
+      const float x0 = n[4] * cos0 - n[5] * sin0;
+      const float y0 = n[5] * cos0 + n[4] * sin0;
+      const float x1 = n[6] * cos1 - n[7] * sin1;
+      const float y1 = n[7] * cos1 + n[6] * sin1;
+      const uint32_t lo = bf16_bits(x0) | (bf16_bits(y0) << 16);
+      const uint32_t hi = bf16_bits(x1) | (bf16_bits(y1) << 16);
+      *reinterpret_cast<uint2*>(rec + kNope + 8 * j) = make_uint2(lo, hi);
+      if (j == 0) scl[kNumQuant] = 0;  // pad byte
+    }
+    if (lane == 0) slot_of[k] = kv_slot;
   }
+
+  // ---- paged insert of every staged record, after the wave's last state read: the k_cache
+  // writes reach HBM in bursts instead of interleaved with the read stream (8-byte stores;
+  // records and scale groups are 8-byte aligned)
+  for (int k = 0; k < tokens_per_wave; ++k) {
+    const int32_t kv_slot = slot_of[k];
+    if (kv_slot < 0) continue;
+    const int32_t kb = kv_slot / p.kv_bs;
+    const int32_t ko = kv_slot - kb * p.kv_bs;
+    uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+    uint8_t* grec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
+    uint8_t* gscl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+                    static_cast<int64_t>(ko) * kScaleBytes;
+    const uint8_t* rec = stage + k * kSlotBytes;
+    *reinterpret_cast<uint2*>(grec + 8 * lane) = *reinterpret_cast<const uint2*>(rec + 8 * lane);
+    if (lane < 8)
+      *reinterpret_cast<uint2*>(grec + 512 + 8 * lane) =
+          *reinterpret_cast<const uint2*>(rec + 512 + 8 * lane);
+    else if (lane == 8)
+      *reinterpret_cast<uint2*>(gscl) = *reinterpret_cast<const uint2*>(rec + kRecordBytes);
+  }
+}
+
+int c4_tokens_per_wave(int64_t num_tokens) {
+  // Enough waves for 2 per SIMD (2048 on 256 CUs x 4 SIMDs) before a wave takes more than
+  // one token; at most kC4MaxTokensPerWave (its LDS stage).
+  int64_t k = (num_tokens + kC4TargetWaves - 1) / kC4TargetWaves;
+  return static_cast<int>(k < 1 ? 1 : (k > kC4MaxTokensPerWave ? kC4MaxTokensPerWave : k));
 }
 
 }  // namespace
 
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  const int64_t groups = (static_cast<int64_t>(p.num_tokens) + kC4TokensPerGroup - 1) /
-                         kC4TokensPerGroup;
+  const int32_t kpw = c4_tokens_per_wave(p.num_tokens);
+  const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
+  const int64_t groups = (waves + kC4WavesPerGroup - 1) / kC4WavesPerGroup;
   const dim3 grid(static_cast<unsigned>(groups));
-  const dim3 block(64 * kC4TokensPerGroup);
+  const dim3 block(64 * kC4WavesPerGroup);
+  const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
   if (p.compressed_out)
-    c4_compress_store_kernel<true><<<grid, block, 0, stream>>>(p, state_bs);
+    c4_compress_store_kernel<true, kC4WavesPerSimd><<<grid, block, 0, stream>>>(p, state_bs, lg,
+                                                                                 kpw);
   else
-    c4_compress_store_kernel<false><<<grid, block, 0, stream>>>(p, state_bs);
+    c4_compress_store_kernel<false, kC4WavesPerSimd><<<grid, block, 0, stream>>>(p, state_bs, lg,
+                                                                                  kpw);
   return hipGetLastError();
 }
 
