@@ -1,4 +1,5 @@
-"""CPU oracle of the sparse-attention compress-store path, C128 and C4 (test infrastructure).
+"""CPU oracle of the compress-store paths: the sparse-attention compressors C128 and C4 and the
+indexer's FP8 compressor (test infrastructure).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never links or calls
@@ -23,6 +24,7 @@ _SRC = os.path.join(_HERE, "c128_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 HEAD = 512
+INDEXER_HEAD = 128
 NOPE = 448
 ROPE = 64
 RECORD = 576
@@ -63,6 +65,9 @@ def lib():
         L.oracle_c128_compress_store.restype = ctypes.c_int
         L.oracle_compress_store.argtypes = [i64, i64, i64] + L.oracle_c128_compress_store.argtypes
         L.oracle_compress_store.restype = ctypes.c_int
+        L.oracle_compress_store_fmt.argtypes = [i64, ctypes.c_int, i64, i64, i64] + \
+            L.oracle_c128_compress_store.argtypes
+        L.oracle_compress_store_fmt.restype = ctypes.c_int
         L.oracle_bf16_bits.argtypes = [dbl]
         L.oracle_bf16_bits.restype = ctypes.c_uint16
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
@@ -126,7 +131,10 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
 
     ``tokens``: ``(lo, hi)`` range, default all.  The workload's k_cache is
     copied first, so the workload stays untouched.  Diagnostics rows of
-    tokens outside the range or that fail the gate are NaN.
+    tokens outside the range or that fail the gate are NaN.  Compress ratio
+    and overlap come from the workload (C128 when absent); an indexer workload
+    (``wl.indexer``) has head 128 and the indexer's cache format, and its
+    ``normed`` rows hold the values that were quantised (after RoPE).
     """
     T = wl.num_tokens
     lo, hi = (0, T) if tokens is None else tokens
@@ -153,17 +161,19 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
     arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in
             (wl.token_to_req, wl.positions, wl.slot_mapping, wl.kv_slot_mapping)]
     rms_w = np.ascontiguousarray(wl.rms_w, dtype=np.float32)
+    indexer = bool(getattr(wl, "indexer", False))
+    head = INDEXER_HEAD if indexer else HEAD
     comp = absn = normd = None
     if diagnostics:
-        comp = np.full((T, HEAD), np.nan)
-        absn = np.full((T, HEAD), np.nan)
-        normd = np.full((T, HEAD), np.nan)
+        comp = np.full((T, head), np.nan)
+        absn = np.full((T, head), np.nan)
+        normd = np.full((T, head), np.nan)
     status = np.full(T, -99, np.int32)
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
     cr = int(getattr(wl, "compress_ratio", 128))
     overlap = int(getattr(wl, "overlap", 0))
-    rc = lib().oracle_compress_store(
-        cr, overlap, (1 + overlap) * HEAD, state.ctypes.data, state.shape[0], sbs, s0, s1,
+    rc = lib().oracle_compress_store_fmt(
+        head, int(indexer), cr, overlap, (1 + overlap) * head, state.ctypes.data, state.shape[0], sbs, s0, s1,
         bt.ctypes.data, bt.shape[0], bt.shape[1], bt.strides[0] // 4,
         arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data, T,
         rms_w.ctypes.data, float(wl.eps), cs.ctypes.data, cs.shape[0], cs.strides[0] // 4,

@@ -1,6 +1,6 @@
 /*
- * CPU ORACLE for the DeepSeek-V4 sparse-attention compress-store path (C128, and the C4
- * compressor with its overlapping window).
+ * CPU ORACLE for the DeepSeek-V4 compress-store paths: the sparse-attention compressors (C128,
+ * and C4 with its overlapping window) and the indexer's FP8 compressor.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file: only the tests, the smoke check and the bench's
@@ -27,6 +27,14 @@
  *   insert  kv slot s >= 0: block s / kv_bs, offset s % kv_bs;
  *           576 data bytes at blk*stride0 + off*576,
  *           8 scale bytes (7 exponents + a zero pad) at blk*stride0 + kv_bs*576 + off*8
+ *
+ * The indexer's compressor (same page, kernel `_fused_kv_compress_norm_rope_insert_indexer_attn`)
+ * pools a head of 128 the same way, then, after RMSNorm:
+ *   rope    dims 64..127: interleaved pairs rotated by table row (pos // CR) * CR, kept in fp32
+ *   quant   all 128 dims, after the rotation: bf16 round trip, one absmax (floor 1e-4),
+ *           e = ceil(log2(absmax / 448)), e4m3fn codes of x * 2^-e, and the scale 2^e as fp32
+ *   insert  128 code bytes at blk*stride0 + off*128, the fp32 scale at blk*stride0 +
+ *           kv_bs*128 + off*4
  *
  * Readings where the pages leave a point open (each one is listed with its
  * reason in the design notes of the repository):
@@ -56,6 +64,10 @@
 #define RECORD 576      /* 448 fp8 bytes + 64 bf16 */
 #define SCALE_DIM 8     /* 7 UE8M0 bytes + 1 pad */
 #define FP8_MAX 448.0
+#define IDX_HEAD 128    /* indexer head size */
+#define IDX_NOPE 64     /* indexer dims before the RoPE dims */
+#define IDX_RECORD 128  /* indexer fp8 bytes per token */
+#define IDX_SCALE 4     /* one fp32 scale per token */
 
 /* ------------------------------------------------------------------------
  * Number formats, from their definitions.
@@ -150,6 +162,8 @@ int oracle_ue8m0_exponent(double absmax) {
  * --------------------------------------------------------------------- */
 
 typedef struct {
+  int64_t head;                                /* 512 (sparse attention) or 128 (indexer) */
+  int indexer;                                 /* 0: sparse-attention k_cache, 1: indexer fp8 */
   int64_t cr, overlap, state_width;            /* compress ratio, 0/1, score column offset */
   const float* state;
   int64_t n_state_blocks, state_bs, s0, s1;    /* element strides */
@@ -173,6 +187,53 @@ typedef struct {
 } oracle_args;
 
 enum { ST_INACTIVE = 0, ST_WRITTEN = 1, ST_NO_SLOT = 2, ST_BAD_INDEX = -1 };
+
+/*
+ * Indexer record of token t from its normalised values n[0..128): RoPE first (dims 64..127,
+ * GPT-J pairs, table row (pos // CR) * CR; the rotated fp64 value is held in fp32, the page's
+ * type), then one quantisation block over all 128 dims, then the insert.  On return n holds
+ * the values that were quantised (before their bf16 round trip), in fp64.
+ */
+static int oracle_indexer_insert(const oracle_args* a, int64_t t, int64_t pos, double* n) {
+  int64_t kv_slot = a->kv_slot_mapping[t];
+  if (kv_slot < 0) return ST_NO_SLOT;
+  int64_t kblk = kv_slot / a->kv_bs, koff = kv_slot % a->kv_bs;
+  if (kblk >= a->n_kv_blocks) return ST_BAD_INDEX;
+  int64_t P = (pos / a->cr) * a->cr;
+  if (P >= a->cs_rows) return ST_BAD_INDEX;
+
+  /* RoPE in fp64 on the normalised pairs (64+2m, 65+2m), m < 32 */
+  const float* cs = a->cos_sin + P * a->cs_stride;
+  double r[IDX_HEAD];
+  for (int j = 0; j < IDX_NOPE; ++j) r[j] = n[j];
+  for (int m = 0; m < HALF_ROPE; ++m) {
+    double x = n[IDX_NOPE + 2 * m], y = n[IDX_NOPE + 2 * m + 1];
+    double C = cs[m], S = cs[HALF_ROPE + m];
+    r[IDX_NOPE + 2 * m] = x * C - y * S;
+    r[IDX_NOPE + 2 * m + 1] = y * C + x * S;
+  }
+
+  /* one quantisation block: fp32, bf16 round trip, absmax, UE8M0 exponent, codes, fp32 scale */
+  uint8_t* blockp = a->k_cache + kblk * a->kv_stride0;
+  uint8_t* data = blockp + koff * IDX_RECORD;
+  uint8_t* scale = blockp + a->kv_bs * IDX_RECORD + koff * IDX_SCALE;
+  double u[IDX_HEAD], amax = 0.0;
+  for (int j = 0; j < IDX_HEAD; ++j) {
+    u[j] = oracle_bf16_value(oracle_bf16_bits((double)(float)r[j]));
+    if (fabs(u[j]) > amax) amax = fabs(u[j]);
+  }
+  int e = oracle_ue8m0_exponent(amax);
+  for (int j = 0; j < IDX_HEAD; ++j) {
+    double x = ldexp(u[j], -e);
+    if (x > FP8_MAX) x = FP8_MAX;
+    if (x < -FP8_MAX) x = -FP8_MAX;
+    data[j] = oracle_e4m3_code(x);
+  }
+  float sv = (float)ldexp(1.0, e); /* exact: -22 <= e <= 120 */
+  memcpy(scale, &sv, 4);            /* little-endian host, as the device */
+  for (int j = 0; j < IDX_HEAD; ++j) n[j] = r[j];
+  return ST_WRITTEN;
+}
 
 static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn, double* n) {
   const int64_t CR = a->cr;
@@ -198,13 +259,14 @@ static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn
     if (!valid[i]) continue;
     int64_t blk = a->block_table[req * a->bt_stride + q / a->state_bs];
     if (blk < 0 || blk >= a->n_state_blocks) return ST_BAD_INDEX;
-    int64_t head_offset = (i >= CR) ? HEAD : 0;
+    int64_t head_offset = (i >= CR) ? a->head : 0;
     row[i] = a->state + blk * a->s0 + (q % a->state_bs) * a->s1 + head_offset;
   }
 
   /* pool: softmax over the window rows of each score column, weights applied to kv */
   const int64_t SW = a->state_width;
-  for (int j = 0; j < HEAD; ++j) {
+  const int64_t H = a->head;
+  for (int j = 0; j < H; ++j) {
     double M = -INFINITY;
     for (int64_t i = 0; i < nrows; ++i) {
       if (!valid[i]) continue;
@@ -229,9 +291,10 @@ static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn
 
   /* RMSNorm */
   double ss = 0.0;
-  for (int j = 0; j < HEAD; ++j) ss += c[j] * c[j];
-  double rrms = 1.0 / sqrt(ss / HEAD + a->eps);
-  for (int j = 0; j < HEAD; ++j) n[j] = c[j] * rrms * (double)a->rms_w[j];
+  for (int j = 0; j < H; ++j) ss += c[j] * c[j];
+  double rrms = 1.0 / sqrt(ss / H + a->eps);
+  for (int j = 0; j < H; ++j) n[j] = c[j] * rrms * (double)a->rms_w[j];
+  if (a->indexer) return oracle_indexer_insert(a, t, pos, n);
 
   int64_t kv_slot = a->kv_slot_mapping[t];
   if (kv_slot < 0) return ST_NO_SLOT;
@@ -288,14 +351,16 @@ static void* oracle_worker(void* p) {
   const oracle_job* jb = (const oracle_job*)p;
   const oracle_args* a = jb->a;
   double c[HEAD], absn[HEAD], n[HEAD];
+  const int64_t H = a->head;
+  const size_t row = (size_t)H * sizeof(double);
   for (int64_t t = jb->lo; t < jb->hi; ++t) {
     for (int j = 0; j < HEAD; ++j) c[j] = absn[j] = n[j] = NAN;
     int st = oracle_token(a, t, c, absn, n);
     if (a->out_status) a->out_status[t] = st;
     if (st == ST_WRITTEN || st == ST_NO_SLOT) {
-      if (a->out_compressed) memcpy(a->out_compressed + t * HEAD, c, sizeof c);
-      if (a->out_absnorm) memcpy(a->out_absnorm + t * HEAD, absn, sizeof absn);
-      if (a->out_normed) memcpy(a->out_normed + t * HEAD, n, sizeof n);
+      if (a->out_compressed) memcpy(a->out_compressed + t * H, c, row);
+      if (a->out_absnorm) memcpy(a->out_absnorm + t * H, absn, row);
+      if (a->out_normed) memcpy(a->out_normed + t * H, n, row);
     }
   }
   return NULL;
@@ -310,8 +375,9 @@ static void* oracle_worker(void* p) {
  * be NULL) are [T, 512] fp64, rows of tokens that do not pass the gate are
  * left untouched.  Returns 0, or -1 on bad arguments.
  */
-int oracle_compress_store(
-    int64_t compress_ratio, int64_t overlap, int64_t state_width, const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
+int oracle_compress_store_fmt(
+    int64_t head, int indexer, int64_t compress_ratio, int64_t overlap, int64_t state_width,
+    const float* state, int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
     const int32_t* block_table, int64_t bt_rows, int64_t bt_cols, int64_t bt_stride,
     const int32_t* token_to_req, const int32_t* positions, const int32_t* slot_mapping,
     int64_t T, const float* rms_w, double eps, const float* cos_sin, int64_t cs_rows,
@@ -322,9 +388,9 @@ int oracle_compress_store(
       !cos_sin || !k_cache || !kv_slot_mapping || state_bs < 1 || kv_bs < 1 || T < 0 ||
       t_lo < 0 || t_hi > T || t_lo > t_hi || nthreads < 1 || compress_ratio < 1 ||
       (overlap != 0 && overlap != 1) || (1 + overlap) * compress_ratio > MAX_ROWS ||
-      state_width < (1 + overlap) * HEAD)
+      (indexer ? head != IDX_HEAD : head != HEAD) || state_width < (1 + overlap) * head)
     return -1;
-  oracle_args a = {compress_ratio, overlap, state_width, state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
+  oracle_args a = {head, indexer, compress_ratio, overlap, state_width, state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
                    bt_stride, token_to_req, positions, slot_mapping, T, rms_w, eps, cos_sin,
                    cs_rows, cs_stride, k_cache, kv_bs, kv_stride0, n_kv_blocks, kv_slot_mapping,
                    out_compressed, out_absnorm, out_normed, out_status};
@@ -351,6 +417,24 @@ int oracle_compress_store(
   return 0;
 }
 
+
+/* The sparse-attention compressors (head 512): compress ratio, overlap 0 or 1, state width. */
+int oracle_compress_store(
+    int64_t compress_ratio, int64_t overlap, int64_t state_width, const float* state,
+    int64_t n_state_blocks, int64_t state_bs, int64_t s0, int64_t s1,
+    const int32_t* block_table, int64_t bt_rows, int64_t bt_cols, int64_t bt_stride,
+    const int32_t* token_to_req, const int32_t* positions, const int32_t* slot_mapping,
+    int64_t T, const float* rms_w, double eps, const float* cos_sin, int64_t cs_rows,
+    int64_t cs_stride, uint8_t* k_cache, int64_t kv_bs, int64_t kv_stride0, int64_t n_kv_blocks,
+    const int32_t* kv_slot_mapping, double* out_compressed, double* out_absnorm,
+    double* out_normed, int32_t* out_status, int64_t t_lo, int64_t t_hi, int nthreads) {
+  return oracle_compress_store_fmt(HEAD, 0, compress_ratio, overlap, state_width, state,
+                                   n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
+                                   bt_stride, token_to_req, positions, slot_mapping, T, rms_w, eps,
+                                   cos_sin, cs_rows, cs_stride, k_cache, kv_bs, kv_stride0,
+                                   n_kv_blocks, kv_slot_mapping, out_compressed, out_absnorm,
+                                   out_normed, out_status, t_lo, t_hi, nthreads);
+}
 
 /* The C128 path: compress ratio 128, no overlap, state width 512. */
 int oracle_c128_compress_store(

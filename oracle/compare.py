@@ -17,6 +17,12 @@ Test infrastructure (see ``oracle/__init__.py``).  Pass criteria:
   1 ulp plus that tolerance carried through the norm and the rotation, and is
   counted ("rope_band");
 * debug fp32 compressed vector: |gpu - oracle| <= 1e-5 * sum_i p_ij |kv_ij|.
+
+The indexer cache (records of 128 E4M3 codes and one fp32 scale 2^e, quantised after RoPE)
+is checked by ``compare_indexer`` with the same rules: untouched bytes bit-exact; the scale
+bit-exact unless the block's absmax sits on a knife edge (then excused and compared by
+dequantised value); codes within 1 step on at most 0.1% of the elements; the debug pooled
+vector within the compressed tolerance.
 """
 
 from __future__ import annotations
@@ -135,6 +141,8 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
     """Compare the GPU k_cache bytes (the whole underlying buffer of the workload's
     k_cache view) with the oracle's, on ``tokens`` (indices; default all) and check
     that every byte outside the written records equals the initial buffer."""
+    if getattr(wl, "indexer", False):
+        return compare_indexer(wl, gpu_kc_base, orc, tokens, gpu_compressed, initial_kc_base)
     kc = wl.k_cache
     bs = kc.shape[1]
     stride0 = kc.strides[0]
@@ -235,4 +243,91 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
         rep["compressed_max_rel"] = worst_rel
         if worst > COMPRESSED_REL:
             rep["failures"].append(f"compressed error {worst:.3e} > 1e-5 of sum p|kv|")
+    return rep
+
+
+IDX_RECORD = 128
+IDX_SCALE = 4
+
+
+def indexer_offsets(slot: int, bs: int, stride0: int):
+    blk, off = slot // bs, slot % bs
+    return blk * stride0 + off * IDX_RECORD, blk * stride0 + bs * IDX_RECORD + off * IDX_SCALE
+
+
+def _compressed_check(wl, orc, toks, gpu_compressed, rep):
+    act = wl.active_mask()
+    worst = 0.0
+    for t in toks:
+        t = int(t)
+        if not act[t] or not np.isfinite(orc.compressed[t]).all():
+            continue
+        g = gpu_compressed[t].astype(np.float64)
+        ratio = np.abs(g - orc.compressed[t]) / np.maximum(orc.absnorm[t], 1e-300)
+        worst = max(worst, float(ratio.max()))
+    rep["compressed_max_ratio"] = worst
+    if worst > COMPRESSED_REL:
+        rep["failures"].append(f"compressed error {worst:.3e} > 1e-5 of sum p|kv|")
+
+
+def compare_indexer(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
+                    initial_kc_base: np.ndarray | None = None) -> Report:
+    """``compare`` for the indexer's FP8 cache ([bs*128 codes][bs*4 fp32 scales] blocks)."""
+    kc = wl.k_cache
+    bs = kc.shape[1]
+    stride0 = kc.strides[0]
+    init = wl.k_cache_base if initial_kc_base is None else initial_kc_base
+    assert gpu_kc_base.shape == init.shape
+    T = wl.num_tokens
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    written = wl.written_mask()
+    rep = Report(tokens=int(len(toks)), failures=[])
+
+    wmask = np.zeros(init.size, dtype=bool)
+    for s_ in wl.kv_slot_mapping[written]:
+        rec, scl = indexer_offsets(int(s_), bs, stride0)
+        wmask[rec:rec + IDX_RECORD] = True
+        wmask[scl:scl + IDX_SCALE] = True
+    diff = (gpu_kc_base != init) & ~wmask
+    rep["untouched_mismatch"] = int(diff.sum())
+    if rep["untouched_mismatch"]:
+        rep["failures"].append(f"{rep['untouched_mismatch']} bytes outside written records changed")
+
+    n_code = n_diff1 = n_scale_bad = n_excused = 0
+    for t in toks:
+        t = int(t)
+        if not written[t]:
+            continue
+        rec, scl = indexer_offsets(int(wl.kv_slot_mapping[t]), bs, stride0)
+        gc, oc = gpu_kc_base[rec:rec + IDX_RECORD], orc.k_cache_base[rec:rec + IDX_RECORD]
+        gs = float(gpu_kc_base[scl:scl + IDX_SCALE].view("<f4")[0])
+        os_ = float(orc.k_cache_base[scl:scl + IDX_SCALE].view("<f4")[0])
+        n_code += IDX_RECORD
+        if gs != os_:
+            # the block's fp64 absmax (orc.normed holds the quantised values, after RoPE)
+            amax = float(np.abs(orc.normed[t]).max()) if orc.normed is not None else 0.0
+            if knife_edge(amax):
+                n_excused += 1
+                gv, ov = e4m3_val(gc) * gs, e4m3_val(oc) * os_
+                step = max(gs, os_) * 2.0 ** (8 - 3)
+                if np.any(np.abs(gv - ov) > step):
+                    rep["failures"].append(f"token {t}: excused block values differ")
+                continue
+            n_scale_bad += 1
+            rep["failures"].append(f"token {t}: scale {gs} != {os_}")
+            continue
+        d = np.abs(e4m3_ord(gc) - e4m3_ord(oc))
+        n_diff1 += int((d == 1).sum())
+        if np.any(d > 1):
+            rep["failures"].append(f"token {t}: code differs by {int(d.max())}")
+    rep["written"] = int(written[toks].sum())
+    rep["scale_mismatch"] = n_scale_bad
+    rep["excused_blocks"] = n_excused
+    rep["code_diff1"] = n_diff1
+    rep["code_diff1_frac"] = (n_diff1 / n_code) if n_code else 0.0
+    rep["code_fail"] = rep["code_diff1_frac"] > CODE_FRAC_MAX
+    if rep["code_fail"]:
+        rep["failures"].append(f"code diff-1 fraction {rep['code_diff1_frac']:.2e} > 1e-3")
+    if gpu_compressed is not None and orc.compressed is not None:
+        _compressed_check(wl, orc, toks, gpu_compressed, rep)
     return rep

@@ -201,6 +201,7 @@ class Workload:
     info: dict = field(default_factory=dict)
     compress_ratio: int = 128
     overlap: int = 0
+    indexer: bool = False
 
     @property
     def num_tokens(self) -> int:
@@ -419,6 +420,63 @@ def c4_varlen_prefill(name: str, seed: int, num_reqs: int, max_chunk: int, max_s
                   slot_mapping.astype(np.int32), _rms_weight(seed), 1e-6, rope_table(cs_rows),
                   kc, kv_slots, seed, state_base, kc_base, compress_ratio=C4_RATIO, overlap=1)
     wl.info = {"kind": "c4 varlen", "tokens": T, "requests": num_reqs, "pool_blocks": n_blocks,
+               "state_bs": state_bs}
+    return wl
+
+
+INDEXER_HEAD = 128
+INDEXER_ROW = 4 * INDEXER_HEAD   # kv (2 x 128) | score (2 x 128)
+INDEXER_RECORD = 128             # fp8 bytes per token
+INDEXER_SCALE = 4                # one fp32 scale per token
+INDEXER_SLOT = INDEXER_RECORD + INDEXER_SCALE
+
+
+def alloc_indexer_cache(n_blocks: int, bs: int, block_pad: int = 0, fill: int = FILL):
+    """uint8 indexer k_cache view ``[n_blocks, bs, 132]``: each block holds ``bs`` records of 128
+    fp8 bytes, then ``bs`` fp32 scales; block stride ``bs*132 + block_pad`` bytes."""
+    stride0 = bs * INDEXER_SLOT + block_pad
+    base = np.full(n_blocks * stride0, fill, dtype=np.uint8)
+    view = np.lib.stride_tricks.as_strided(
+        base, shape=(n_blocks, bs, INDEXER_SLOT), strides=(stride0, INDEXER_SLOT, 1))
+    return base, view
+
+
+def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
+                         table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int,
+                         state_bs: int = 8, score_std: float = math.sqrt(2.0), k_min: int = 1,
+                         kc_block_pad: int = 0, threads: int | None = None) -> Workload:
+    """The indexer's compressor: one boundary token per request at position 4k-1, k ~
+    U{k_min..k_max}, an 8-row overlapping window as for C4, head 128 (state rows [S, state_bs,
+    512]: kv 2 x 128 | score 2 x 128).  Windows get state blocks of their own; kv slots are a
+    seeded injection into ``kv_blocks * kv_bs`` slots of a [B, kv_bs, 132] indexer cache."""
+    T = num_tokens
+    if T > kv_blocks * kv_bs:
+        raise ValueError("not enough kv slots")
+    k = randint(T, k_min, k_max, seed, 60)
+    positions = (C4_RATIO * k - 1).astype(np.int64)
+    if int(positions.max(initial=0)) // state_bs >= table_cols:
+        raise ValueError("block table too narrow for k_max")
+    per_tok = -(-C4_ROWS // state_bs) + 1
+    if T * per_tok > n_blocks:
+        raise ValueError("pool too small for disjoint windows")
+    perm = permutation(n_blocks, seed, 61)
+    bt = (bits(T * table_cols, seed, 62) % np.uint64(n_blocks)).astype(np.int32).reshape(
+        T, table_cols)
+    for r in range(T):
+        lo = max(0, int(positions[r]) - (C4_ROWS - 1)) // state_bs
+        hi = int(positions[r]) // state_bs
+        bt[r, lo:hi + 1] = perm[r * per_tok:r * per_tok + (hi - lo + 1)]
+    last_blk = bt[np.arange(T), positions // state_bs].astype(np.int64)
+    slot_mapping = (last_blk * state_bs + positions % state_bs).astype(np.int32)
+    kv_slots = permutation(kv_blocks * kv_bs, seed, 63)[:T].astype(np.int32)
+    state_base, state = alloc_state(n_blocks, row_width=INDEXER_ROW, rows_per_block=state_bs)
+    fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * INDEXER_HEAD)
+    kc_base, kc = alloc_indexer_cache(kv_blocks, kv_bs, kc_block_pad)
+    w = (1.0 + 0.1 * normal(INDEXER_HEAD, seed, 3).astype(np.float64)).astype(np.float32)
+    wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),
+                  slot_mapping, w, 1e-6, rope_table(cs_rows), kc, kv_slots, seed, state_base,
+                  kc_base, compress_ratio=C4_RATIO, overlap=1, indexer=True)
+    wl.info = {"kind": "indexer decode", "tokens": T, "pool_blocks": n_blocks,
                "state_bs": state_bs}
     return wl
 

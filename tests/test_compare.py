@@ -77,3 +77,51 @@ def test_flags_compressed_error(case):
     g = orc.compressed.astype(np.float32).copy()
     g[3, 100] += np.float32(1e-3)
     assert not compare(wl, orc.k_cache_base.copy(), orc, gpu_compressed=g).ok()
+
+
+# ---------------------------------------------------------------- indexer cache
+
+@pytest.fixture(scope="module")
+def icase():
+    wl = synth.indexer_decode_batch("icmp", 8, 12, 60, 8, 8, kv_bs=4, kv_blocks=8, cs_rows=64)
+    return wl, oracle.run(wl, 2)
+
+
+def iplanted(wl, orc, fn):
+    from oracle.compare import indexer_offsets
+    body = orc.k_cache_base.copy()
+    rec, scl = indexer_offsets(int(wl.kv_slot_mapping[5]), wl.k_cache.shape[1],
+                               wl.k_cache.strides[0])
+    fn(body, rec, scl)
+    return compare(wl, body, orc)
+
+
+def test_indexer_identical_output_passes(icase):
+    wl, orc = icase
+    rep = compare(wl, orc.k_cache_base.copy(), orc,
+                  gpu_compressed=orc.compressed.astype(np.float32))
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 12
+
+
+def test_indexer_flags_code_scale_and_stray_bytes(icase):
+    wl, orc = icase
+
+    def code(b, rec, scl):
+        c = int(b[rec + 3])
+        b[rec + 3] = (c & 0x80) | ((c & 0x7F) - 2 if (c & 0x7F) >= 2 else (c & 0x7F) + 2)
+
+    def scale(b, rec, scl):
+        b[scl:scl + 4] = np.frombuffer(np.float32(b[scl:scl + 4].view("<f4")[0] * 2).tobytes(),
+                                       np.uint8)
+
+    assert not iplanted(wl, orc, code).ok()
+    assert not iplanted(wl, orc, scale).ok()
+    # a byte of a kv slot that no token writes
+    from oracle.compare import indexer_offsets
+    free = sorted(set(range(32)) - set(int(x) for x in wl.kv_slot_mapping))[0]
+    rec, _ = indexer_offsets(free, wl.k_cache.shape[1], wl.k_cache.strides[0])
+    body = orc.k_cache_base.copy()
+    body[rec] ^= 0xFF
+    rep = compare(wl, body, orc)
+    assert not rep.ok() and rep["untouched_mismatch"] == 1
