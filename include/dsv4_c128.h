@@ -1,6 +1,7 @@
 /*
  * dsv4_c128.h -- C ABI of the DeepSeek-V4 sparse-attention compress-store path on
- * MI355X (gfx950): the C128 compressor (below) and the C4 compressor (dsv4_c4_*).
+ * MI355X (gfx950): the C128 compressor (below), the C4 compressor (dsv4_c4_*) and the
+ * indexer's FP8 compressor (dsv4_indexer_*).
  *
  * What it computes (vLLM API page "fused_compress_quant_cache", DeepSeek-V4
  * common ops: the sparse-attention fused kernel
@@ -74,7 +75,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 4
+#define DSV4_ABI_VERSION 5
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -239,6 +240,54 @@ int dsv4_c4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_ta
                      const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
                      const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
                      const dsv4_tensor* kv_slot_mapping);
+
+/*
+ * The indexer's FP8 compressor (vLLM fused_compress_quant_cache page, kernel
+ * `_fused_kv_compress_norm_rope_insert_indexer_attn`), on the overlapping window of compress
+ * ratio 4.  For every token t whose state slot is >= 0 and (pos+1) % 4 == 0:
+ *   1. window rows q = pos-7 .. pos as for dsv4_c4_compress_store (rows with q < 0 left out),
+ *      with head 128: a state row is kv[0:256] | score[256:512]; window row i < 4 contributes
+ *      kv[j] and score[256 + j], row i >= 4 kv[128 + j] and score[384 + j], j < 128;
+ *   2. compressed[j] = sum_i softmax_i(score) * kv, j < 128; RMSNorm over 128 with rms_w[128];
+ *   3. RoPE first: dims 64..127 as interleaved pairs (64+2m, 65+2m), m < 32, rotated by
+ *      cos_sin[(pos / 4) * 4][m] and [32 + m]; dims 0..63 unchanged;
+ *   4. then one quantisation block over all 128 dims: bf16 round trip, absmax (floor 1e-4),
+ *      e = ceil(log2(absmax / 448)), codes = E4M3FN(x * 2^-e), scale = 2^e as fp32;
+ *   5. if kv_slot_mapping[t] >= 0: with bs = k_cache.shape[1], blk = slot / bs, off = slot %
+ *      bs, the 128 codes at byte blk*k_cache.stride[0] + off*128 and the fp32 scale
+ *      (little-endian) at blk*k_cache.stride[0] + bs*128 + off*4.
+ *
+ *   state_cache     f32 [S, bs, 512]   bs >= 1, strides and alignment as for C4 (stride[1] >= 512)
+ *   rms_w           f32 [128]          contiguous, 16-byte aligned
+ *   k_cache         u8  [B, bs, 132]   stride[2] == 1, stride[1] == 132, stride[0] >= bs*132
+ *                                      and a multiple of 4; data 4-byte aligned
+ *   every other argument as for dsv4_c4_compress_store; compressed_out of the debug entry
+ *   point is [T, 128] fp32.
+ */
+int dsv4_indexer_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping, void* stream);
+
+/* dsv4_indexer_compress_store that also writes the fp32 pooled vectors ([T, 128], 16-byte
+ * aligned; rows of tokens that do not pass the gate are left unchanged; may be NULL). */
+int dsv4_indexer_compress_store_debug(const dsv4_tensor* state_cache,
+                                      const dsv4_tensor* block_table,
+                                      const dsv4_tensor* token_to_req,
+                                      const dsv4_tensor* positions,
+                                      const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                      float eps, const dsv4_tensor* cos_sin,
+                                      const dsv4_tensor* k_cache,
+                                      const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                      void* stream);
+
+/* Host-only validation of indexer descriptors (as dsv4_c128_validate). */
+int dsv4_indexer_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                          const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                          const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                          const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                          const dsv4_tensor* kv_slot_mapping);
 
 /*
  * Host-only validation of the descriptors, exactly as the compute entry

@@ -101,6 +101,13 @@ def library():
         lib.dsv4_c4_compress_store.restype = ctypes.c_int
         lib.dsv4_c4_compress_store_debug.argtypes = args10 + [ctypes.c_void_p, ctypes.c_void_p]
         lib.dsv4_c4_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_indexer_compress_store.argtypes = args10 + [ctypes.c_void_p]
+        lib.dsv4_indexer_compress_store.restype = ctypes.c_int
+        lib.dsv4_indexer_compress_store_debug.argtypes = args10 + [ctypes.c_void_p,
+                                                                  ctypes.c_void_p]
+        lib.dsv4_indexer_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_indexer_validate.argtypes = args10
+        lib.dsv4_indexer_validate.restype = ctypes.c_int
         lib.dsv4_c4_validate.argtypes = args10
         lib.dsv4_c4_validate.restype = ctypes.c_int
         lib.dsv4_c128_validate.argtypes = args10
@@ -272,6 +279,35 @@ def c4_validate(state_cache, block_table, token_to_req, positions, slot_mapping,
     return library().dsv4_c4_validate(*refs[:6], float(eps), *refs[6:])
 
 
+def indexer_compress_store(state_cache, block_table, token_to_req, positions, slot_mapping,
+                           rms_w, eps, cos_sin, k_cache, kv_slot_mapping, compressed_out=None,
+                           stream: int | None = None) -> None:
+    """The indexer's FP8 compressor (head 128, ratio 4 with the overlapping window; state rows
+    kv 2x128 | score 2x128, any state block size; k_cache u8 [B, bs, 132]).
+    ``compressed_out``: optional contiguous float32 [T, 128] device tensor."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    dev = _require_cuda(ts + ([compressed_out] if compressed_out is not None else []))
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 128)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 128] tensor")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_indexer_compress_store_debug(*refs[:6], float(eps), *refs[6:],
+                                                       out_ptr, s))
+
+
+def indexer_validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                     cos_sin, k_cache, kv_slot_mapping) -> int:
+    """Host-only validation of indexer descriptors; returns the status code."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping)
+    _, refs = _descriptors(ts)
+    return library().dsv4_indexer_validate(*refs[:6], float(eps), *refs[6:])
+
+
 def validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
              cos_sin, k_cache, kv_slot_mapping) -> int:
     """Host-only validation of the descriptors (no HIP call); returns the status code."""
@@ -295,5 +331,6 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
 
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
            "compress_store_varlen", "varlen_workspace_bytes", "c4_compress_store", "c4_validate",
+           "indexer_compress_store", "indexer_validate",
            "validate", "e4m3_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

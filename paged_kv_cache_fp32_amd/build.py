@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsv4_c128.so")
 SOURCES = [os.path.join(CSRC, "c128_kernel.hip"), os.path.join(CSRC, "c128_schedules.hip"),
-           os.path.join(CSRC, "c4_kernel.hip"), os.path.join(CSRC, "c128_abi.cpp")]
+           os.path.join(CSRC, "c4_kernel.hip"), os.path.join(CSRC, "indexer_kernel.hip"),
+           os.path.join(CSRC, "c128_abi.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

@@ -1,4 +1,4 @@
-// C ABI of the compress-store library (C128 and C4): descriptor validation
+// C ABI of the compress-store library (C128, C4, indexer FP8): descriptor validation
 // (host only), launch, error codes and the per-thread error message.  The
 // contract is documented in include/dsv4_c128.h.
 //
@@ -64,19 +64,26 @@ int check_token_array(const dsv4_tensor* t, const char* name, int64_t T) {
   return DSV4_OK;
 }
 
-// State-cache layout a compressor expects: row width in floats, rows per block (0 = any
-// positive count) and the fewest block-table columns a window can need.
+// Layout a compressor expects: state row width in floats, rows per block (0 = any positive
+// count), the fewest block-table columns a window can need, the head size (rms_w length), the
+// cache's bytes per token (last k_cache dimension) and the alignment its stores need.
 struct StateLayout {
   const char* path;
   int64_t row_floats;
   int64_t block_rows;
   int64_t min_bt_cols;
+  int64_t head;
+  int64_t slot_bytes;
+  int64_t kc_align;
 };
-// C128: kv 512 | score 512, blocks of 8 rows, 16 blocks per window.
+// C128: kv 512 | score 512, blocks of 8 rows, 16 blocks per window; 576 + 8 cache bytes.
 constexpr StateLayout kC128Layout{"C128", dsv4::kRowFloats, dsv4::kStateBlock,
-                                  dsv4::kWindowBlocks};
+                                  dsv4::kWindowBlocks, dsv4::kHead, dsv4::kSlotBytes, 8};
 // C4 with its overlapping window: kv 2 x 512 | score 2 x 512; any block size.
-constexpr StateLayout kC4Layout{"C4", 4 * dsv4::kHead, 0, 1};
+constexpr StateLayout kC4Layout{"C4", 4 * dsv4::kHead, 0, 1, dsv4::kHead, dsv4::kSlotBytes, 8};
+// Indexer (head 128, overlapping window of ratio 4): kv 2 x 128 | score 2 x 128; 128 fp8
+// bytes + one fp32 scale per token.
+constexpr StateLayout kIndexerLayout{"indexer", 4 * 128, 0, 1, 128, 128 + 4, 4};
 
 int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_tensor* t2r,
                  const dsv4_tensor* pos, const dsv4_tensor* slot, const dsv4_tensor* w, float eps,
@@ -125,9 +132,9 @@ int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_ten
 
   // rms weight f32 [512]
   if ((rc = check_tensor(w, "rms_w", DSV4_F32, 1))) return rc;
-  if (w->shape[0] != kHead)
-    return fail(DSV4_ERR_SHAPE, "rms_w: %lld entries, head size is 512",
-                static_cast<long long>(w->shape[0]));
+  if (w->shape[0] != L.head)
+    return fail(DSV4_ERR_SHAPE, "rms_w: %lld entries, the %s head size is %lld",
+                static_cast<long long>(w->shape[0]), L.path, static_cast<long long>(L.head));
   if (w->stride[0] != 1) return fail(DSV4_ERR_STRIDE, "rms_w: must be contiguous");
   if (!aligned16(w->data)) return fail(DSV4_ERR_ALIGN, "rms_w: data must be 16-byte aligned");
   if (!(eps >= 0.0f) || eps != eps)
@@ -142,22 +149,25 @@ int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_ten
   if (cs->shape[0] > 1 && cs->stride[0] < cs->shape[1])
     return fail(DSV4_ERR_STRIDE, "cos_sin: stride[0] < shape[1] (rows overlap)");
 
-  // k_cache u8 [B, bs, 584]
+  // k_cache u8 [B, bs, slot bytes]: 584 (576 data + 8 scale) or, for the indexer, 132
   if ((rc = check_tensor(kc, "k_cache", DSV4_U8, 3))) return rc;
-  if (kc->shape[2] != kSlotBytes)
-    return fail(DSV4_ERR_SHAPE, "k_cache: last dimension %lld, the sparse-attention layout "
-                "needs 584 bytes per token (576 data + 8 scale)",
-                static_cast<long long>(kc->shape[2]));
+  if (kc->shape[2] != L.slot_bytes)
+    return fail(DSV4_ERR_SHAPE, "k_cache: last dimension %lld, the %s cache layout needs %lld "
+                "bytes per token", static_cast<long long>(kc->shape[2]), L.path,
+                static_cast<long long>(L.slot_bytes));
   if (kc->shape[1] < 1) return fail(DSV4_ERR_SHAPE, "k_cache: block size must be >= 1");
-  if (kc->stride[2] != 1 || kc->stride[1] != kSlotBytes)
-    return fail(DSV4_ERR_STRIDE, "k_cache: stride[2] must be 1 and stride[1] 584");
-  if (kc->stride[0] < kc->shape[1] * kSlotBytes)
-    return fail(DSV4_ERR_STRIDE, "k_cache: stride[0] = %lld < bs*584 = %lld",
-                static_cast<long long>(kc->stride[0]),
-                static_cast<long long>(kc->shape[1] * kSlotBytes));
-  // records are stored with 4- and 8-byte vector stores; every bs*584 is a multiple of 8
-  if ((reinterpret_cast<uintptr_t>(kc->data) & 7u) || (kc->stride[0] & 7))
-    return fail(DSV4_ERR_ALIGN, "k_cache: data and stride[0] must be 8-byte aligned");
+  if (kc->stride[2] != 1 || kc->stride[1] != L.slot_bytes)
+    return fail(DSV4_ERR_STRIDE, "k_cache: stride[2] must be 1 and stride[1] %lld",
+                static_cast<long long>(L.slot_bytes));
+  if (kc->stride[0] < kc->shape[1] * L.slot_bytes)
+    return fail(DSV4_ERR_STRIDE, "k_cache: stride[0] = %lld < bs*%lld = %lld",
+                static_cast<long long>(kc->stride[0]), static_cast<long long>(L.slot_bytes),
+                static_cast<long long>(kc->shape[1] * L.slot_bytes));
+  // records are stored with 4- or 8-byte stores (bs*584 is a multiple of 8, bs*132 of 4)
+  if ((reinterpret_cast<uintptr_t>(kc->data) & (L.kc_align - 1)) ||
+      (kc->stride[0] & (L.kc_align - 1)))
+    return fail(DSV4_ERR_ALIGN, "k_cache: data and stride[0] must be %lld-byte aligned",
+                static_cast<long long>(L.kc_align));
 
   if (out) {
     out->state = static_cast<const float*>(state->data);
@@ -357,6 +367,49 @@ int dsv4_c4_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* bl
   return dsv4_c4_compress_store_debug(state_cache, block_table, token_to_req, positions,
                                       slot_mapping, rms_w, eps, cos_sin, k_cache,
                                       kv_slot_mapping, nullptr, stream);
+}
+
+int dsv4_indexer_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                          const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                          const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+                          const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                          const dsv4_tensor* kv_slot_mapping) {
+  return validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                      cos_sin, k_cache, kv_slot_mapping, nullptr, kIndexerLayout);
+}
+
+int dsv4_indexer_compress_store_debug(const dsv4_tensor* state_cache,
+                                      const dsv4_tensor* block_table,
+                                      const dsv4_tensor* token_to_req,
+                                      const dsv4_tensor* positions,
+                                      const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                      float eps, const dsv4_tensor* cos_sin,
+                                      const dsv4_tensor* k_cache,
+                                      const dsv4_tensor* kv_slot_mapping, float* compressed_out,
+                                      void* stream) {
+  dsv4::C128Params p;
+  int32_t sbs = 0;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p, kIndexerLayout, &sbs);
+  if (rc) return rc;
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  p.compressed_out = compressed_out;
+  hipError_t err = dsv4::launch_indexer_compress_store(p, sbs, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
+int dsv4_indexer_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping, void* stream) {
+  return dsv4_indexer_compress_store_debug(state_cache, block_table, token_to_req, positions,
+                                           slot_mapping, rms_w, eps, cos_sin, k_cache,
+                                           kv_slot_mapping, nullptr, stream);
 }
 
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -26,6 +26,9 @@ size_t compacted_workspace_bytes(int64_t num_tokens);
 // C4 compressor (ratio 4, overlapping 8-row window), one wave per token: c4_kernel.hip.
 // state_bs is the state cache's rows per block.
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream);
+// Indexer FP8 compressor (head 128, ratio 4, overlapping window): indexer_kernel.hip.
+hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,
+                                         hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace dsv4

@@ -55,12 +55,15 @@ class DeviceWorkload:
         """One call; splits None = the plain entry points, else compress_store_ex with that
         split count (0 = automatic) and a workspace of the size it needs; varlen = the
         compacted schedule (compress_store_varlen).  A C4 workload (compress ratio 4) always
-        goes to c4_compress_store."""
+        goes to c4_compress_store, an indexer workload to indexer_compress_store."""
         comp = None
+        indexer = getattr(self.wl, "indexer", False)
         if debug:
-            comp = torch.full((self.wl.num_tokens, 512), float("nan"), dtype=torch.float32,
-                              device=self.state.device)
-        if getattr(self.wl, "compress_ratio", 128) == 4:
+            comp = torch.full((self.wl.num_tokens, 128 if indexer else 512), float("nan"),
+                              dtype=torch.float32, device=self.state.device)
+        if indexer:
+            c128.indexer_compress_store(*self.args(), compressed_out=comp)
+        elif getattr(self.wl, "compress_ratio", 128) == 4:
             c128.c4_compress_store(*self.args(), compressed_out=comp)
         elif varlen:
             ws = torch.empty(max(c128.varlen_workspace_bytes(self.wl.num_tokens), 16),

@@ -323,3 +323,48 @@ def test_c4_layout_errors():
     a = c4_args()
     a["block_table"] = torch.zeros(4, 1, dtype=torch.int32)
     assert c4_validate(a) == 0
+
+
+def idx_args(T=4, S=16, sbs=8, bs=4):
+    a = c4_args(T=T, S=S, sbs=sbs, bs=bs)
+    a["state_cache"] = torch.zeros(S, sbs, 512, dtype=torch.float32)
+    a["rms_w"] = torch.ones(128, dtype=torch.float32)
+    a["k_cache"] = torch.zeros(2, bs, 132, dtype=torch.uint8)
+    return a
+
+
+def idx_validate(a):
+    return c128.indexer_validate(a["state_cache"], a["block_table"], a["token_to_req"],
+                                 a["positions"], a["slot_mapping"], a["rms_w"], a["eps"],
+                                 a["cos_sin"], a["k_cache"], a["kv_slot_mapping"])
+
+
+@pytest.mark.parametrize("sbs", [1, 4, 8, 64])
+def test_indexer_accepts_layout(sbs):
+    assert idx_validate(idx_args(sbs=sbs)) == 0, c128.last_error()
+
+
+def test_indexer_layout_errors():
+    """State row 512 floats, rms_w 128, k_cache [B, bs, 132] with 4-byte alignment; the sparse
+    layouts are rejected and the indexer layout is rejected by the C4 entry point."""
+    a = idx_args()
+    a["state_cache"] = torch.zeros(16, 8, 2048)
+    assert idx_validate(a) == -4
+    a = idx_args()
+    a["rms_w"] = torch.ones(512)
+    assert idx_validate(a) == -4 and "128" in c128.last_error()
+    a = idx_args()
+    a["k_cache"] = torch.zeros(2, 4, 584, dtype=torch.uint8)
+    assert idx_validate(a) == -4 and "132" in c128.last_error()
+    a = idx_args()
+    a["k_cache"] = torch.zeros(2 * 4 * 132 + 2, dtype=torch.uint8)[2:].view(2, 4, 132)
+    assert idx_validate(a) == -6
+    a = idx_args()
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * 530, dtype=torch.uint8), (2, 4, 132),
+                                    (530, 132, 1))
+    assert idx_validate(a) == -6
+    a = idx_args()
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * 532, dtype=torch.uint8), (2, 4, 132),
+                                    (532, 132, 1))
+    assert idx_validate(a) == 0
+    assert c4_validate(idx_args()) == -4

@@ -1,0 +1,89 @@
+"""GPU parity of the indexer's FP8 compressor kernel (dsv4_indexer_compress_store) against the
+CPU oracle: decode batches over several state and cache block sizes (including windows at
+position 3), gate decisions and out-of-range device indices, and the 16384-token batch the
+bench times."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.compare import compare
+from synth.device import run_gpu
+
+pytestmark = pytest.mark.gpu
+
+THREADS = synth.default_threads()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check(wl, label, debug=True):
+    announce(label)
+    body, comp, guards_ok = run_gpu(wl, debug=debug)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    return rep, body, comp
+
+
+def idx_batch(T, seed, state_bs=8, k_max=16, kv_bs=16, score_std=2 ** 0.5, kc_block_pad=0):
+    return synth.indexer_decode_batch(f"indexer T={T} bs={state_bs}", seed, T,
+                                      T * (-(-8 // state_bs) + 1) + 8, k_max,
+                                      -(-4 * k_max // state_bs) + 1, kv_bs=kv_bs,
+                                      kv_blocks=-(-2 * T // kv_bs), cs_rows=4 * k_max + 4,
+                                      state_bs=state_bs, score_std=score_std,
+                                      kc_block_pad=kc_block_pad)
+
+
+@pytest.mark.parametrize("state_bs", [8, 4, 1])
+@pytest.mark.parametrize("T", [1, 5, 300, 2500])
+def test_indexer_decode_parity(T, state_bs):
+    wl = idx_batch(T, 500 + T + state_bs, state_bs=state_bs, k_max=3 if T == 1 else 40)
+    rep, *_ = check(wl, f"indexer decode T={T} state bs={state_bs}")
+    assert rep["written"] == T
+
+
+@pytest.mark.parametrize("kv_bs,pad", [(1, 0), (3, 4), (64, 8)])
+def test_indexer_cache_block_sizes(kv_bs, pad):
+    wl = idx_batch(40, 71, kv_bs=kv_bs, kc_block_pad=pad)
+    check(wl, f"indexer cache bs={kv_bs} pad={pad}")
+
+
+def test_indexer_first_windows_and_peaky_scores():
+    wl = idx_batch(64, 73, k_max=2, score_std=4.0)
+    assert set(wl.positions.tolist()) == {3, 7}
+    check(wl, "indexer positions 3 and 7, score std 4")
+
+
+def test_indexer_gate_and_bad_indices():
+    wl = idx_batch(8, 79, k_max=8)
+    wl.positions[:] = np.array([2, 4, 7, 6, 11, 15, 19, 23], np.int32)
+    wl.slot_mapping[:] = np.array([1, 1, 1, 1, -1, 1, 1, 1], np.int32)
+    wl.kv_slot_mapping[5] = -1
+    wl.token_to_req[6] = wl.block_table.shape[0]
+    wl.kv_slot_mapping[7] = wl.k_cache.shape[0] * wl.k_cache.shape[1]
+    announce("indexer gate / bad indices")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [0, 0, 1, 0, 0, 2, -1, -1]
+    wl.kv_slot_mapping[[6, 7]] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 1
+    assert np.isnan(comp[[0, 1, 3, 4, 6]]).all() and np.isfinite(comp[[2, 5, 7]]).all()
+
+
+def test_indexer_large_batch():
+    wl = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024, 512,
+                                    kv_bs=64, kv_blocks=256, cs_rows=4096)
+    rep, *_ = check(wl, "indexer decode T=16384", debug=False)
+    assert rep["written"] == 16384
