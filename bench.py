@@ -54,8 +54,21 @@ C4_ROW_BYTES = 2 * 512 * 4
 C4_TOKEN_BYTES = 8 + 256 + 584
 
 
+# indexer (head 128, same window): 1 KiB per existing row (kv half 512 B + score half 512 B),
+# the 128-byte record and its 4-byte scale
+IDX_ROW_BYTES = 2 * 128 * 4
+IDX_TOKEN_BYTES = 8 + 256 + 132
+
+
 def algorithmic_bytes(wl) -> int:
     act = wl.active_mask()
+    if getattr(wl, "indexer", False):
+        pos = wl.positions[act].astype(np.int64)
+        bs = wl.state.shape[1]
+        first = np.maximum(pos - 7, 0)
+        per = (pos - first + 1) * IDX_ROW_BYTES + (pos // bs - first // bs + 1) * 4 + \
+            IDX_TOKEN_BYTES
+        return int(per.sum()) + wl.num_tokens * ANY_TOKEN_BYTES + 128 * 4
     if getattr(wl, "compress_ratio", 128) == 4:
         pos = wl.positions[act].astype(np.int64)
         bs = wl.state.shape[1]
@@ -267,7 +280,10 @@ def sweep(args, path):
         """splits None: the single-pass entry point; else compress_store_ex with that split
         count (0 = automatic) and a workspace per window set; varlen: the compacted schedule
         (compress_store_varlen) with a workspace per window set."""
-        if getattr(dws[0].wl, "compress_ratio", 128) == 4:
+        if getattr(dws[0].wl, "indexer", False):
+            calls = [(lambda d=d: c128.indexer_compress_store(*d.args(), stream=sid))
+                     for d in dws]
+        elif getattr(dws[0].wl, "compress_ratio", 128) == 4:
             calls = [(lambda d=d: c128.c4_compress_store(*d.args(), stream=sid)) for d in dws]
         elif varlen:
             wss = [torch.empty(max(16, c128.varlen_workspace_bytes(d.wl.num_tokens)),
@@ -290,7 +306,8 @@ def sweep(args, path):
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
         rec = {"workload": name, "tokens": wl.num_tokens,
                "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
-               "entry": ("c4" if getattr(wl, "compress_ratio", 128) == 4 else
+               "entry": ("indexer" if getattr(wl, "indexer", False) else
+                         "c4" if getattr(wl, "compress_ratio", 128) == 4 else
                          "varlen (compacted)" if varlen else
                          "single pass" if splits is None else f"fan-out splits={splits}"),
                "algorithmic_bytes_per_call": nbytes,
@@ -352,6 +369,7 @@ def sweep(args, path):
     del pool, pool_dev
     torch.cuda.empty_cache()
     c4_sweep(want, measure, dev)
+    indexer_sweep(want, measure, dev)
     out.close()
 
 
@@ -367,6 +385,29 @@ def c4_slices(wl, T, n_sets):
             positions=wl.positions[sl], slot_mapping=wl.slot_mapping[sl],
             kv_slot_mapping=wl.kv_slot_mapping[sl]))
     return out
+
+
+def indexer_sweep(want, measure, dev):
+    """Indexer compressor: decode batches cut from one 16384-token batch (512 MiB pool)."""
+    import synth
+    from synth.device import DeviceWorkload
+    sizes = (1, 128, 1024, 4096, 16384)
+    names = [f"indexer decode T={T}" for T in sizes]
+    if not any(want(n) for n in names):
+        return
+    big = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024, 512,
+                                     kv_bs=64, kv_blocks=256, cs_rows=4096)
+    pool_dev = None
+    for T, name in zip(sizes, names):
+        if not want(name):
+            continue
+        dws = []
+        for wl in c4_slices(big, T, min(64, 16384 // T)):
+            d = DeviceWorkload(wl, device=dev, state=pool_dev)
+            pool_dev = (d.state_buf, d.state)
+            dws.append(d)
+        measure(name, dws, 1000 if T <= 4096 else 400)
+        del dws
 
 
 def c4_sweep(want, measure, dev):
