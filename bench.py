@@ -255,6 +255,21 @@ def cpu_baseline(wl, gpu_body, nbytes):
     }
 
 
+def oracle_timing(wl, nbytes):
+    """CPU baseline of a sweep workload: the oracle (no diagnostics) on the host cores, on the
+    same host inputs as the GPU run."""
+    import oracle
+    import synth
+
+    threads = synth.default_threads()
+    t0 = time.perf_counter()
+    oracle.run(wl, threads, diagnostics=False)
+    dt = time.perf_counter() - t0
+    return {"kind": "oracle", "cores": threads, "seconds": round(dt, 4),
+            "value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+            "sample": f"the whole workload ({wl.num_tokens} tokens), fp64"}
+
+
 def sweep(args, path):
     """Per-workload timings (warm: back-to-back calls rotating over disjoint window sets;
     cold: a 1 GiB buffer is read (a sum) before each individually timed call, which evicts the
@@ -275,6 +290,7 @@ def sweep(args, path):
         torch.sum(scratch, dim=0, out=sink)
 
     out = open(path, "w")
+    cpu_seen = {}  # workload name -> its oracle timing (taken once per workload)
 
     def measure(name, dws, steps, warm_only=False, splits=None, varlen=False):
         """splits None: the single-pass entry point; else compress_store_ex with that split
@@ -319,6 +335,10 @@ def sweep(args, path):
             rec["cold_us_median"] = round(float(np.median(percold)) * 1e3, 2)
             rec["cold_gbs"] = round(nbytes / (rec["cold_us_median"] * 1e-6) / 1e9, 1)
         rec["pct_peak_hbm_warm"] = round(100 * rec["warm_gbs"] / PEAK_GBS, 2)
+        if not args.no_cpu_baseline:
+            if name not in cpu_seen:
+                cpu_seen[name] = oracle_timing(wl, nbytes)
+            rec["cpu_baseline"] = cpu_seen[name]
         out.write(json.dumps(rec) + "\n")
         out.flush()
         log(f"[sweep] {json.dumps(rec)}")

@@ -113,3 +113,50 @@ def test_c4_large_batch():
                                kv_bs=64, kv_blocks=256, cs_rows=4096)
     rep, *_ = check(wl, "c4 decode T=16384", debug=False)
     assert rep["written"] == 16384
+
+
+def test_c4_empty_batch_and_zero_window():
+    """T = 0 is a no-op; an all-zero window gives zero codes, scale bytes 105 (e = -22 from the
+    1e-4 floor) and a zero pad byte."""
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    from synth.device import DeviceWorkload
+    announce("c4 T = 0")
+    d = DeviceWorkload(c4_batch(1, 83))
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    before = d.kc_buf.clone()
+    c128.c4_compress_store(d.state, d.block_table, e, e, e, d.rms_w, 1e-6, d.cos_sin, d.k_cache,
+                           e)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d.kc_buf)
+    wl = c4_batch(4, 89)
+    wl.state[:, :, :1024] = 0.0
+    rep, body, comp = check(wl, "c4 all-zero windows")
+    assert np.all(comp == 0.0)
+    kc = wl.k_cache
+    for t in range(4):
+        s = int(wl.kv_slot_mapping[t])
+        blk, off = s // kc.shape[1], s % kc.shape[1]
+        base = blk * kc.strides[0]
+        assert np.all(body[base + off * 576: base + off * 576 + 448] & 0x7F == 0)
+        scl = body[base + kc.shape[1] * 576 + off * 8: base + kc.shape[1] * 576 + off * 8 + 8]
+        assert list(scl) == [105] * 7 + [0]
+
+
+def test_c4_side_stream():
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    from synth.device import DeviceWorkload
+    wl = c4_batch(16, 97)
+    announce("c4 side stream")
+    d = DeviceWorkload(wl)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c128.c4_compress_store(*d.args())
+    s.synchronize()
+    body, ok = d.k_cache_bytes()
+    rep = compare(wl, body, oracle.run(wl, 2))
+    assert ok and rep.ok(), rep.summary()

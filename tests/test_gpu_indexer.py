@@ -87,3 +87,32 @@ def test_indexer_large_batch():
                                     kv_bs=64, kv_blocks=256, cs_rows=4096)
     rep, *_ = check(wl, "indexer decode T=16384", debug=False)
     assert rep["written"] == 16384
+
+
+def test_indexer_empty_batch_and_zero_window():
+    """T = 0 is a no-op; an all-zero window gives zero codes and the scale 2^-22 (the 1e-4
+    floor: ceil(log2(1e-4 / 448)) = -22)."""
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    from synth.device import DeviceWorkload
+    announce("indexer T = 0")
+    d = DeviceWorkload(idx_batch(1, 101))
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    before = d.kc_buf.clone()
+    c128.indexer_compress_store(d.state, d.block_table, e, e, e, d.rms_w, 1e-6, d.cos_sin,
+                                d.k_cache, e)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d.kc_buf)
+    wl = idx_batch(4, 103)
+    wl.state[:, :, :256] = 0.0
+    rep, body, comp = check(wl, "indexer all-zero windows")
+    assert np.all(comp == 0.0)
+    kc = wl.k_cache
+    for t in range(4):
+        s = int(wl.kv_slot_mapping[t])
+        blk, off = s // kc.shape[1], s % kc.shape[1]
+        base = blk * kc.strides[0]
+        assert np.all(body[base + off * 128: base + off * 128 + 128] & 0x7F == 0)
+        sc = body[base + kc.shape[1] * 128 + off * 4: base + kc.shape[1] * 128 + off * 4 + 4]
+        assert float(sc.view("<f4")[0]) == 2.0 ** -22
