@@ -353,7 +353,8 @@ C4_ROW = 4 * HEAD            # kv (2 x 512) | score (2 x 512)
 
 def c4_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
                     table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int, state_bs: int = 8,
-                    score_std: float = math.sqrt(2.0), k_min: int = 1,
+                    score_std: float = math.sqrt(2.0), k_min: int = 1, row_pad: int = 0,
+                    block_pad: int = 0, kc_block_pad: int = 0,
                     threads: int | None = None) -> Workload:
     """C4 compressor: one boundary token per request at position 4k-1, k ~ U{k_min..k_max}.
 
@@ -382,9 +383,10 @@ def c4_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max:
     last_blk = bt[np.arange(T), positions // state_bs].astype(np.int64)
     slot_mapping = (last_blk * state_bs + positions % state_bs).astype(np.int32)
     kv_slots = permutation(kv_blocks * kv_bs, seed, 43)[:T].astype(np.int32)
-    state_base, state = alloc_state(n_blocks, row_width=C4_ROW, rows_per_block=state_bs)
+    state_base, state = alloc_state(n_blocks, row_width=C4_ROW, rows_per_block=state_bs,
+                                    row_pad=row_pad, block_pad=block_pad)
     fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * HEAD)
-    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs)
+    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs, kc_block_pad)
     wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),
                   slot_mapping, _rms_weight(seed), 1e-6, rope_table(cs_rows), kc, kv_slots, seed,
                   state_base, kc_base, compress_ratio=C4_RATIO, overlap=1)
@@ -444,7 +446,8 @@ def alloc_indexer_cache(n_blocks: int, bs: int, block_pad: int = 0, fill: int = 
 def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
                          table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int,
                          state_bs: int = 8, score_std: float = math.sqrt(2.0), k_min: int = 1,
-                         kc_block_pad: int = 0, threads: int | None = None) -> Workload:
+                         kc_block_pad: int = 0, row_pad: int = 0, block_pad: int = 0,
+                         threads: int | None = None) -> Workload:
     """The indexer's compressor: one boundary token per request at position 4k-1, k ~
     U{k_min..k_max}, an 8-row overlapping window as for C4, head 128 (state rows [S, state_bs,
     512]: kv 2 x 128 | score 2 x 128).  Windows get state blocks of their own; kv slots are a
@@ -469,7 +472,8 @@ def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k
     last_blk = bt[np.arange(T), positions // state_bs].astype(np.int64)
     slot_mapping = (last_blk * state_bs + positions % state_bs).astype(np.int32)
     kv_slots = permutation(kv_blocks * kv_bs, seed, 63)[:T].astype(np.int32)
-    state_base, state = alloc_state(n_blocks, row_width=INDEXER_ROW, rows_per_block=state_bs)
+    state_base, state = alloc_state(n_blocks, row_width=INDEXER_ROW, rows_per_block=state_bs,
+                                    row_pad=row_pad, block_pad=block_pad)
     fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * INDEXER_HEAD)
     kc_base, kc = alloc_indexer_cache(kv_blocks, kv_bs, kc_block_pad)
     w = (1.0 + 0.1 * normal(INDEXER_HEAD, seed, 3).astype(np.float64)).astype(np.float32)

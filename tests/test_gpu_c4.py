@@ -160,3 +160,21 @@ def test_c4_side_stream():
     body, ok = d.k_cache_bytes()
     rep = compare(wl, body, oracle.run(wl, 2))
     assert ok and rep.ok(), rep.summary()
+
+
+def test_c4_padded_strides_and_largest_position():
+    """Padded state rows/blocks and k_cache blocks; a token at position 2^31 - 1 (a boundary of
+    ratio 4) is skipped without overflow."""
+    wl = synth.c4_decode_batch("c4 padded", 107, 24, 24 * 2 + 8, 16, 9, kv_bs=16, kv_blocks=3,
+                               cs_rows=68, row_pad=16, block_pad=32, kc_block_pad=24)
+    check(wl, "c4 padded strides")
+    wl.positions[5] = 2 ** 31 - 1
+    announce("c4 largest position")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert orc.status[5] == -1 and (np.delete(orc.status, 5) == 1).all()
+    wl.kv_slot_mapping[5] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[5]).all()

@@ -116,3 +116,20 @@ def test_indexer_empty_batch_and_zero_window():
         assert np.all(body[base + off * 128: base + off * 128 + 128] & 0x7F == 0)
         sc = body[base + kc.shape[1] * 128 + off * 4: base + kc.shape[1] * 128 + off * 4 + 4]
         assert float(sc.view("<f4")[0]) == 2.0 ** -22
+
+
+def test_indexer_padded_strides_and_largest_position():
+    wl = synth.indexer_decode_batch("indexer padded", 109, 24, 24 * 2 + 8, 16, 9, kv_bs=16,
+                                    kv_blocks=3, cs_rows=68, row_pad=16, block_pad=32,
+                                    kc_block_pad=12)
+    check(wl, "indexer padded strides")
+    wl.positions[5] = 2 ** 31 - 1
+    announce("indexer largest position")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert orc.status[5] == -1 and (np.delete(orc.status, 5) == 1).all()
+    wl.kv_slot_mapping[5] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[5]).all()

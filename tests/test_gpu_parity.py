@@ -394,3 +394,36 @@ def test_varlen_gate_and_bad_indices():
     rep = compare(wl, body, orc)
     assert rep.ok(), rep.summary()
     assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
+
+
+# ---------------------------------------------------------------- layouts and extremes on
+# every schedule
+
+@pytest.mark.parametrize("mode", ["fanout", "varlen"])
+def test_padded_strides_other_schedules(mode):
+    """Padded state rows and blocks and a padded k_cache block stride through the fan-out
+    (8 splits) and the compacted schedule."""
+    wl = small(T=12, seed=17, row_pad=32, block_pad=64, kc_block_pad=48)
+    label = f"padded strides ({mode})"
+    if mode == "fanout":
+        check_ex(wl, 8, label)
+    else:
+        check_varlen(wl, label)
+
+
+@pytest.mark.parametrize("mode", ["single", "fanout", "varlen"])
+def test_largest_position_is_skipped(mode):
+    """A boundary token at position 2^31 - 1 needs block-table column 2^28 - 1: no table is that
+    wide, so the token is skipped (nothing written, no overflow); the others are unaffected."""
+    wl = small(T=5, seed=19)
+    wl.positions[2] = 2 ** 31 - 1
+    announce(f"largest position ({mode})")
+    kw = {"splits": 4} if mode == "fanout" else ({"varlen": True} if mode == "varlen" else {})
+    body, comp, guards_ok = run_gpu(wl, debug=True, **kw)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [1, 1, -1, 1, 1]
+    wl.kv_slot_mapping[2] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[2]).all()
