@@ -11,11 +11,14 @@ insert into a KV-block-size-64 k_cache.  Inputs are resident in HBM before
 timing starts.
 
 Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
-``--sweep PATH`` also writes per-workload JSONL (decode sweep 1..4096 tokens,
-single-token, decode batch, varlen prefill) with warm and cold timings.
-``--mode copy`` times a plain device-to-device copy (the counter-calibration
-kernel for rocprofv3); ``--mode read`` times a plain streaming read (the
-attainable-bandwidth reference line).
+``--sweep PATH`` also writes per-workload JSONL with warm and cold timings and the
+oracle's time beside each workload: the C128 decode sweep 1..4096 tokens, the
+single-token, decode-batch and varlen-prefill workloads on every entry point
+(single pass, fan-out, compacted), and the C4 and indexer compressors
+(``--sweep-filter REGEX`` keeps matching workloads; ``--mode sweep`` skips the
+large-batch line).  ``--mode copy`` times a plain device-to-device copy (the
+counter-calibration kernel for rocprofv3); ``--mode read`` times plain streaming
+reads (the attainable-bandwidth reference lines).
 """
 
 from __future__ import annotations

@@ -1,13 +1,17 @@
-"""MI355X (gfx950) C128 compress-store for the DeepSeek-V4 sparse-attention compressor.
+"""MI355X (gfx950) compress-store for the DeepSeek-V4 compressors: C128 (single pass,
+small-batch fan-out, compacted varlen schedule), C4 and the indexer's FP8 compressor.
 
 Thin ctypes binding of ``libdsv4_c128.so`` (C ABI in ``include/dsv4_c128.h``).
 The binding only marshals torch tensors into descriptors and passes torch's
-current HIP stream; every step of the computation runs in the HIP kernel.
+current HIP stream; every step of the computation runs in the HIP kernels.
 Loading fails loudly when the library is missing -- there is no fallback.
 
     import paged_kv_cache_fp32_amd as c128
     c128.compress_store(state_cache, block_table, token_to_req, positions,
                         slot_mapping, rms_w, eps, cos_sin, k_cache, kv_slot_mapping)
+    c128.compress_store_varlen(...)       # long prefill batches
+    c128.c4_compress_store(...)           # ratio 4, overlapping window
+    c128.indexer_compress_store(...)      # head 128, fp8 + fp32 scale
 """
 
 from __future__ import annotations

@@ -201,8 +201,9 @@ __device__ __forceinline__ void finish_token(const C128Params& p, int32_t t, int
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fan-out for small batches: a token's 16 window blocks are split over S = RG*NBW... workgroups
-// (grid = T x S).  Workgroup (t, s) streams window blocks s*RG*NBW .. (s+1)*RG*NBW - 1 and
+// Fan-out for small batches: a token's 16 window blocks are split over S = 16 / (RG*NBW)
+// workgroups (grid = T x S).  Workgroup (t, s) streams window blocks s*RG*NBW ..
+// (s+1)*RG*NBW - 1 (NBW blocks for each of its RG row groups) and
 // writes its merged partial state to the workspace:
 //   ws[((t * S + s) * 3 + {0: m (log2 units), 1: l, 2: acc}) * 512 + column].
 // The finish kernel then merges the S partials of each token and runs the epilogue.

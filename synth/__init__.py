@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the C128 compress-store path.
+"""Seeded synthetic inputs for the compress-store paths (C128, C4, indexer).
 
 This module draws the inputs that both the CPU oracle and the HIP path
 consume; it holds none of the compressor's arithmetic.  Every random value
@@ -18,6 +18,10 @@ layout" of the sparse-attention kernel; vLLM PR 44230, "Summary"):
   bytes.
 * cos_sin: fp32 ``[P, 64]``, cos in columns [0, 32), sin in [32, 64),
   angle ``p * 10000**(-2i/64)`` (computed in fp64, rounded to fp32).
+* C4 state: fp32 ``[S, bs, 2048]`` (kv of the previous and current window's
+  projections, 2 x 512, then their scores); indexer state ``[S, bs, 512]``
+  (2 x 128 each) and indexer cache ``[B, bs, 132]`` (bs records of 128 fp8
+  bytes, then bs fp32 scales).
 """
 
 from __future__ import annotations
