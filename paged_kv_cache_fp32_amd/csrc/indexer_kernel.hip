@@ -16,7 +16,7 @@
 //  * One wave per token.  Lane l owns columns 2l, 2l+1 (8-byte vectors: each wave-wide load
 //    is a 512-byte contiguous segment of a row), so lanes 32..63 hold exactly the 32 RoPE
 //    pairs, and the RMSNorm sum and the quantisation absmax are single wave reductions.
-//  * A wave takes 1 to 8 consecutive tokens (enough waves for 2 per SIMD first); their gate,
+//  * A wave takes 1 to 8 consecutive tokens (enough waves for 8 per SIMD first); their gate,
 //    block ids and range checks are resolved up front, one lane per (token, window row).
 //  * Records go to the wave's LDS stage and reach the cache after the wave's last state read,
 //    so that the writes do not land in the middle of the HBM read stream.
@@ -39,7 +39,7 @@ constexpr int kIdxScale = 4;                // one fp32 scale per token
 constexpr int kIdxSlot = kIdxRecord + kIdxScale;
 constexpr int kIdxWavesPerGroup = 4;
 constexpr int kIdxMaxTokensPerWave = 8;     // 8 tokens x 8 window rows = the 64 lanes
-constexpr int kIdxTargetWaves = 2048;       // 2 waves per SIMD on 256 CUs
+constexpr int kIdxTargetWaves = 8192;       // 8 waves per SIMD on 256 CUs (57-59 VGPRs)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
