@@ -313,8 +313,7 @@ def sweep(args, path):
         elif splits is None:
             calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
         else:
-            wss = [torch.empty(max(16, c128.workspace_bytes(d.wl.num_tokens, splits)),
-                               dtype=torch.uint8, device=dev) for d in dws]
+            wss = [c128.fanout_workspace(d.wl.num_tokens, splits, dev) for d in dws]
             calls = [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w,
                                                               splits=splits, stream=sid))
                      for d, w in zip(dws, wss)]

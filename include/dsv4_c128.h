@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 5
+#define DSV4_ABI_VERSION 6
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -133,22 +133,29 @@ int dsv4_c128_compress_store_debug(const dsv4_tensor* state_cache,
 /*
  * Small-batch fan-out.  The same computation as dsv4_c128_compress_store, with each token's 16
  * window blocks split over `splits` workgroups (grid T x splits) that write partial softmax
- * states to `workspace`; a second, stream-ordered kernel merges them per token and runs the
- * epilogue.  It exists because one workgroup per token leaves most of the 256 CUs idle when
- * T is small (decode batches of up to a few hundred tokens); the pages' own split kernel
- * (vLLM fused_compress_quant_cache page, `_compress_gather_split_sparse_attn` and
+ * states to `workspace`; the last workgroup of a token to finish (found with a per-token arrival
+ * counter in the workspace) merges them and runs the epilogue, in the same kernel.  It exists
+ * because one workgroup per token leaves most of the 256 CUs idle when T is small (decode
+ * batches of up to about a hundred tokens); the pages' own split kernel (vLLM
+ * fused_compress_quant_cache page, `_compress_gather_split_sparse_attn` and
  * `_pick_compress_num_splits`) has the same purpose.
  *
  *   splits          0 = the library's choice for T (see dsv4_c128_workspace_bytes), or 1, 2,
- *                   4, 8, 16.  1 is the single-pass kernel.
+ *                   4, 8, 16.  1 is the single-pass kernel.  With splits > 1, T may be at most
+ *                   4096 (else DSV4_ERR_ARG; with splits == 0 the library never splits there).
  *   workspace       device memory of at least dsv4_c128_workspace_bytes(T, splits) bytes,
- *                   16-byte aligned, owned by the caller; its contents need no initialisation
- *                   and are scratch after the call.  Calls that share a workspace must be
+ *                   16-byte aligned, owned by the caller.  Its first 16384 bytes hold the
+ *                   arrival counters: they must be zero before the first call that splits (fill
+ *                   the buffer with zeros once, when it is allocated), and every call leaves them
+ *                   zero again, so the same workspace serves any number of later calls with any
+ *                   T and splits.  The rest is scratch.  Calls that share a workspace must be
  *                   ordered on one stream.  With splits == 0 and no (or too small a) workspace
  *                   the single pass runs; with explicit splits > 1 it is DSV4_ERR_ARG.
  *   compressed_out  NULL, or as in dsv4_c128_compress_store_debug.
  *
- * k_cache results equal the single pass's up to the fp32 summation order of the pooling.
+ * k_cache results equal the single pass's up to the fp32 summation order of the pooling, and do
+ * not depend on which workgroup of a token finishes last (the partials are merged in split
+ * order).
  */
 int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
                                 const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
@@ -159,9 +166,10 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
 
 /*
  * Bytes of workspace dsv4_c128_compress_store_ex needs for num_tokens tokens and `splits`
- * (0 = the library's choice: 8 for num_tokens <= 16, 4 for 17..64, 1 above).  0 when no
- * workspace is needed or splits is not valid.
- * Host-only; no HIP call.
+ * (0 = the library's choice: 8 for num_tokens <= 16, 4 for 17..64, 2 for 65..128, 1 above):
+ * 16384 + num_tokens * splits * 6144.  0 when no workspace is needed (splits 1) or the
+ * combination is not valid (splits not in {0, 1, 2, 4, 8, 16}, or more than 4096 tokens with
+ * splits > 1).  Host-only; no HIP call.
  */
 size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);
 

@@ -196,13 +196,23 @@ def workspace_bytes(num_tokens: int, splits: int = 0) -> int:
     return int(library().dsv4_c128_workspace_bytes(int(num_tokens), int(splits)))
 
 
+def fanout_workspace(num_tokens: int, splits: int = 0, device="cuda"):
+    """A zero-filled workspace for ``compress_store_ex`` (``workspace_bytes(T, splits)`` bytes, at
+    least 16).  Its arrival counters must start at zero; every call leaves them zero, so one
+    workspace, allocated once, serves later calls with any T and split count that fit it."""
+    return torch.zeros(max(workspace_bytes(num_tokens, splits), 16), dtype=torch.uint8,
+                       device=device)
+
+
 def compress_store_ex(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
                       cos_sin, k_cache, kv_slot_mapping, compressed_out=None, workspace=None,
                       splits: int = 0, stream: int | None = None) -> None:
     """``compress_store`` with the small-batch fan-out: each token's window is split over
     ``splits`` workgroups (0 = automatic; 1 = single pass) whose partial states go to
-    ``workspace`` (a device tensor of at least ``workspace_bytes(T, splits)`` bytes), then merged
-    per token.  ``compressed_out`` as in ``compress_store_debug``."""
+    ``workspace`` and are merged by the last of them to finish.  ``workspace``: a device tensor
+    of at least ``workspace_bytes(T, splits)`` bytes whose first 16384 bytes were zero-filled
+    before its first use (``fanout_workspace`` makes one).  ``compressed_out`` as in
+    ``compress_store_debug``."""
     ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
           k_cache, kv_slot_mapping]
     extra = [t for t in (compressed_out, workspace) if t is not None]
@@ -334,6 +344,7 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
 
 
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
+           "fanout_workspace",
            "compress_store_varlen", "varlen_workspace_bytes", "c4_compress_store", "c4_validate",
            "indexer_compress_store", "indexer_validate",
            "validate", "e4m3_encode", "last_error",

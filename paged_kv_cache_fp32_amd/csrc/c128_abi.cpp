@@ -275,6 +275,9 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
   if (compressed_out && !aligned16(compressed_out))
     return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
   if (p.num_tokens == 0) return DSV4_OK;
+  if (splits > 1 && p.num_tokens > dsv4::kFanoutMaxTokens)
+    return fail(DSV4_ERR_ARG, "the fan-out takes at most %lld tokens (got %d with %d splits)",
+                static_cast<long long>(dsv4::kFanoutMaxTokens), p.num_tokens, splits);
   int s = splits;
   if (s == 0) {
     s = dsv4::fanout_auto_splits(p.num_tokens);
@@ -289,7 +292,7 @@ int dsv4_c128_compress_store_ex(const dsv4_tensor* state_cache, const dsv4_tenso
     if (!aligned16(workspace)) return fail(DSV4_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
   p.compressed_out = compressed_out;
-  hipError_t err = dsv4::launch_c128_fanout(p, static_cast<float*>(workspace), s,
+  hipError_t err = dsv4::launch_c128_fanout(p, workspace, s,
                                             static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));

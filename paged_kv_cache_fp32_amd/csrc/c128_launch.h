@@ -13,9 +13,13 @@ namespace dsv4 {
 // Single pass and encoder: c128_kernel.hip.  Every launcher returns the hipError_t of its launch.
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
 // Fan-out and compacted schedules: c128_schedules.hip.
-// Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) with a
-// workspace of fanout_workspace_bytes(T, splits) bytes, 16-byte aligned.
-hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream);
+// Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) for at
+// most kFanoutMaxTokens tokens, with a workspace of fanout_workspace_bytes(T, splits) bytes,
+// 16-byte aligned, whose first kFanoutCounterBytes (the per-token arrival counters) are zero
+// before the call; the call leaves them zero.
+constexpr int64_t kFanoutMaxTokens = 4096;
+constexpr size_t kFanoutCounterBytes = kFanoutMaxTokens * sizeof(uint32_t);
+hipError_t launch_c128_fanout(const C128Params& p, void* ws, int splits, hipStream_t stream);
 int fanout_auto_splits(int64_t num_tokens);
 size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
 // Compacted schedule for long varlen batches: a gate scan into a workspace of

@@ -4,9 +4,9 @@
 // "fused_compress_quant_cache" API page, sparse-attention fused kernel), distributed
 // differently over workgroups:
 //
-//  * fan-out, for decode batches of up to a few dozen tokens, where one workgroup per token
-//    leaves most CUs idle: a token's window is split over several workgroups whose partial
-//    softmax states are merged by a second kernel;
+//  * fan-out, for decode batches of up to about a hundred tokens, where one workgroup per token
+//    leaves most CUs idle: a token's window is split over several workgroups, and the last of
+//    them to finish merges their partial softmax states;
 //  * compacted, for long varlen (prefill) batches where about one token in 128 closes a window:
 //    a gate scan lists those tokens, and a persistent grid processes only them.
 
@@ -200,16 +200,50 @@ __device__ __forceinline__ void finish_token(const C128Params& p, int32_t t, int
   if (epilogue_wave) epilogue<kDebug>(p, t, rope_row, c, half, lane, col, lds_ss[0] + lds_ss[1]);
 }
 
+// 16 bytes as two 8-byte agent-scope atomic accesses (relaxed): coherent across the XCDs
+// within a kernel.  p is 8-byte aligned.
+__device__ __forceinline__ void store_agent4(float* p, float a, float b, float c, float d) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  const uint64_t lo = static_cast<uint64_t>(__float_as_uint(a)) |
+                      (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+  const uint64_t hi = static_cast<uint64_t>(__float_as_uint(c)) |
+                      (static_cast<uint64_t>(__float_as_uint(d)) << 32);
+  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4 load_agent4(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float(static_cast<uint32_t>(lo)),
+                     __uint_as_float(static_cast<uint32_t>(lo >> 32)),
+                     __uint_as_float(static_cast<uint32_t>(hi)),
+                     __uint_as_float(static_cast<uint32_t>(hi >> 32)));
+}
+
 // ---------------------------------------------------------------------------------------------
-// Fan-out for small batches: a token's 16 window blocks are split over S = 16 / (RG*NBW)
-// workgroups (grid = T x S).  Workgroup (t, s) streams window blocks s*RG*NBW ..
-// (s+1)*RG*NBW - 1 (NBW blocks for each of its RG row groups) and
-// writes its merged partial state to the workspace:
-//   ws[((t * S + s) * 3 + {0: m (log2 units), 1: l, 2: acc}) * 512 + column].
-// The finish kernel then merges the S partials of each token and runs the epilogue.
-template <int RG, int NBW, int CH>
-__global__ void __launch_bounds__(128 * RG) c128_fanout_partial_kernel(const C128Params p,
-                                                                     float* __restrict__ ws) {
+// Fan-out for small batches, one kernel: a token's 16 window blocks are split over
+// S = 16 / (RG*NBW) workgroups (grid = T x S).  Workgroup (t, s) streams window blocks
+// s*RG*NBW .. (s+1)*RG*NBW - 1 (NBW blocks for each of its RG row groups), merges its row groups
+// and writes its partial state to the workspace:
+//   partials[((t * S + s) * 3 + {0: m (log2 units), 1: l, 2: acc}) * 512 + column],
+// then adds 1 to the token's arrival counter.  The workgroup that brings the counter to S is the
+// last of the token: it folds the S partials in split order, runs the epilogue and puts the
+// counter back to 0, so every call leaves the counters as it found them.
+//
+// Cross-workgroup visibility without cache-wide fences.  The 8 XCDs' L2 caches are not coherent
+// with each other inside a kernel, and an agent-scope release/acquire fence pair would write
+// back and invalidate a whole L2 per workgroup (which serialises hundreds of workgroups).
+// Instead the partial states are written with agent-scope atomic stores and read with
+// agent-scope atomic loads (device-coherent accesses that do not rely on the L2 line state), and
+// each wave waits for its stores to complete (s_waitcnt) before the workgroup barrier that
+// precedes the counter update; the last workgroup only reads partials after its own counter
+// update returned S - 1.  No workgroup ever waits for another, so the kernel cannot stall.
+template <int RG, int NBW, int CH, bool kDebug>
+__global__ void __launch_bounds__(128 * RG) c128_fanout_kernel(const C128Params p,
+                                                             float* __restrict__ partials,
+                                                             uint32_t* __restrict__ counters) {
   constexpr int kBlocksPerGroup = RG * NBW;
   static_assert(kWindowBlocks % kBlocksPerGroup == 0, "splits must divide the window");
   constexpr int S = kWindowBlocks / kBlocksPerGroup;
@@ -217,6 +251,8 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_partial_kernel(const C12
   __shared__ float4 lds_ml[RG][2][64];
   __shared__ float4 lds_l[RG][2][64];
   __shared__ float4 lds_acc[RG][2][64];
+  __shared__ float lds_ss[2];
+  __shared__ uint32_t lds_last;
 
   const int32_t t = blockIdx.x;
   const int s = blockIdx.y;
@@ -226,6 +262,8 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_partial_kernel(const C12
   const int rg = wave >> 1;
   const int col = half * 256 + lane * 4;
 
+  // Every workgroup of a token takes the same decision here, so either all S of them reach the
+  // counter or none does.
   const Window win = gate_and_window(p, t);
   if (!win.ok) return;
 
@@ -233,42 +271,40 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_partial_kernel(const C12
   stream_blocks<NBW, CH>(p, win.bt + s * kBlocksPerGroup + rg * NBW, static_cast<uint32_t>(col),
                          ml, l, acc);
   merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
+
+  float* base = partials + static_cast<int64_t>(t) * S * (3 * kHead) + col;
   if (rg == 0) {
-    float* out = ws + (static_cast<int64_t>(t) * S + s) * (3 * kHead) + col;
-    *reinterpret_cast<float4*>(out) = make_float4(ml[0], ml[1], ml[2], ml[3]);
-    *reinterpret_cast<float4*>(out + kHead) = make_float4(l[0], l[1], l[2], l[3]);
-    *reinterpret_cast<float4*>(out + 2 * kHead) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    float* out = base + s * (3 * kHead);
+    store_agent4(out, ml[0], ml[1], ml[2], ml[3]);
+    store_agent4(out + kHead, l[0], l[1], l[2], l[3]);
+    store_agent4(out + 2 * kHead, acc[0], acc[1], acc[2], acc[3]);
   }
-}
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const uint32_t last = arrived == static_cast<uint32_t>(S);
+    if (last) __hip_atomic_store(counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_last = last;
+  }
+  __syncthreads();
+  if (!lds_last) return;
 
-// One workgroup of 128 lanes per token: merge the S partials, then the fused epilogue.
-template <int S, bool kDebug>
-__global__ void __launch_bounds__(128) c128_fanout_finish_kernel(const C128Params p,
-                                                               const float* __restrict__ ws) {
-  __shared__ float lds_ss[2];
-  const int32_t t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = half * 256 + lane * 4;
-
-  const Window win = gate_and_window(p, t);  // the same decision the partial kernel took
-  if (!win.ok) return;
-
-  const float* in = ws + static_cast<int64_t>(t) * S * (3 * kHead) + col;
-  const float4 m0 = *reinterpret_cast<const float4*>(in);
-  const float4 l0 = *reinterpret_cast<const float4*>(in + kHead);
-  const float4 a0 = *reinterpret_cast<const float4*>(in + 2 * kHead);
-  float ml[4] = {m0.x, m0.y, m0.z, m0.w};
-  float l[4] = {l0.x, l0.y, l0.z, l0.w};
-  float acc[4] = {a0.x, a0.y, a0.z, a0.w};
+  if (rg == 0) {
+    const float4 m0 = load_agent4(base);
+    const float4 l0 = load_agent4(base + kHead);
+    const float4 a0 = load_agent4(base + 2 * kHead);
+    ml[0] = m0.x; ml[1] = m0.y; ml[2] = m0.z; ml[3] = m0.w;
+    l[0] = l0.x; l[1] = l0.y; l[2] = l0.z; l[3] = l0.w;
+    acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
 #pragma unroll
-  for (int s = 1; s < S; ++s) {
-    const float* q = in + s * (3 * kHead);
-    fold(ml, l, acc, *reinterpret_cast<const float4*>(q),
-         *reinterpret_cast<const float4*>(q + kHead),
-         *reinterpret_cast<const float4*>(q + 2 * kHead));
+    for (int q = 1; q < S; ++q) {
+      const float* in = base + q * (3 * kHead);
+      fold(ml, l, acc, load_agent4(in), load_agent4(in + kHead), load_agent4(in + 2 * kHead));
+    }
   }
-  finish_token<kDebug>(p, t, win.rope_row, true, half, lane, col, l, acc, lds_ss);
+  finish_token<kDebug>(p, t, win.rope_row, rg == 0, half, lane, col, l, acc, lds_ss);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -407,38 +443,43 @@ __global__ void __launch_bounds__(128 * kRowGroups)
 namespace {
 
 // Fan-out shapes: S splits of the 16 window blocks, each streamed by RG row groups of NBW blocks.
+// The workspace holds the arrival counters (kFanoutMaxTokens of them, at a fixed place so that
+// calls with different T or S never overwrite a counter with partial states), then the partials.
 template <int RG, int NBW>
-hipError_t launch_fanout(const C128Params& p, float* ws, hipStream_t stream) {
+hipError_t launch_fanout(const C128Params& p, void* ws, hipStream_t stream) {
   constexpr int S = kWindowBlocks / (RG * NBW);
-  const dim3 grid1(static_cast<unsigned>(p.num_tokens), S);
-  c128_fanout_partial_kernel<RG, NBW, kStageRows><<<grid1, dim3(128 * RG), 0, stream>>>(p, ws);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const dim3 grid2(static_cast<unsigned>(p.num_tokens));
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kFanoutCounterBytes);
+  const dim3 grid(static_cast<unsigned>(p.num_tokens), S);
   if (p.compressed_out)
-    c128_fanout_finish_kernel<S, true><<<grid2, dim3(128), 0, stream>>>(p, ws);
+    c128_fanout_kernel<RG, NBW, kStageRows, true>
+        <<<grid, dim3(128 * RG), 0, stream>>>(p, partials, counters);
   else
-    c128_fanout_finish_kernel<S, false><<<grid2, dim3(128), 0, stream>>>(p, ws);
+    c128_fanout_kernel<RG, NBW, kStageRows, false>
+        <<<grid, dim3(128 * RG), 0, stream>>>(p, partials, counters);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int fanout_auto_splits(int64_t num_tokens) {
-  // Measured on MI355X with the window sets rotated (cold HBM): 8 splits are fastest up to 16
-  // tokens, 4 up to 64; from about 100 tokens on the single pass already has enough
-  // workgroups and the extra partial-state traffic and second launch make the fan-out slower.
-  if (num_tokens <= 0 || num_tokens > 64) return 1;
-  return num_tokens <= 16 ? 8 : 4;
+  // Measured on MI355X (same-process timings, window sets rotated): 8 splits are fastest up to
+  // 16 tokens, 4 up to 64, 2 up to 128; from about 200 tokens on the single pass already has
+  // enough workgroups and the partial-state traffic makes the fan-out slower.
+  if (num_tokens <= 0 || num_tokens > 128) return 1;
+  if (num_tokens <= 16) return 8;
+  return num_tokens <= 64 ? 4 : 2;
 }
 
 size_t fanout_workspace_bytes(int64_t num_tokens, int splits) {
-  if (splits <= 1 || num_tokens <= 0) return 0;
-  return static_cast<size_t>(num_tokens) * static_cast<size_t>(splits) * 3 * kHead * sizeof(float);
+  if (splits <= 1 || num_tokens <= 0 || num_tokens > kFanoutMaxTokens) return 0;
+  return kFanoutCounterBytes +
+         static_cast<size_t>(num_tokens) * static_cast<size_t>(splits) * 3 * kHead * sizeof(float);
 }
 
-hipError_t launch_c128_fanout(const C128Params& p, float* ws, int splits, hipStream_t stream) {
+hipError_t launch_c128_fanout(const C128Params& p, void* ws, int splits, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
+  if (splits > 1 && p.num_tokens > kFanoutMaxTokens) return hipErrorInvalidValue;
   switch (splits) {
     case 1:
       return launch_c128_compress_store(p, stream);

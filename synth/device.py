@@ -75,8 +75,7 @@ class DeviceWorkload:
             else:
                 c128.compress_store(*self.args())
         else:
-            nbytes = c128.workspace_bytes(self.wl.num_tokens, splits)
-            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.state.device)
+            ws = c128.fanout_workspace(self.wl.num_tokens, splits, self.state.device)
             c128.compress_store_ex(*self.args(), compressed_out=comp, workspace=ws,
                                    splits=splits)
         torch.cuda.synchronize()

@@ -129,6 +129,8 @@ int main(void) {
   CHECK(dsv4_c128_workspace_bytes(16, 8) > dsv4_c128_workspace_bytes(16, 4));
   CHECK(dsv4_c128_workspace_bytes(16, 0) == dsv4_c128_workspace_bytes(16, 8));
   CHECK(dsv4_c128_workspace_bytes(1000, 0) == 0);
+  CHECK(dsv4_c128_workspace_bytes(100, 0) == 16384 + 100 * 2 * 6144); /* counters + partials */
+  CHECK(dsv4_c128_workspace_bytes(4097, 2) == 0);                      /* above 4096 tokens */
   CHECK(dsv4_c128_varlen_workspace_bytes(0) == 0);
   CHECK(dsv4_c128_varlen_workspace_bytes(1) == 4112); /* 4 * 1025 rounded up to 16 */
   CHECK(dsv4_c128_varlen_workspace_bytes(100) % 16 == 0);

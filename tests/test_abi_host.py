@@ -206,16 +206,21 @@ def test_python_binding_rejects_host_tensors():
 
 
 def test_workspace_bytes_rules():
-    """Automatic splits: 8 up to 16 tokens, 4 up to 64, 1 (no workspace) above; explicit
-    splits give T*splits*3*512 floats; invalid splits give 0."""
+    """Automatic splits: 8 up to 16 tokens, 4 up to 64, 2 up to 128, 1 (no workspace) above;
+    explicit splits give the 16 KiB counter region plus T*splits*3*512 floats; invalid splits,
+    or more than 4096 tokens with splits > 1, give 0."""
     wb = c128.workspace_bytes
     per = 3 * 512 * 4
-    assert wb(1, 0) == 1 * 8 * per
-    assert wb(16, 0) == 16 * 8 * per
-    assert wb(17, 0) == 17 * 4 * per
-    assert wb(64, 0) == 64 * 4 * per
-    assert wb(65, 0) == 0 and wb(512, 0) == 0 and wb(16384, 0) == 0
-    assert wb(10, 4) == 10 * 4 * per and wb(10, 1) == 0 and wb(100, 16) == 100 * 16 * per
+    cnt = 16384
+    assert wb(1, 0) == cnt + 1 * 8 * per
+    assert wb(16, 0) == cnt + 16 * 8 * per
+    assert wb(17, 0) == cnt + 17 * 4 * per
+    assert wb(64, 0) == cnt + 64 * 4 * per
+    assert wb(65, 0) == cnt + 65 * 2 * per and wb(128, 0) == cnt + 128 * 2 * per
+    assert wb(129, 0) == 0 and wb(512, 0) == 0 and wb(16384, 0) == 0
+    assert wb(10, 4) == cnt + 10 * 4 * per and wb(10, 1) == 0
+    assert wb(100, 16) == cnt + 100 * 16 * per
+    assert wb(4096, 2) == cnt + 4096 * 2 * per and wb(4097, 2) == 0
     assert wb(10, 3) == 0 and wb(10, 32) == 0 and wb(0, 4) == 0
 
 
@@ -237,6 +242,8 @@ def test_fanout_argument_errors_before_launch():
     assert ex_call(a, 32) == -8
     assert ex_call(a, 4) == -8 and "workspace" in c128.last_error()
     assert ex_call(a, 4, workspace=16, nbytes=16) == -8
+    big = valid_args(T=4097)
+    assert ex_call(big, 2, workspace=16, nbytes=1 << 40) == -8 and "4096" in c128.last_error()
     bad = valid_args()
     bad["state_cache"] = torch.zeros(32, 8, 512)
     assert ex_call(bad, 4) == -4

@@ -55,7 +55,7 @@ def test_graph_single_pass_and_fanout():
     d = DeviceWorkload(wl)
     announce("graph: single pass")
     capture_and_replay(d, lambda: c128.compress_store(*d.args()))
-    ws = torch.empty(c128.workspace_bytes(wl.num_tokens, 4), dtype=torch.uint8, device="cuda")
+    ws = c128.fanout_workspace(wl.num_tokens, 4)
     announce("graph: fan-out splits=4")
     capture_and_replay(d, lambda: c128.compress_store_ex(*d.args(), workspace=ws, splits=4))
 

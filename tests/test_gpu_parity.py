@@ -270,9 +270,35 @@ def test_fanout_automatic_on_workloads():
     check_ex(small(T=600, seed=77, kv_bs=64, kv_blocks=20), 0, "decode T=600")
 
 
+def test_fanout_workspace_reuse():
+    """One workspace, zero-filled once, serves a sequence of calls with different batch sizes,
+    split counts and windows (the same token indices get new windows in every call).  Between
+    calls the partial-state region is filled with NaN, so a read of anything but this call's
+    partials would show; after every call the 16 KiB counter region is zero again, and every
+    call's bytes agree with the oracle."""
+    import paged_kv_cache_fp32_amd as c128
+    ws = c128.fanout_workspace(130, 16)
+    counters, partials = ws[:16384], ws[16384:].view(torch.float32)
+    for i, (T, splits) in enumerate([(130, 16), (7, 8), (64, 2), (1, 4), (130, 2), (40, 0),
+                                     (16, 16), (100, 0)]):
+        wl = small(T=T, seed=900 + i, kv_bs=16, kv_blocks=-(-2 * T // 16) + 1)
+        d = DeviceWorkload(wl)
+        partials.fill_(float("nan"))
+        torch.cuda.synchronize()
+        announce(f"fan-out workspace reuse: call {i}, T={T}, splits={splits}")
+        c128.compress_store_ex(*d.args(), workspace=ws, splits=splits)
+        torch.cuda.synchronize()
+        assert int(counters.count_nonzero()) == 0, f"call {i}: counters not back at zero"
+        body, ok = d.k_cache_bytes()
+        rep = compare(wl, body, oracle.run(wl, THREADS))
+        assert ok and rep.ok(), f"call {i}: {rep.summary()}"
+        assert rep["written"] == T
+
+
 def test_fanout_gate_and_bad_indices():
     """Non-boundary tokens, negative slots and out-of-range device indices take the same
-    decisions in the partial and the finish kernels: nothing is written for them."""
+    decision in every workgroup of the token: nothing is written for them, and the token's
+    arrival counter is never touched."""
     wl = small(T=6, seed=7)
     wl.positions[:] = np.array([126, 128, 255, 254, 383, 511], np.int32)
     wl.slot_mapping[:] = np.array([3, 3, 3, 3, -1, 9], np.int32)
