@@ -295,6 +295,21 @@ def test_fanout_workspace_reuse():
         assert rep["written"] == T
 
 
+@pytest.fixture(scope="module")
+def batch_4096():
+    T = 4096
+    return synth.decode_batch(f"fan-out T={T}", 4100, T, 16 * T + 16, 64, 1024, kv_bs=64,
+                              kv_blocks=T // 64 + 1, cs_rows=8192)
+
+
+@pytest.mark.parametrize("splits", [2, 16])
+def test_fanout_largest_batch(batch_4096, splits):
+    """4096 tokens, the most the fan-out takes: the last arrival counter of the workspace's
+    counter region is used, and every token agrees with the oracle."""
+    rep, *_ = check_ex(batch_4096, splits, "decode T=4096", debug=False)
+    assert rep["written"] == 4096
+
+
 def test_fanout_gate_and_bad_indices():
     """Non-boundary tokens, negative slots and out-of-range device indices take the same
     decision in every workgroup of the token: nothing is written for them, and the token's
