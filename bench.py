@@ -42,8 +42,10 @@ PEAK_GBS = 8000.0  # MI355X HBM3E peak
 ACTIVE_TOKEN_BYTES = 128 * 1024 * 4 + 64 + 8 + 256 + 584
 ANY_TOKEN_BYTES = 8          # positions + slot_mapping, read for every token
 CALL_BYTES = 512 * 4         # rms weight
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c128_cfg4_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc", "c128_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c128_staged_16384tok_traffic.txt")
+CSRC = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc")
+KERNEL_SOURCES = ("c128_kernel.hip", "c128_schedules.hip", "c128_device.h", "c128_params.h",
+                  "c128_launch.h")
 
 
 def log(*a):
@@ -84,11 +86,12 @@ def algorithmic_bytes(wl) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the large-batch kernel is built from (the staged schedule, its
+    helpers and constants, and the dispatch in the single-pass file)."""
     import hashlib
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_device.h"),
-              os.path.join(os.path.dirname(KERNEL_SOURCE), "c128_params.h")):
-        h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -258,13 +261,13 @@ def cpu_baseline(wl, gpu_body, nbytes):
     }
 
 
-def oracle_timing(wl, nbytes):
-    """CPU baseline of a sweep workload: the oracle (no diagnostics) on the host cores, on the
-    same host inputs as the GPU run."""
+def oracle_timing(wl, nbytes, threads=None):
+    """CPU baseline of a sweep workload: the oracle (no diagnostics) on the host cores (or on
+    ``threads`` of them), on the same host inputs as the GPU run."""
     import oracle
     import synth
 
-    threads = synth.default_threads()
+    threads = synth.default_threads() if threads is None else threads
     t0 = time.perf_counter()
     oracle.run(wl, threads, diagnostics=False)
     dt = time.perf_counter() - t0
@@ -340,6 +343,8 @@ def sweep(args, path):
         if not args.no_cpu_baseline:
             if name not in cpu_seen:
                 cpu_seen[name] = oracle_timing(wl, nbytes)
+                if name.startswith("cfg1"):  # the 128-token batch also on one core
+                    cpu_seen[name]["one_core"] = oracle_timing(wl, nbytes, threads=1)
             rec["cpu_baseline"] = cpu_seen[name]
         out.write(json.dumps(rec) + "\n")
         out.flush()

@@ -107,6 +107,13 @@ typedef struct dsv4_tensor {
  * The fused compress-store (steps 1-6 above) for all T tokens, launched on
  * `stream` (a hipStream_t; NULL means the default stream).
  * `eps` is the RMSNorm epsilon.
+ *
+ * Below 8192 tokens one workgroup handles each token (the single pass).  From
+ * 8192 tokens on, a workgroup takes up to 64 tokens and inserts their records
+ * after its last state read (the staged schedule), which keeps the k_cache
+ * writes out of the state stream.  It merges 8 partial row groups per token
+ * instead of 4, so a code can differ from the single pass's by one step of
+ * fp32 rounding; both agree with the definition to the same tolerance.
  */
 int dsv4_c128_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
                              const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
@@ -180,8 +187,9 @@ size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);
  * returns early unless (pos + 1) % 128 == 0), and in a prefill batch that is about one token in
  * 128.  A first kernel tests the gate on every token and writes the passing token indices,
  * compacted, to `workspace`; a persistent grid of workgroups then processes only those tokens.
- * Results are identical to dsv4_c128_compress_store's, bit for bit, and do not depend on the
- * schedule.  For decode batches, where every token passes, the plain entry point is faster.
+ * Per token it computes exactly what the single pass computes, so below 8192 tokens its results
+ * equal dsv4_c128_compress_store's bit for bit; they never depend on the schedule.  For decode
+ * batches, where every token passes, the plain entry point is faster.
  *
  *   workspace       device memory of at least dsv4_c128_varlen_workspace_bytes(T) bytes,
  *                   16-byte aligned, owned by the caller; no initialisation needed, scratch after

@@ -223,6 +223,7 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
 
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
+  if (p.num_tokens >= kStagedMinTokens) return launch_c128_staged(p, stream);
   const dim3 grid(static_cast<unsigned>(p.num_tokens));
   const dim3 block(128 * kRowGroups);
   if (p.compressed_out)

@@ -11,7 +11,15 @@
 namespace dsv4 {
 
 // Single pass and encoder: c128_kernel.hip.  Every launcher returns the hipError_t of its launch.
+// Batches of kStagedMinTokens and more go to the staged schedule.
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
+// Staged schedule for large batches (c128_schedules.hip): a workgroup of kStagedRowGroups row
+// groups takes up to kStagedMaxTokens tokens and inserts their records after its last state read.
+constexpr int64_t kStagedMinTokens = 8192;
+constexpr int kStagedMaxTokens = 64;
+constexpr int kStagedRowGroups = 8;
+constexpr int kStagedWavesPerSimd = 4;
+hipError_t launch_c128_staged(const C128Params& p, hipStream_t stream);
 // Fan-out and compacted schedules: c128_schedules.hip.
 // Fan-out over `splits` workgroups per token (1, 2, 4, 8 or 16; 1 is the single pass) for at
 // most kFanoutMaxTokens tokens, with a workspace of fanout_workspace_bytes(T, splits) bytes,

@@ -10,6 +10,8 @@
 //  * compacted, for long varlen (prefill) batches where about one token in 128 closes a window:
 //    a gate scan lists those tokens, and a persistent grid processes only them.
 
+#include <atomic>
+
 #include "c128_device.h"
 #include "c128_launch.h"
 
@@ -119,11 +121,14 @@ __device__ __forceinline__ void merge_row_groups(float4 (&lds_ml)[RG][2][64],
 
 // Fused epilogue of token t on 128 lanes (2 waves, one per column half; 4 columns per lane):
 // RMSNorm, bf16 round trip, per-64 absmax -> UE8M0 exponent -> E4M3FN codes, GPT-J RoPE ->
-// bf16, paged insert.  sumsq is the sum of squares of all 512 pooled values.
-template <bool kDebug>
-__device__ __forceinline__ void epilogue(const C128Params& p, int32_t t, int32_t rope_row,
-                                         const float (&c)[4], int half, int lane, int col,
-                                         float sumsq) {
+// bf16, paged insert.  sumsq is the sum of squares of all 512 pooled values.  The 584-byte
+// record goes to the token's k_cache slot, or with kStage to `stage` (an LDS record: 576 data
+// bytes, then the 8 scale bytes) for a later insert.  Returns the kv slot, or -1 when the token
+// has none (nothing is written then).
+template <bool kDebug, bool kStage = false>
+__device__ __forceinline__ int32_t epilogue(const C128Params& p, int32_t t, int32_t rope_row,
+                                            const float (&c)[4], int half, int lane, int col,
+                                            float sumsq, uint8_t* stage = nullptr) {
   const float var = sumsq * (1.0f / kHead);
   const float rrms = 1.0f / __builtin_sqrtf(var + p.eps);
   const float4 w = *reinterpret_cast<const float4*>(p.rms_w + col);
@@ -142,13 +147,20 @@ __device__ __forceinline__ void epilogue(const C128Params& p, int32_t t, int32_t
   amax = group16_max(amax);
 
   const int32_t kv_slot = p.kv_slot_mapping[t];
-  if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return;
-  const int32_t kb = kv_slot / p.kv_bs;
-  const int32_t ko = kv_slot - kb * p.kv_bs;
-  uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
-  uint8_t* rec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
-  uint8_t* scl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
-                 static_cast<int64_t>(ko) * kScaleBytes;
+  if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return -1;
+  uint8_t* rec;
+  uint8_t* scl;
+  if constexpr (kStage) {
+    rec = stage;
+    scl = stage + kRecordBytes;
+  } else {
+    const int32_t kb = kv_slot / p.kv_bs;
+    const int32_t ko = kv_slot - kb * p.kv_bs;
+    uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+    rec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
+    scl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+          static_cast<int64_t>(ko) * kScaleBytes;
+  }
 
   const bool rope_lane = (half == 1) && (lane >= 48);
   if (!rope_lane) {
@@ -179,15 +191,17 @@ __device__ __forceinline__ void epilogue(const C128Params& p, int32_t t, int32_t
     *reinterpret_cast<uint2*>(rec + kNope + 8 * j) = make_uint2(lo, hi);
     if (j == 0) scl[kNumQuant] = 0;  // pad byte
   }
+  return kv_slot;
 }
 
 // c = acc / l, then the RMSNorm sum of squares over both column halves (one barrier), then the
-// epilogue on the 128 lanes of the first two waves.  Every wave must call it.
-template <bool kDebug>
-__device__ __forceinline__ void finish_token(const C128Params& p, int32_t t, int32_t rope_row,
-                                             bool epilogue_wave, int half, int lane, int col,
-                                             const float (&l)[4], const float (&acc)[4],
-                                             float* lds_ss) {
+// epilogue on the 128 lanes of the first two waves.  Every wave must call it.  Returns the
+// epilogue's kv slot on the epilogue waves, -1 on the others.
+template <bool kDebug, bool kStage = false>
+__device__ __forceinline__ int32_t finish_token(const C128Params& p, int32_t t, int32_t rope_row,
+                                                bool epilogue_wave, int half, int lane, int col,
+                                                const float (&l)[4], const float (&acc)[4],
+                                                float* lds_ss, uint8_t* stage = nullptr) {
   float c[4] = {0.f, 0.f, 0.f, 0.f};
   if (epilogue_wave) {
 #pragma unroll
@@ -197,7 +211,9 @@ __device__ __forceinline__ void finish_token(const C128Params& p, int32_t t, int
     if (lane == 0) lds_ss[half] = ss;
   }
   __syncthreads();
-  if (epilogue_wave) epilogue<kDebug>(p, t, rope_row, c, half, lane, col, lds_ss[0] + lds_ss[1]);
+  if (!epilogue_wave) return -1;
+  return epilogue<kDebug, kStage>(p, t, rope_row, c, half, lane, col, lds_ss[0] + lds_ss[1],
+                                  stage);
 }
 
 // 16 bytes as two 8-byte agent-scope atomic accesses (relaxed): coherent across the XCDs
@@ -438,6 +454,165 @@ __global__ void __launch_bounds__(128 * kRowGroups)
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Staged schedule for large batches.  With one workgroup per token, each token's 584-byte record
+// reaches HBM on its own, in the middle of the state stream; on MI355X those scattered writes
+// cost about 4.5% of the large-batch call (measured: the single pass with its stores switched off
+// runs at the rate of a pure read of the same gather).  Here a workgroup of 8 row groups (16
+// waves, one window block per wave) takes `tokens_per_group` tokens, keeps their records in LDS
+// and inserts them all after its last state read, so the k_cache writes arrive in one burst at
+// the end of the call.
+//
+//  * Token assignment: with G = gridDim.x, step k of workgroup b takes token k*G + ((b + 3k) mod
+//    G), a permutation of each row of G tokens.  A dense run of active tokens, or prefill window
+//    ends 128 tokens apart, spread over all workgroups instead of queueing on a few.
+//  * Prologue: one thread per (token, window block) resolves the gate, request, window column,
+//    RoPE row and block id of every token of the workgroup at once, into LDS, and one wave lists
+//    the tokens that go on.  Inside the token loop every per-token value then comes from LDS: a
+//    global load after a workgroup barrier cannot be a scalar load (the barrier's fence counts
+//    as a possible write), and a chain of vector loads with full waits in front of every token
+//    costs more than the staging gains.
+//  * Per token, the same steps as the single pass (stream, row-group merge, fused epilogue);
+//    8 row groups instead of 4, so the fp32 summation order differs from the single pass's.
+template <int RG, int CH, int WPE, int KMAX, bool kDebug>
+__global__ void __launch_bounds__(128 * RG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+c128_staged_kernel(const C128Params p, int32_t tokens_per_group) {
+  static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
+  static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
+  static_assert(KMAX * kWindowBlocks <= 128 * RG, "one prologue thread per (token, block)");
+  constexpr int NB = kWindowBlocks / RG;  // state blocks per wave
+  constexpr int NCH = NB * kStateBlock / CH;
+  constexpr int kStagesPerBlock = kStateBlock / CH;
+  static_assert(NCH % 2 == 0, "ping-pong needs an even chunk count");
+
+  __shared__ float4 lds_ml[RG][2][64];
+  __shared__ float4 lds_l[RG][2][64];
+  __shared__ float4 lds_acc[RG][2][64];
+  __shared__ float lds_ss[2];
+  __shared__ __align__(16) int32_t lds_ids[KMAX][kWindowBlocks];  // -1: out of range
+  __shared__ int32_t lds_rope[KMAX];  // RoPE row; -1: the token is skipped
+  __shared__ int32_t lds_kv[KMAX];    // kv slot of a staged record; -1: none
+  __shared__ int32_t lds_list[KMAX];  // the tokens that go on, in order
+  __shared__ int32_t lds_count;
+  __shared__ __align__(16) uint8_t lds_stage[KMAX][kSlotBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int rg = wave >> 1;
+  const int64_t G = gridDim.x;
+  auto token_of = [&](int k) -> int64_t {
+    return static_cast<int64_t>(k) * G + (static_cast<int64_t>(blockIdx.x) + 3 * k) % G;
+  };
+
+  // ---- prologue: thread (k, i) resolves window block i of the workgroup's k-th token
+  {
+    const int k = threadIdx.x / kWindowBlocks, i = threadIdx.x % kWindowBlocks;
+    if (k < tokens_per_group) {
+      int32_t rope = -1, id = -1;
+      const int64_t t = token_of(k);
+      if (t < p.num_tokens) {
+        const int32_t pos = p.positions[t];
+        const int32_t slot = p.slot_mapping[t];
+        if (slot >= 0 && pos >= 0 && (pos & (kRatio - 1)) == kRatio - 1) {
+          const int32_t win = pos >> 7;
+          const int32_t req = p.token_to_req[t];
+          if (req >= 0 && req < p.bt_rows &&
+              static_cast<int64_t>(win + 1) * kWindowBlocks <= p.bt_cols &&
+              win * kRatio < p.cs_rows) {
+            rope = win * kRatio;
+            const int32_t b = p.block_table[static_cast<int64_t>(req) * p.bt_stride +
+                                            static_cast<int64_t>(win) * kWindowBlocks + i];
+            id = static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks) ? b : -1;
+          }
+        }
+      }
+      lds_ids[k][i] = id;
+      if (i == 0) {
+        lds_rope[k] = rope;
+        lds_kv[k] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- wave 0 lists the tokens that pass the gate with every block id in range (lane k: token
+  // k), so that a sparse group (a prefill batch: about one token in 128 closes a window) costs
+  // only its prologue
+  if (wave == 0) {
+    bool go = false;
+    if (lane < tokens_per_group && lds_rope[lane] >= 0) {
+      const int4* idv = reinterpret_cast<const int4*>(lds_ids[lane]);
+      const int4 a0 = idv[0], a1 = idv[1], a2 = idv[2], a3 = idv[3];
+      go = (a0.x | a0.y | a0.z | a0.w | a1.x | a1.y | a1.z | a1.w | a2.x | a2.y | a2.z | a2.w |
+            a3.x | a3.y | a3.z | a3.w) >= 0;
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(go);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+    if (go) lds_list[below] = lane;
+    if (lane == 0) lds_count = __builtin_popcountll(mask);
+  }
+  __syncthreads();
+  const int count = __builtin_amdgcn_readfirstlane(lds_count);
+  if (count == 0) return;  // uniform: nothing to stream, nothing to insert
+
+  const int col = half * 256 + lane * 4;
+  const uint32_t ucol = static_cast<uint32_t>(col);
+  const int64_t s0 = p.s0, s1 = p.s1;
+  for (int j = 0; j < count; ++j) {
+    // every value below is workgroup-uniform (LDS), so all waves meet the barriers
+    const int k = __builtin_amdgcn_readfirstlane(lds_list[j]);
+    const int32_t rope_row = __builtin_amdgcn_readfirstlane(lds_rope[k]);
+    int32_t mybt[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mybt[b] = __builtin_amdgcn_readfirstlane(lds_ids[k][rg * NB + b]);
+    auto rowptr = [&](int ch) {  // wave-uniform
+      return p.state + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
+             static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
+    };
+
+    float ml[4], l[4], acc[4];
+    float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
+    load_rows<CH>(kvA, scA, rowptr(0), s1, ucol);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ch += 2) {
+      load_rows<CH>(kvB, scB, rowptr(ch + 1), s1, ucol);
+      if (ch == 0)
+        update<true, CH>(kvA, scA, ml, l, acc);
+      else
+        update<false, CH>(kvA, scA, ml, l, acc);
+      if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1, ucol);
+      update<false, CH>(kvB, scB, ml, l, acc);
+    }
+    merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
+    const int32_t t = static_cast<int32_t>(token_of(k));
+    const int32_t kv = finish_token<kDebug, true>(p, t, rope_row, rg == 0, half, lane, col, l,
+                                                  acc, lds_ss, lds_stage[k]);
+    if (rg == 0 && half == 0 && lane == 0) lds_kv[k] = kv;
+    // No barrier here: the next token's merge writes lds_ml/l/acc only, which the epilogue
+    // waves have finished reading, and its lds_ss writes follow that merge's barrier.
+  }
+
+  // ---- insert the staged records (8-byte stores: 72 record chunks, then the scale chunk)
+  __syncthreads();
+  constexpr int kChunks = kSlotBytes / 8;
+  for (int idx = threadIdx.x; idx < count * kChunks; idx += 128 * RG) {
+    const int j = idx / kChunks, c = idx - j * kChunks;
+    const int k = lds_list[j];
+    const int32_t kv_slot = lds_kv[k];
+    if (kv_slot < 0) continue;
+    const int32_t kb = kv_slot / p.kv_bs;
+    const int32_t ko = kv_slot - kb * p.kv_bs;
+    uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+    uint8_t* dst = c < kRecordBytes / 8
+                       ? blockp + static_cast<int64_t>(ko) * kRecordBytes + 8 * c
+                       : blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+                             static_cast<int64_t>(ko) * kScaleBytes;
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&lds_stage[k][8 * c]);
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -533,6 +708,46 @@ hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stre
   else
     c128_compacted_kernel<false><<<dim3(grid), dim3(128 * kRowGroups), 0, stream>>>(
         p, counts, list, chunk, nblocks);
+  return hipGetLastError();
+}
+
+namespace {
+
+// Compute units of the current device (the staged grid is sized in whole rounds of one
+// workgroup per CU); looked up once per device, 256 on MI355X.
+int staged_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace
+
+hipError_t launch_c128_staged(const C128Params& p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  // One round = one workgroup per CU (the LDS stage allows no second one); as many rounds as
+  // kStagedMaxTokens tokens per workgroup need, then the tokens spread evenly over them.
+  const int64_t cus = staged_cu_count();
+  const int64_t per_round = cus * kStagedMaxTokens;
+  const int64_t rounds = (p.num_tokens + per_round - 1) / per_round;
+  const int64_t groups = cus * rounds;
+  const int32_t per_group = static_cast<int32_t>((p.num_tokens + groups - 1) / groups);
+  const dim3 grid(static_cast<unsigned>(groups));
+  const dim3 block(128 * kStagedRowGroups);
+  if (p.compressed_out)
+    c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, true>
+        <<<grid, block, 0, stream>>>(p, per_group);
+  else
+    c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, false>
+        <<<grid, block, 0, stream>>>(p, per_group);
   return hipGetLastError();
 }
 

@@ -350,6 +350,34 @@ def scattered_batch(name: str, seed: int, num_tokens: int, num_reqs: int, n_bloc
     return wl
 
 
+
+def shared_pool_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
+                      kv_bs: int, kv_blocks: int, cs_rows: int,
+                      score_std: float = math.sqrt(2.0), kc_block_pad: int = 0) -> Workload:
+    """Large decode-shaped batches on a small pool: one request per token, each at position
+    128k-1 with k ~ U{1..k_max}, block-table entries uniform over an ``n_blocks`` pool (windows
+    may share blocks; a window reads 16 of them), kv slots a seeded injection.  Every token
+    closes a window; tests perturb gates and indices afterwards."""
+    T = num_tokens
+    if T > kv_blocks * kv_bs:
+        raise ValueError("not enough kv slots")
+    cols = 16 * k_max
+    k = randint(T, 1, k_max, seed, 50)
+    positions = (WINDOW * k - 1).astype(np.int64)
+    bt = (bits(T * cols, seed, 51) % np.uint64(n_blocks)).astype(np.int32).reshape(T, cols)
+    blk = bt[np.arange(T), positions // STATE_BLOCK].astype(np.int64)
+    slot_mapping = (blk * STATE_BLOCK + positions % STATE_BLOCK).astype(np.int32)
+    kv_slots = permutation(kv_blocks * kv_bs, seed, 52)[:T].astype(np.int32)
+    state_base, state = alloc_state(n_blocks)
+    fill_state(state, seed, 1.0, score_std)
+    kc_base, kc = alloc_k_cache(kv_blocks, kv_bs, kc_block_pad)
+    wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),
+                  slot_mapping, _rms_weight(seed), 1e-6, rope_table(cs_rows), kc, kv_slots, seed,
+                  state_base, kc_base)
+    wl.info = {"kind": "shared-pool decode", "tokens": T, "pool_blocks": n_blocks}
+    return wl
+
+
 C4_RATIO = 4
 C4_ROWS = 2 * C4_RATIO       # window rows: the previous window's 4 and the current 4
 C4_ROW = 4 * HEAD            # kv (2 x 512) | score (2 x 512)
