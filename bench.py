@@ -44,6 +44,7 @@ ANY_TOKEN_BYTES = 8          # positions + slot_mapping, read for every token
 CALL_BYTES = 512 * 4         # rms weight
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c128_staged_16384tok_traffic.txt")
 CSRC = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc")
+STAGED_MIN_TOKENS = 8192  # the plain entry point's switch to the staged schedule
 KERNEL_SOURCES = ("c128_kernel.hip", "c128_schedules.hip", "c128_device.h", "c128_params.h",
                   "c128_launch.h")
 
@@ -330,7 +331,8 @@ def sweep(args, path):
                "entry": ("indexer" if getattr(wl, "indexer", False) else
                          "c4" if getattr(wl, "compress_ratio", 128) == 4 else
                          "varlen (compacted)" if varlen else
-                         "single pass" if splits is None else f"fan-out splits={splits}"),
+                         ("staged" if wl.num_tokens >= STAGED_MIN_TOKENS else "single pass")
+                         if splits is None else f"fan-out splits={splits}"),
                "algorithmic_bytes_per_call": nbytes,
                "warm_us_median": round(float(np.median(per)) * 1e3, 2),
                "warm_us_mean": round(float(np.mean(per)) * 1e3, 2)}
