@@ -467,10 +467,10 @@ def c4_sweep(want, measure, dev):
 
 
 def read_line(args):
-    """Attainable-bandwidth references on this machine (bench_support probes): a plain
-    sequential streaming read of 4 GiB (best of a few launch shapes), and a read of the
-    16-block windows of the 16384-token workload with the compress kernel's lane mapping
-    but none of its arithmetic."""
+    """Attainable-bandwidth references on this machine (bench_support probes): a sequential
+    streaming read of 4 GiB (best of a few launch shapes), and a read of the 16-block windows
+    of the 16384-token workload with the compress kernel's lane mapping but none of its
+    arithmetic; each with plain loads and with the non-temporal hint."""
     import ctypes
 
     import torch
@@ -487,15 +487,17 @@ def read_line(args):
     src = torch.ones(n, dtype=torch.float32, device=dev)
     out = torch.empty(1 << 16, dtype=torch.float32, device=dev)
     rec = {"mode": "read", "stream_bytes": 4 * n}
-    best = None
-    for blocks, threads in ((1024, 512), (2048, 512), (4096, 256), (8192, 256), (2048, 256)):
-        def call(b=blocks, t=threads):
-            assert L.probe_stream_read(src.data_ptr(), 4 * n, out.data_ptr(), b, t, sid) == 0
-        _, per = time_calls(torch, stream, [call], args.steps, args.warmup)
-        gbs = 4 * n / (float(np.median(per)) * 1e-3) / 1e9
-        rec[f"stream_gbs_{blocks}x{threads}"] = round(gbs, 1)
-        best = gbs if best is None else max(best, gbs)
-    rec["stream_gbs_best"] = round(best, 1)
+    for nt, tag in ((0, ""), (1, "_nt")):
+        best = None
+        for blocks, threads in ((1024, 512), (2048, 512), (4096, 256), (8192, 256), (2048, 256)):
+            def call(b=blocks, t=threads, nt=nt):
+                assert L.probe_stream_read(src.data_ptr(), 4 * n, out.data_ptr(), b, t, nt,
+                                           sid) == 0
+            _, per = time_calls(torch, stream, [call], args.steps, args.warmup)
+            gbs = 4 * n / (float(np.median(per)) * 1e-3) / 1e9
+            rec[f"stream{tag}_gbs_{blocks}x{threads}"] = round(gbs, 1)
+            best = gbs if best is None else max(best, gbs)
+        rec[f"stream{tag}_gbs_best"] = round(best, 1)
     del src
     torch.cuda.empty_cache()
     wl = synth.config4()
@@ -507,14 +509,15 @@ def read_line(args):
     ids_d = torch.from_numpy(ids).to(dev)
     s0 = d.state.stride(0)
 
-    def gather():
-        assert L.probe_block_gather_read(d.state.data_ptr(), s0, ids_d.data_ptr(), T,
-                                         out.data_ptr(), sid) == 0
-    _, per = time_calls(torch, stream, [gather], args.steps, args.warmup)
-    ms = float(np.median(per))
     rec["gather_bytes"] = T * 128 * 4096
-    rec["gather_us"] = round(ms * 1e3, 2)
-    rec["gather_gbs"] = round(T * 128 * 4096 / (ms * 1e-3) / 1e9, 1)
+    for nt, tag in ((0, ""), (1, "_nt")):
+        def gather(nt=nt):
+            assert L.probe_block_gather_read(d.state.data_ptr(), s0, ids_d.data_ptr(), T,
+                                             out.data_ptr(), nt, sid) == 0
+        _, per = time_calls(torch, stream, [gather], args.steps, args.warmup)
+        ms = float(np.median(per))
+        rec[f"gather{tag}_us"] = round(ms * 1e3, 2)
+        rec[f"gather{tag}_gbs"] = round(T * 128 * 4096 / (ms * 1e-3) / 1e9, 1)
     print(json.dumps(rec), flush=True)
 
 

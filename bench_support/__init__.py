@@ -27,9 +27,9 @@ def lib():
             raise ImportError(f"{LIB} missing: run __graft_entry__.build()")
         L = ctypes.CDLL(LIB)
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.probe_stream_read.argtypes = [vp, i64, vp, ci, ci, vp]
+        L.probe_stream_read.argtypes = [vp, i64, vp, ci, ci, ci, vp]
         L.probe_stream_read.restype = ci
-        L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, vp]
+        L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, ci, vp]
         L.probe_block_gather_read.restype = ci
         _lib = L
     return _lib

@@ -6,6 +6,7 @@
 //    ids[16w .. 16w+15] (32 KiB each when stride0 = 8192 floats) with the same
 //    lane-to-16-byte-vector mapping as the compress kernel, summing them: the
 //    compress kernel's exact HBM access pattern without its arithmetic.
+// Each comes with plain loads and with the non-temporal hint the compress kernels use.
 // Both write one float per workgroup so the loads cannot be removed.
 
 #include <hip/hip_runtime.h>
@@ -13,6 +14,19 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNt>
+__device__ __forceinline__ float4 ld(const float4* p) {
+  if constexpr (kNt) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
+template <bool kNt>
 __global__ void __launch_bounds__(512) stream_read(const float4* __restrict__ p, int64_t n4,
                                                    float* __restrict__ out) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -21,12 +35,12 @@ __global__ void __launch_bounds__(512) stream_read(const float4* __restrict__ p,
   for (; i + 7 * stride < n4; i += 8 * stride) {
     float4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[i + k * stride];
+    for (int k = 0; k < 8; ++k) v[k] = ld<kNt>(p + i + k * stride);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += (v[k].x + v[k].y) + (v[k].z + v[k].w);
   }
   for (; i < n4; i += stride) {
-    const float4 v = p[i];
+    const float4 v = ld<kNt>(p + i);
     acc += (v.x + v.y) + (v.z + v.w);
   }
   if (threadIdx.x == 0 || acc == 1234.5f) out[blockIdx.x] = acc;
@@ -34,6 +48,7 @@ __global__ void __launch_bounds__(512) stream_read(const float4* __restrict__ p,
 
 // 512 lanes: lane l of wave w covers 16-byte vector (w % 2) * 64 + l of each 4 KiB row
 // half pair ... here simply: the workgroup sweeps each 32 KiB block with 512 x 16 B per step.
+template <bool kNt>
 __global__ void __launch_bounds__(512) block_gather_read(const float* __restrict__ pool,
                                                          int64_t stride0,
                                                          const int32_t* __restrict__ ids,
@@ -50,8 +65,8 @@ __global__ void __launch_bounds__(512) block_gather_read(const float* __restrict
     float4 v[16];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      v[2 * r] = *reinterpret_cast<const float4*>(base + r * 1024);
-      v[2 * r + 1] = *reinterpret_cast<const float4*>(base + r * 1024 + 512);
+      v[2 * r] = ld<kNt>(reinterpret_cast<const float4*>(base + r * 1024));
+      v[2 * r + 1] = ld<kNt>(reinterpret_cast<const float4*>(base + r * 1024 + 512));
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc += (v[k].x + v[k].y) + (v[k].z + v[k].w);
@@ -62,17 +77,25 @@ __global__ void __launch_bounds__(512) block_gather_read(const float* __restrict
 }  // namespace
 
 extern "C" int probe_stream_read(const void* p, int64_t bytes, float* out, int blocks,
-                                 int threads, void* stream) {
+                                 int threads, int nt, void* stream) {
   if (!p || !out || bytes < 16 || blocks < 1 || threads < 64 || threads > 512) return -1;
-  stream_read<<<blocks, threads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const float4*>(p), bytes / 16, out);
+  if (nt)
+    stream_read<true><<<blocks, threads, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const float4*>(p), bytes / 16, out);
+  else
+    stream_read<false><<<blocks, threads, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const float4*>(p), bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 extern "C" int probe_block_gather_read(const float* pool, int64_t stride0, const int32_t* ids,
-                                       int n_windows, float* out, void* stream) {
+                                       int n_windows, float* out, int nt, void* stream) {
   if (!pool || !ids || !out || n_windows < 1 || stride0 < 8192) return -1;
-  block_gather_read<<<n_windows, 512, 0, static_cast<hipStream_t>(stream)>>>(pool, stride0, ids,
-                                                                           out);
+  if (nt)
+    block_gather_read<true><<<n_windows, 512, 0, static_cast<hipStream_t>(stream)>>>(
+        pool, stride0, ids, out);
+  else
+    block_gather_read<false><<<n_windows, 512, 0, static_cast<hipStream_t>(stream)>>>(
+        pool, stride0, ids, out);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
