@@ -60,6 +60,14 @@ def test_graph_single_pass_and_fanout():
     capture_and_replay(d, lambda: c128.compress_store_ex(*d.args(), workspace=ws, splits=4))
 
 
+def test_graph_staged_schedule():
+    """8192 tokens: the plain entry point takes the staged schedule."""
+    wl = synth.shared_pool_batch("graph staged", 1305, 8192, 2048, 8, 64, 130, 1024)
+    d = DeviceWorkload(wl)
+    announce("graph: staged schedule (plain entry point, 8192 tokens)")
+    capture_and_replay(d, lambda: c128.compress_store(*d.args()))
+
+
 def test_graph_compacted_schedule():
     wl = synth.varlen_prefill("graph varlen", 1302, 8, 600, 1024, 8 * 208, kv_bs=64,
                               cs_rows=2048)
