@@ -86,13 +86,24 @@ def algorithmic_bytes(wl) -> int:
     return int(act.sum()) * ACTIVE_TOKEN_BYTES + wl.num_tokens * ANY_TOKEN_BYTES + CALL_BYTES
 
 
+def code_text(path: str) -> str:
+    """A C++ source with its comments and whitespace removed (the sources have no string
+    literals that contain comment markers)."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the sources the large-batch kernel is built from (the staged schedule, its
-    helpers and constants, and the dispatch in the single-pass file)."""
+    """Hash of the code of the sources the large-batch kernel is built from (the staged
+    schedule, its helpers and constants, and the dispatch in the single-pass file); edits to
+    comments do not change it."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        h.update(open(os.path.join(CSRC, name), "rb").read())
+        h.update(code_text(os.path.join(CSRC, name)).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,7 +8,10 @@
 //    leaves most CUs idle: a token's window is split over several workgroups, and the last of
 //    them to finish merges their partial softmax states;
 //  * compacted, for long varlen (prefill) batches where about one token in 128 closes a window:
-//    a gate scan lists those tokens, and a persistent grid processes only them.
+//    a gate scan lists those tokens, and a persistent grid processes only them;
+//  * staged, which the plain entry point takes from 8192 tokens on: a workgroup takes up to 64
+//    tokens and inserts their records after its last state read, so that the k_cache writes do
+//    not land in the middle of the state stream.
 
 #include <atomic>
 
