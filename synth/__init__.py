@@ -353,7 +353,8 @@ def scattered_batch(name: str, seed: int, num_tokens: int, num_reqs: int, n_bloc
 
 def shared_pool_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_max: int,
                       kv_bs: int, kv_blocks: int, cs_rows: int,
-                      score_std: float = math.sqrt(2.0), kc_block_pad: int = 0) -> Workload:
+                      score_std: float = math.sqrt(2.0), kc_block_pad: int = 0,
+                      row_pad: int = 0, block_pad: int = 0) -> Workload:
     """Large decode-shaped batches on a small pool: one request per token, each at position
     128k-1 with k ~ U{1..k_max}, block-table entries uniform over an ``n_blocks`` pool (windows
     may share blocks; a window reads 16 of them), kv slots a seeded injection.  Every token
@@ -368,7 +369,7 @@ def shared_pool_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k_ma
     blk = bt[np.arange(T), positions // STATE_BLOCK].astype(np.int64)
     slot_mapping = (blk * STATE_BLOCK + positions % STATE_BLOCK).astype(np.int32)
     kv_slots = permutation(kv_blocks * kv_bs, seed, 52)[:T].astype(np.int32)
-    state_base, state = alloc_state(n_blocks)
+    state_base, state = alloc_state(n_blocks, row_pad=row_pad, block_pad=block_pad)
     fill_state(state, seed, 1.0, score_std)
     kc_base, kc = alloc_k_cache(kv_blocks, kv_bs, kc_block_pad)
     wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),

@@ -356,6 +356,26 @@ def test_staged_threshold_and_rounds(T):
     assert rep["written"] == T
 
 
+def test_staged_padded_strides_and_largest_position():
+    """The staged schedule on padded state rows and blocks and padded k_cache blocks (8192
+    tokens); then a token at position 2^31 - 1 (a boundary of ratio 128) is skipped without
+    overflow and the others still agree with the oracle."""
+    wl = synth.shared_pool_batch("staged padded", 5200, 8192, 2048, 8, 64, 130, 1024,
+                                 row_pad=16, block_pad=32, kc_block_pad=24)
+    rep, *_ = check(wl, label="staged padded strides T=8192")
+    assert rep["written"] == 8192
+    wl.positions[4321] = 2 ** 31 - 1
+    announce("staged largest position")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    orc = oracle.run(wl, THREADS)
+    assert orc.status[4321] == -1 and (np.delete(orc.status, 4321) == 1).all()
+    wl.kv_slot_mapping[4321] = -1
+    rep = compare(wl, body, orc)
+    assert rep.ok(), rep.summary()
+    assert np.isnan(comp[4321]).all()
+
+
 def test_staged_gates_and_bad_indices():
     """A 12,000-token staged batch with non-boundary positions, negative state and kv slots, and
     out-of-range requests, block ids and kv slots scattered through it: the tokens the oracle
