@@ -3,22 +3,23 @@
 
     python bench.py [--steps K] [--warmup W] [--sweep PATH] [--no-cpu-baseline]
 
-A step is one call of the fused kernel over the whole batch: 16384 boundary
-tokens (one per request, position 128k-1, k ~ U{1..64}), each gathering 16
-distinct blocks of a 262144-block fp32 state pool (8.59 GB, every block read
-once per call), then RMSNorm, UE8M0/E4M3 quantisation, RoPE and the paged
-insert into a KV-block-size-64 k_cache.  Inputs are resident in HBM before
-timing starts.
+A step is one call of the plain entry point over the whole batch (one kernel
+launch; at this size the staged schedule): 16384 boundary tokens (one per
+request, position 128k-1, k ~ U{1..64}), each gathering 16 distinct blocks of a
+262144-block fp32 state pool (8.59 GB, every block read once per call), then
+RMSNorm, UE8M0/E4M3 quantisation, RoPE and the paged insert into a
+KV-block-size-64 k_cache.  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
 ``--sweep PATH`` also writes per-workload JSONL with warm and cold timings and the
 oracle's time beside each workload: the C128 decode sweep 1..4096 tokens, the
 single-token, decode-batch and varlen-prefill workloads on every entry point
-(single pass, fan-out, compacted), and the C4 and indexer compressors
+(plain: single pass or staged; fan-out; compacted), and the C4 and indexer compressors
 (``--sweep-filter REGEX`` keeps matching workloads; ``--mode sweep`` skips the
 large-batch line).  ``--mode copy`` times a plain device-to-device copy (the
-counter-calibration kernel for rocprofv3); ``--mode read`` times plain streaming
-reads (the attainable-bandwidth reference lines).
+counter-calibration kernel for rocprofv3); ``--mode read`` times streaming and
+window-gather reads, with plain and non-temporal loads (the attainable-bandwidth
+reference lines).
 """
 
 from __future__ import annotations
