@@ -77,3 +77,29 @@ def test_fuzz(case):
     assert guards_ok, "k_cache guard bands were written"
     rep = compare(wl, body, oracle.run(wl, 4), gpu_compressed=comp)
     assert rep.ok(), rep.summary()
+
+
+def draw_large(case):
+    """Batches the plain entry point runs on the staged schedule (8192 tokens and more), on a
+    small shared pool, with random paddings and the same gate and slot perturbations."""
+    rng = np.random.default_rng(9500 + case)
+    T = int(rng.choice([8192, 9001, 12345, 16500]))
+    kv_bs = int(rng.choice([16, 64]))
+    wl = synth.shared_pool_batch(f"fuzz large {case}", 9500 + case, T, 2048, 8, kv_bs,
+                                 -(-T // kv_bs) + 2, 1024,
+                                 score_std=float(rng.choice([0.5, 2 ** 0.5, 4.0])),
+                                 kc_block_pad=int(rng.choice([0, 8, 40])),
+                                 row_pad=int(rng.choice([0, 16])),
+                                 block_pad=int(rng.choice([0, 32])))
+    perturb(wl, rng, 128)
+    return wl
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_fuzz_staged(case):
+    wl = draw_large(case)
+    announce(f"fuzz staged case {case}: T={wl.num_tokens} kv_bs={wl.k_cache.shape[1]}")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok, "k_cache guard bands were written"
+    rep = compare(wl, body, oracle.run(wl, 8), gpu_compressed=comp)
+    assert rep.ok(), rep.summary()
