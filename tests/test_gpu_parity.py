@@ -295,6 +295,26 @@ def test_fanout_workspace_reuse():
         assert rep["written"] == T
 
 
+def test_fanout_many_calls_one_workspace():
+    """24 calls in a row on one workspace, nothing cleared in between: random batch sizes (1 to
+    64 tokens) and split counts, new windows for the same token indices every call, so a read of
+    a previous call's partial state (a valid-looking value) would show against the oracle."""
+    import paged_kv_cache_fp32_amd as c128
+    ws = c128.fanout_workspace(64, 16)
+    rng = np.random.default_rng(7700)
+    for i in range(24):
+        T = int(rng.integers(1, 65))
+        splits = int(rng.choice([2, 4, 8, 16]))
+        wl = small(T=T, seed=7700 + i, kv_bs=16, kv_blocks=-(-2 * T // 16) + 1)
+        d = DeviceWorkload(wl)
+        announce(f"fan-out call {i}: T={T}, splits={splits}")
+        c128.compress_store_ex(*d.args(), workspace=ws, splits=splits)
+        body, ok = d.k_cache_bytes()
+        rep = compare(wl, body, oracle.run(wl, THREADS))
+        assert ok and rep.ok(), f"call {i}: {rep.summary()}"
+    assert int(ws[:16384].count_nonzero()) == 0
+
+
 @pytest.fixture(scope="module")
 def batch_4096():
     T = 4096
