@@ -298,7 +298,10 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_kernel(const C128Params 
     store_agent4(out + kHead, l[0], l[1], l[2], l[3]);
     store_agent4(out + 2 * kHead, acc[0], acc[1], acc[2], acc[3]);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  // This wave's partial stores have completed before the barrier.  An asm statement with a
+  // memory clobber, so the compiler cannot move the stores below it (the s_waitcnt builtin
+  // does not constrain memory operations).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t arrived =
