@@ -45,7 +45,7 @@ ANY_TOKEN_BYTES = 8          # positions + slot_mapping, read for every token
 CALL_BYTES = 512 * 4         # rms weight
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c128_staged_16384tok_traffic.txt")
 CSRC = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc")
-STAGED_MIN_TOKENS = 8192  # the plain entry point's switch to the staged schedule
+STAGED_MIN_TOKENS = 2048  # the plain entry point's switch to the staged schedule
 KERNEL_SOURCES = ("c128_kernel.hip", "c128_schedules.hip", "c128_device.h", "c128_params.h",
                   "c128_launch.h")
 

@@ -108,8 +108,8 @@ typedef struct dsv4_tensor {
  * `stream` (a hipStream_t; NULL means the default stream).
  * `eps` is the RMSNorm epsilon.
  *
- * Below 8192 tokens one workgroup handles each token (the single pass).  From
- * 8192 tokens on, a workgroup takes up to 64 tokens and inserts their records
+ * Below 2048 tokens one workgroup handles each token (the single pass).  From
+ * 2048 tokens on, a workgroup takes up to 64 tokens and inserts their records
  * after its last state read (the staged schedule), which keeps the k_cache
  * writes out of the state stream.  It merges 8 partial row groups per token
  * instead of 4, so a code can differ from the single pass's by one step of
@@ -187,7 +187,7 @@ size_t dsv4_c128_workspace_bytes(int64_t num_tokens, int splits);
  * returns early unless (pos + 1) % 128 == 0), and in a prefill batch that is about one token in
  * 128.  A first kernel tests the gate on every token and writes the passing token indices,
  * compacted, to `workspace`; a persistent grid of workgroups then processes only those tokens.
- * Per token it computes exactly what the single pass computes, so below 8192 tokens its results
+ * Per token it computes exactly what the single pass computes, so below 2048 tokens its results
  * equal dsv4_c128_compress_store's bit for bit; they never depend on the schedule.  For decode
  * batches, where every token passes, the plain entry point is faster.
  *

@@ -1,5 +1,5 @@
 """MI355X (gfx950) compress-store for the DeepSeek-V4 compressors: C128 (single pass, staged
-schedule from 8192 tokens, small-batch fan-out, compacted varlen schedule), C4 and the
+schedule from 2048 tokens, small-batch fan-out, compacted varlen schedule), C4 and the
 indexer's FP8 compressor.
 
 Thin ctypes binding of ``libdsv4_c128.so`` (C ABI in ``include/dsv4_c128.h``).
@@ -166,7 +166,7 @@ def compress_store(state_cache, block_table, token_to_req, positions, slot_mappi
                    cos_sin, k_cache, kv_slot_mapping, stream: int | None = None) -> None:
     """Fused C128 compress -> RMSNorm -> FP8/UE8M0 quant -> RoPE -> paged insert (in place
     on ``k_cache``), enqueued on ``stream`` (default: torch's current stream).  One kernel
-    launch: a workgroup per token below 8192 tokens, the staged schedule from 8192 on."""
+    launch: a workgroup per token below 2048 tokens, the staged schedule from 2048 on."""
     ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
           k_cache, kv_slot_mapping)
     dev = _require_cuda(ts)

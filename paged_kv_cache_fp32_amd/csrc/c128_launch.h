@@ -15,7 +15,7 @@ namespace dsv4 {
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
 // Staged schedule for large batches (c128_schedules.hip): a workgroup of kStagedRowGroups row
 // groups takes up to kStagedMaxTokens tokens and inserts their records after its last state read.
-constexpr int64_t kStagedMinTokens = 8192;
+constexpr int64_t kStagedMinTokens = 2048;
 constexpr int kStagedMaxTokens = 64;
 constexpr int kStagedRowGroups = 8;
 constexpr int kStagedWavesPerSimd = 4;

@@ -9,7 +9,7 @@
 //    them to finish merges their partial softmax states;
 //  * compacted, for long varlen (prefill) batches where about one token in 128 closes a window:
 //    a gate scan lists those tokens, and a persistent grid processes only them;
-//  * staged, which the plain entry point takes from 8192 tokens on: a workgroup takes up to 64
+//  * staged, which the plain entry point takes from 2048 tokens on: a workgroup takes up to 64
 //    tokens and inserts their records after its last state read, so that the k_cache writes do
 //    not land in the middle of the state stream.
 

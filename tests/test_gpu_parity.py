@@ -367,10 +367,10 @@ def shared(T, seed):
     return synth.shared_pool_batch(f"shared pool T={T}", seed, T, 2048, 8, 64, T // 64 + 2, 1024)
 
 
-@pytest.mark.parametrize("T", [8191, 8192, 20000])
+@pytest.mark.parametrize("T", [2047, 2048, 8192, 20000])
 def test_staged_threshold_and_rounds(T):
-    """8191 tokens take the single pass and 8192 the staged schedule (one round, 32 tokens per
-    workgroup); 20000 take two rounds of 40.  Every record and every pooled vector of the debug
+    """2047 tokens take the single pass and 2048 the staged schedule (one round, 8 tokens per
+    workgroup); 8192 take one round of 32 and 20000 two rounds of 40.  Every record and every pooled vector of the debug
     entry point agrees with the oracle."""
     rep, *_ = check(shared(T, 5000 + T), label=f"shared pool T={T}")
     assert rep["written"] == T
