@@ -41,7 +41,7 @@
  *                                      both strides 16-byte aligned
  *   block_table     i32 [R, M]         stride[1] == 1, M >= 16
  *   token_to_req    i32 [T]            contiguous
- *   positions       i32 [T]            contiguous
+ *   positions       i32 [T]            contiguous; T <= DSV4_MAX_TOKENS
  *   slot_mapping    i32 [T]            contiguous; only its sign is used
  *   rms_w           f32 [512]          contiguous, 16-byte aligned
  *   cos_sin         f32 [P, >= 64]     stride[1] == 1; cos in [0,32), sin in [32,64)
@@ -75,7 +75,12 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 6
+#define DSV4_ABI_VERSION 7
+
+/* Most tokens one call takes (2^27).  The largest launch grid, the staged schedule's 16
+   work-items per token, then stays within half of the 32-bit work-item count of a dispatch.
+   Longer batches are split by the caller: tokens are independent. */
+#define DSV4_MAX_TOKENS 134217728
 
 enum dsv4_dtype { DSV4_F32 = 1, DSV4_I32 = 2, DSV4_U8 = 3 };
 
@@ -87,7 +92,7 @@ enum dsv4_status {
   DSV4_ERR_SHAPE = -4,  /* state block != 8, state row != 1024 (head 512 + score 512),
                            k_cache row != 584, rms_w != 512, cos_sin < 64 columns,
                            block table < 16 columns, token arrays of different length,
-                           or a size above INT32_MAX */
+                           more than DSV4_MAX_TOKENS tokens, or a size above INT32_MAX */
   DSV4_ERR_STRIDE = -5, /* inner stride != 1, overlapping rows/blocks, k_cache stride[0]
                            below bs*584 */
   DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the alignment stated above */

@@ -95,6 +95,9 @@ int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_ten
   // positions defines T; every other token array must match it
   if ((rc = check_tensor(pos, "positions", DSV4_I32, 1))) return rc;
   const int64_t T = pos->shape[0];
+  if (T > DSV4_MAX_TOKENS)
+    return fail(DSV4_ERR_SHAPE, "positions: %lld tokens, at most %lld per call",
+                static_cast<long long>(T), static_cast<long long>(DSV4_MAX_TOKENS));
   if ((rc = check_token_array(pos, "positions", T))) return rc;
   if ((rc = check_token_array(t2r, "token_to_req", T))) return rc;
   if ((rc = check_token_array(slot, "slot_mapping", T))) return rc;

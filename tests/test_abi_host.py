@@ -88,9 +88,8 @@ def test_kv_block_size_one_passes():
 def test_padded_views_pass():
     a = valid_args()
     a["state_cache"] = torch.zeros(32, 8, 1024 + 64)[:, :, :1024]
-    a["k_cache"] = torch.zeros(2, 4 * 584 + 48, dtype=torch.uint8)[:, :4 * 584].view(
-        2, 4, 584) if False else torch.as_strided(torch.zeros(2 * (4 * 584 + 48), dtype=torch.uint8),
-                                                  (2, 4, 584), (4 * 584 + 48, 584, 1))
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * (4 * 584 + 48), dtype=torch.uint8),
+                                    (2, 4, 584), (4 * 584 + 48, 584, 1))
     a["cos_sin"] = torch.zeros(128, 96)[:, :64]
     a["block_table"] = torch.zeros(4, 80, dtype=torch.int32)[:, :64]
     assert call_validate(a) == 0, c128.last_error()
@@ -163,6 +162,46 @@ def test_null_descriptor():
     rc = lib.dsv4_c128_validate(*[ctypes.byref(x) for x in d], 1e-6,
                                 *[ctypes.byref(x) for x in rest])
     assert rc == -1
+
+
+TOKEN_ARRAYS = ("token_to_req", "positions", "slot_mapping", "kv_slot_mapping")
+ARG_ORDER = ("state_cache", "block_table", "token_to_req", "positions", "slot_mapping", "rms_w",
+             "cos_sin", "k_cache", "kv_slot_mapping")
+
+
+def descriptors_with_tokens(a, T):
+    """Descriptors of ``a`` whose four token arrays claim T tokens (validation reads only the
+    descriptors, so a small buffer stands behind them)."""
+    ds = [c128.describe(a[k]) for k in ARG_ORDER]
+    for k, d in zip(ARG_ORDER, ds):
+        if k in TOKEN_ARRAYS:
+            d.shape[0] = T
+    refs = [ctypes.byref(d) for d in ds]
+    return refs[:6], refs[6:]
+
+
+@pytest.mark.parametrize("fn,args", [("dsv4_c128_validate", valid_args),
+                                     ("dsv4_c4_validate", lambda: c4_args()),
+                                     ("dsv4_indexer_validate", lambda: idx_args())])
+def test_token_count_limit(fn, args):
+    """DSV4_MAX_TOKENS tokens pass validation; one more is DSV4_ERR_SHAPE with a message that
+    names the limit, for every compressor."""
+    limit = header_constant("DSV4_MAX_TOKENS")
+    assert limit == 1 << 27
+    lib = c128.library()
+    a = args()
+    head, tail = descriptors_with_tokens(a, limit)
+    assert getattr(lib, fn)(*head, 1e-6, *tail) == 0, c128.last_error()
+    head, tail = descriptors_with_tokens(a, limit + 1)
+    assert getattr(lib, fn)(*head, 1e-6, *tail) == -4
+    assert f"at most {limit}" in c128.last_error()
+
+
+def test_compute_entry_point_rejects_too_many_tokens_before_launch():
+    """The limit is checked before any HIP call (host pointers, no GPU)."""
+    lib = c128.library()
+    head, tail = descriptors_with_tokens(valid_args(), header_constant("DSV4_MAX_TOKENS") + 1)
+    assert lib.dsv4_c128_compress_store(*head, 1e-6, *tail, None) == -4
 
 
 def test_compute_entry_points_reject_before_any_hip_call():
