@@ -414,3 +414,14 @@ def test_indexer_layout_errors():
                                     (532, 132, 1))
     assert idx_validate(a) == 0
     assert c4_validate(idx_args()) == -4
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no fallback path."""
+    monkeypatch.setattr(c128, "LIBRARY_PATH", str(tmp_path / "libdsv4_c128.so"))
+    monkeypatch.setattr(c128, "_lib", None)
+    with pytest.raises(ImportError, match="no fallback"):
+        c128.abi_version()
+    a = valid_args()
+    with pytest.raises(ImportError):
+        call_validate(a)
