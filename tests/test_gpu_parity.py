@@ -6,6 +6,7 @@ on <= 0.1% of elements, RoPE bf16 within 1 ulp, fp32 compressed within 1e-5
 of sum_i p_ij |kv_ij|.  Every test prints its case before touching the GPU.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -556,3 +557,50 @@ def test_largest_position_is_skipped(mode):
     rep = compare(wl, body, orc)
     assert rep.ok(), rep.summary()
     assert np.isnan(comp[2]).all()
+
+
+# ---------------------------------------------------------------- pool beyond 2^31 floats
+
+def test_state_pool_beyond_2_31_floats():
+    """A 17.2 GB state pool of 2^19 + 64 blocks (more than 2^32 floats).  A 2048-token batch's
+    2048 distinct blocks are placed at random ids across the whole pool, the last block among
+    them, so row addresses pass 2^31 and 2^32 floats.  The plain entry point (staged at 2048
+    tokens), a 40-token single pass, the fan-out and the compacted schedule each agree with
+    the oracle run on the compact pool: moving blocks and renumbering the table changes no
+    result (a pinned property of the oracle)."""
+    n_big = (1 << 19) + 64
+    wl = synth.shared_pool_batch("pool beyond 2^31 floats", 7300, 2048, 2048, 8, 64, 34, 1024)
+    n_small = wl.state.shape[0]
+    assert wl.block_table.min() >= 0 and wl.block_table.max() < n_small
+    rng = np.random.default_rng(7301)
+    ids = rng.choice(n_big - 1, size=n_small - 1, replace=False)
+    ids = rng.permutation(np.append(ids, n_big - 1)).astype(np.int64)
+    cols = (wl.positions // 8)[:, None] - np.arange(16)[None, :]     # each token's window
+    top = int(ids[wl.block_table[np.arange(wl.num_tokens)[:, None], cols]].max())
+    assert top == n_big - 1 and top * 8 * 1024 > (1 << 32)
+    announce(f"pool beyond 2^31 floats: allocating {n_big} blocks ({n_big * 32 / 2**20:.1f} GiB)")
+    pool = torch.empty((n_big, 8, 1024), dtype=torch.float32, device="cuda")
+    pool[torch.from_numpy(ids).cuda()] = torch.from_numpy(np.ascontiguousarray(wl.state)).cuda()
+    big_table = torch.from_numpy(ids[wl.block_table].astype(np.int32)).cuda()
+    sub = dataclasses.replace(wl, name="pool beyond 2^31 floats, 40 tokens",
+                              token_to_req=wl.token_to_req[:40], positions=wl.positions[:40],
+                              slot_mapping=wl.slot_mapping[:40],
+                              kv_slot_mapping=wl.kv_slot_mapping[:40])
+    try:
+        for w, kw, label in ((wl, {}, "plain entry point (staged), 2048 tokens"),
+                             (sub, {}, "plain entry point (single pass), 40 tokens"),
+                             (sub, {"splits": 4}, "fan-out splits=4, 40 tokens"),
+                             (wl, {"varlen": True}, "compacted schedule, 2048 tokens")):
+            announce(f"pool beyond 2^31 floats: {label}")
+            d = DeviceWorkload(w, state=(pool, pool))
+            d.block_table = big_table
+            comp = d.run(debug=True, **kw)
+            body, guards_ok = d.k_cache_bytes()
+            assert guards_ok, "k_cache guard bands were written"
+            rep = compare(w, body, oracle.run(w, THREADS), gpu_compressed=comp.cpu().numpy())
+            print(rep.summary(), flush=True)
+            assert rep.ok(), rep.summary()
+            assert rep["written"] == w.num_tokens
+    finally:
+        del pool
+        torch.cuda.empty_cache()
