@@ -89,6 +89,23 @@ class DeviceWorkload:
         return buf[g:-g].copy(), guards_ok
 
 
+def relocated_pool(wl, n_blocks, ids, device="cuda"):
+    """A device state pool of ``n_blocks`` blocks (the block and row shape of ``wl.state``, no
+    padding) that holds block b of ``wl.state`` at id ``ids[b]``; the other blocks stay
+    uninitialised, so the block table must send every window read to a relocated block.
+    Returns (pool, block table renumbered through ``ids``, as an int32 device tensor)."""
+    st = wl.state
+    ids = np.asarray(ids, dtype=np.int64)
+    assert ids.shape == (st.shape[0],) and len(np.unique(ids)) == ids.size
+    assert ids.min() >= 0 and ids.max() < n_blocks
+    bt = wl.block_table
+    assert bt.min() >= 0 and bt.max() < st.shape[0], "every table entry must name a pool block"
+    pool = torch.empty((n_blocks,) + st.shape[1:], dtype=torch.float32, device=device)
+    pool[torch.from_numpy(ids).to(device)] = torch.from_numpy(np.ascontiguousarray(st)).to(device)
+    table = torch.from_numpy(ids[bt].astype(np.int32)).to(device)
+    return pool, table
+
+
 def run_gpu(wl, debug=True, splits=None, varlen=False):
     d = DeviceWorkload(wl)
     comp = d.run(debug=debug, splits=splits, varlen=varlen)

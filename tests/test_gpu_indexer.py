@@ -7,11 +7,12 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synth
 from oracle.compare import compare
-from synth.device import run_gpu
+from synth.device import DeviceWorkload, relocated_pool, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +134,34 @@ def test_indexer_padded_strides_and_largest_position():
     rep = compare(wl, body, orc)
     assert rep.ok(), rep.summary()
     assert np.isnan(comp[5]).all()
+
+
+def test_indexer_state_pool_beyond_2_31_floats():
+    """A 17.2 GB indexer state pool (more than 2^32 floats: rows of 512 floats, blocks of 8 rows).
+    A 2500-token batch's blocks are placed at random ids across it, one window block at the last
+    id, and the kernel agrees with the oracle run on the compact pool (relocating blocks and
+    renumbering the table changes no result)."""
+    wl = idx_batch(2500, 7400 + 512, state_bs=8)
+    n_small, sbs = wl.state.shape[0], wl.state.shape[1]
+    n_big = (1 << 32) // (sbs * 512) + 64
+    rng = np.random.default_rng(7401)
+    ids = rng.choice(n_big - 1, size=n_small, replace=False).astype(np.int64)
+    pos = wl.positions.astype(np.int64)
+    first = int(wl.block_table[0, pos[0] // sbs])          # a block that token 0's window reads
+    ids[first] = n_big - 1
+    assert (n_big - 1) * sbs * 512 > (1 << 32)
+    announce(f"indexer pool beyond 2^31 floats: {n_big} blocks")
+    pool, table = relocated_pool(wl, n_big, ids)
+    try:
+        d = DeviceWorkload(wl, state=(pool, pool))
+        d.block_table = table
+        comp = d.run(debug=True)
+        body, guards_ok = d.k_cache_bytes()
+        assert guards_ok, "k_cache guard bands were written"
+        rep = compare(wl, body, oracle.run(wl, THREADS), gpu_compressed=comp.cpu().numpy())
+        print(rep.summary(), flush=True)
+        assert rep.ok(), rep.summary()
+        assert rep["written"] == wl.num_tokens
+    finally:
+        del pool
+        torch.cuda.empty_cache()

@@ -16,7 +16,7 @@ import torch
 import oracle
 import synth
 from oracle.compare import compare
-from synth.device import DeviceWorkload, run_gpu
+from synth.device import DeviceWorkload, relocated_pool, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -579,9 +579,7 @@ def test_state_pool_beyond_2_31_floats():
     top = int(ids[wl.block_table[np.arange(wl.num_tokens)[:, None], cols]].max())
     assert top == n_big - 1 and top * 8 * 1024 > (1 << 32)
     announce(f"pool beyond 2^31 floats: allocating {n_big} blocks ({n_big * 32 / 2**20:.1f} GiB)")
-    pool = torch.empty((n_big, 8, 1024), dtype=torch.float32, device="cuda")
-    pool[torch.from_numpy(ids).cuda()] = torch.from_numpy(np.ascontiguousarray(wl.state)).cuda()
-    big_table = torch.from_numpy(ids[wl.block_table].astype(np.int32)).cuda()
+    pool, big_table = relocated_pool(wl, n_big, ids)
     sub = dataclasses.replace(wl, name="pool beyond 2^31 floats, 40 tokens",
                               token_to_req=wl.token_to_req[:40], positions=wl.positions[:40],
                               slot_mapping=wl.slot_mapping[:40],
