@@ -1,5 +1,5 @@
 """CPU oracle of the compress-store paths: the sparse-attention compressors C128 and C4 and the
-indexer's FP8 compressor (test infrastructure).
+indexer's compressor with its FP8 and MXFP4 caches (test infrastructure).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never links or calls
@@ -31,6 +31,7 @@ RECORD = 576
 SCALE_DIM = 8
 
 STATUS_INACTIVE, STATUS_WRITTEN, STATUS_NO_SLOT, STATUS_BAD_INDEX = 0, 1, 2, -1
+FMT_SPARSE, FMT_INDEXER_FP8, FMT_INDEXER_MXFP4 = 0, 1, 2   # cache formats
 
 
 def build(force: bool = True) -> str:
@@ -80,8 +81,15 @@ def lib():
         L.oracle_ceil_log2.restype = ctypes.c_int
         L.oracle_ue8m0_exponent.argtypes = [dbl]
         L.oracle_ue8m0_exponent.restype = ctypes.c_int
+        L.oracle_e2m1_code.argtypes = [dbl]
+        L.oracle_e2m1_code.restype = ctypes.c_uint8
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_value.restype = dbl
+        L.oracle_mxfp4_exponent.argtypes = [dbl]
+        L.oracle_mxfp4_exponent.restype = ctypes.c_int
         for name in ("oracle_bf16_bits_array", "oracle_e4m3_code_array",
-                     "oracle_ue8m0_exponent_array"):
+                     "oracle_ue8m0_exponent_array", "oracle_e2m1_code_array",
+                     "oracle_mxfp4_exponent_array"):
             getattr(L, name).argtypes = [vp, vp, i64]
             getattr(L, name).restype = None
         _lib = L
@@ -113,6 +121,25 @@ def e4m3_value(code: int) -> float:
     return lib().oracle_e4m3_value(code)
 
 
+def e2m1_codes(x) -> np.ndarray:
+    """E2M1 codes (low nibble; 0x8 = sign) of the values ``x``."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e2m1_code_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def mxfp4_exponents(absmax) -> np.ndarray:
+    x = np.ascontiguousarray(absmax, dtype=np.float64)
+    out = np.empty(x.shape, np.int32)
+    lib().oracle_mxfp4_exponent_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
 class OracleResult:
     """k_cache after the oracle ran, plus per-token fp64 diagnostics."""
 
@@ -133,8 +160,9 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
     copied first, so the workload stays untouched.  Diagnostics rows of
     tokens outside the range or that fail the gate are NaN.  Compress ratio
     and overlap come from the workload (C128 when absent); an indexer workload
-    (``wl.indexer``) has head 128 and the indexer's cache format, and its
-    ``normed`` rows hold the values that were quantised (after RoPE).
+    (``wl.indexer``) has head 128 and the indexer's FP8 cache format, or its MXFP4
+    format when ``wl.indexer_fp4`` is set, and its ``normed`` rows hold the
+    rotated values that were quantised (before their bf16 round trip).
     """
     T = wl.num_tokens
     lo, hi = (0, T) if tokens is None else tokens
@@ -163,6 +191,8 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
     rms_w = np.ascontiguousarray(wl.rms_w, dtype=np.float32)
     indexer = bool(getattr(wl, "indexer", False))
     head = INDEXER_HEAD if indexer else HEAD
+    fmt = (FMT_INDEXER_MXFP4 if getattr(wl, "indexer_fp4", False) else FMT_INDEXER_FP8) \
+        if indexer else FMT_SPARSE
     comp = absn = normd = None
     if diagnostics:
         comp = np.full((T, head), np.nan)
@@ -173,7 +203,7 @@ def run(wl, nthreads: int = 1, tokens=None, diagnostics: bool = True,
     cr = int(getattr(wl, "compress_ratio", 128))
     overlap = int(getattr(wl, "overlap", 0))
     rc = lib().oracle_compress_store_fmt(
-        head, int(indexer), cr, overlap, (1 + overlap) * head, state.ctypes.data, state.shape[0], sbs, s0, s1,
+        head, fmt, cr, overlap, (1 + overlap) * head, state.ctypes.data, state.shape[0], sbs, s0, s1,
         bt.ctypes.data, bt.shape[0], bt.shape[1], bt.strides[0] // 4,
         arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data, T,
         rms_w.ctypes.data, float(wl.eps), cs.ctypes.data, cs.shape[0], cs.strides[0] // 4,

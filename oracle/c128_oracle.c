@@ -36,12 +36,24 @@
  *   insert  128 code bytes at blk*stride0 + off*128, the fp32 scale at blk*stride0 +
  *           kv_bs*128 + off*4
  *
+ * Its MXFP4 variant (same page, kernel `_fused_kv_compress_norm_rope_insert_indexer_mxfp4_attn`)
+ * pools, normalises and rotates the same way, then:
+ *   round   every rotated value (held in fp32) goes through bf16
+ *   quant   four blocks of 32 consecutive dims: absmax (floor 6 * 2^-126), exponent
+ *           e = ceil(log2(absmax / 6)) clamped to [-127, 127], E2M1 codes of x * 2^-e
+ *   insert  64 bytes at blk*stride0 + off*64, byte p holding dim 2p in its low nibble and
+ *           dim 2p+1 in its high nibble; the 4 exponent bytes e + 127 at blk*stride0 +
+ *           kv_bs*64 + off*4
+ *
  * Readings where the pages leave a point open (each one is listed with its
  * reason in the design notes of the repository):
  *   - int32 index arrays; fp32 rms weight and cos/sin table;
  *   - `.to(bfloat16)` and `.to(float8e4nv)` round to nearest, ties to even;
  *     float8e4nv is the OCP E4M3FN format (bias 7, max 448, no infinities);
- *   - the exponent is the exact ceil(log2) of the fp32 product absmax * fl32(1/448);
+ *   - the exponent is the exact ceil(log2) of the fp32 product absmax * fl32(1/448)
+ *     (MXFP4: absmax * fl32(1/6));
+ *   - the page does not print its E2M1 conversion: E2M1 rounds to nearest, ties to the
+ *     even code, keeps the sign (zero included) and saturates at 6, like the E4M3 reading;
  *   - the normalised value is held in fp32 before the bf16 round trip (its
  *     storage type on the page); RoPE rotates the fp64 normalised value and
  *     rounds once to bf16;
@@ -68,6 +80,12 @@
 #define IDX_NOPE 64     /* indexer dims before the RoPE dims */
 #define IDX_RECORD 128  /* indexer fp8 bytes per token */
 #define IDX_SCALE 4     /* one fp32 scale per token */
+#define FP4_BLOCK 32    /* MXFP4 quantisation block */
+#define FP4_RECORD 64   /* packed E2M1 bytes per token, two dims a byte */
+#define FP4_SCALES 4    /* one UE8M0 byte per block */
+#define FP4_MAX 6.0
+
+enum { FMT_SPARSE = 0, FMT_INDEXER_FP8 = 1, FMT_INDEXER_MXFP4 = 2 };
 
 /* ------------------------------------------------------------------------
  * Number formats, from their definitions.
@@ -136,6 +154,36 @@ double oracle_e4m3_value(uint8_t c) {
   return s ? -v : v;
 }
 
+/*
+ * OCP 4-bit floating point, E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit.  Exponent
+ * field 0 holds the subnormals m * 0.5; field E > 0 holds (1 + m/2) * 2^(E-1).  So the eight
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Round |x| (finite) to nearest, ties to the even
+ * code; magnitudes beyond 6 saturate to 6.  The sign bit 0x8 follows the sign of x.
+ */
+uint8_t oracle_e2m1_code(double x) {
+  double a = fabs(x);
+  unsigned sign = signbit(x) ? 0x8u : 0x0u;
+  unsigned code;
+  if (a < 1.0) {
+    /* subnormal step 0.5; rint = 2 is the smallest normal, 1.0 */
+    code = (unsigned)rint(a * 2.0);
+  } else {
+    int k;
+    frexp(a, &k);
+    int E = k - 1;                                          /* a in [2^E, 2^(E+1)) */
+    double m = rint((ldexp(a, -E) - 1.0) * 2.0);            /* 1-bit mantissa, RNE */
+    if (m == 2.0) { m = 0.0; E += 1; }
+    code = E > 2 ? 7u : (((unsigned)(E + 1) << 1) | (unsigned)m);
+  }
+  return (uint8_t)(sign | code);
+}
+
+double oracle_e2m1_value(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
 /* Exact ceil(log2(r)) for a positive finite r. */
 int oracle_ceil_log2(double r) {
   int k;
@@ -157,13 +205,28 @@ int oracle_ue8m0_exponent(double absmax) {
   return oracle_ceil_log2(raw);
 }
 
+/*
+ * UE8M0 exponent of one MXFP4 block from its absmax (of bf16 values): absmax is floored at
+ * 6 * 2^-126, multiplied by fl32(1/6) in fp32, e = ceil(log2(that product)), and e is clamped
+ * to [-127, 127].  As above, the fp64 product of the two fp32 values is exact, so one cast
+ * to float is the fp32 multiply.
+ */
+int oracle_mxfp4_exponent(double absmax) {
+  double floor_ = ldexp(FP4_MAX, -126);
+  double A = absmax > floor_ ? absmax : floor_;
+  double inv = (double)(float)(1.0 / FP4_MAX);
+  double raw = (double)(float)(A * inv);
+  int e = oracle_ceil_log2(raw);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 /* ------------------------------------------------------------------------
  * One token.
  * --------------------------------------------------------------------- */
 
 typedef struct {
   int64_t head;                                /* 512 (sparse attention) or 128 (indexer) */
-  int indexer;                                 /* 0: sparse-attention k_cache, 1: indexer fp8 */
+  int indexer;                                 /* FMT_*: the cache format */
   int64_t cr, overlap, state_width;            /* compress ratio, 0/1, score column offset */
   const float* state;
   int64_t n_state_blocks, state_bs, s0, s1;    /* element strides */
@@ -235,6 +298,52 @@ static int oracle_indexer_insert(const oracle_args* a, int64_t t, int64_t pos, d
   return ST_WRITTEN;
 }
 
+/*
+ * MXFP4 indexer record of token t from its normalised values n[0..128): the same RoPE as the
+ * FP8 record, every rotated value (held in fp32) through bf16, then four blocks of 32
+ * consecutive dims, each with its own UE8M0 exponent, two E2M1 codes a byte (even dim in the
+ * low nibble).  On return n holds the rotated values (before their bf16 round trip), in fp64.
+ */
+static int oracle_indexer_mxfp4_insert(const oracle_args* a, int64_t t, int64_t pos, double* n) {
+  int64_t kv_slot = a->kv_slot_mapping[t];
+  if (kv_slot < 0) return ST_NO_SLOT;
+  int64_t kblk = kv_slot / a->kv_bs, koff = kv_slot % a->kv_bs;
+  if (kblk >= a->n_kv_blocks) return ST_BAD_INDEX;
+  int64_t P = (pos / a->cr) * a->cr;
+  if (P >= a->cs_rows) return ST_BAD_INDEX;
+
+  /* RoPE in fp64 on the normalised pairs (64+2m, 65+2m), m < 32; dims 0..63 unchanged */
+  const float* cs = a->cos_sin + P * a->cs_stride;
+  double r[IDX_HEAD];
+  for (int j = 0; j < IDX_NOPE; ++j) r[j] = n[j];
+  for (int m = 0; m < HALF_ROPE; ++m) {
+    double x = n[IDX_NOPE + 2 * m], y = n[IDX_NOPE + 2 * m + 1];
+    double C = cs[m], S = cs[HALF_ROPE + m];
+    r[IDX_NOPE + 2 * m] = x * C - y * S;
+    r[IDX_NOPE + 2 * m + 1] = y * C + x * S;
+  }
+
+  uint8_t* blockp = a->k_cache + kblk * a->kv_stride0;
+  uint8_t* data = blockp + koff * FP4_RECORD;
+  uint8_t* scales = blockp + a->kv_bs * FP4_RECORD + koff * FP4_SCALES;
+  double u[IDX_HEAD];
+  for (int j = 0; j < IDX_HEAD; ++j) u[j] = oracle_bf16_value(oracle_bf16_bits((double)(float)r[j]));
+  for (int g = 0; g < IDX_HEAD / FP4_BLOCK; ++g) {
+    double amax = 0.0;
+    for (int j = g * FP4_BLOCK; j < (g + 1) * FP4_BLOCK; ++j)
+      if (fabs(u[j]) > amax) amax = fabs(u[j]);
+    int e = oracle_mxfp4_exponent(amax);
+    for (int j = g * FP4_BLOCK; j < (g + 1) * FP4_BLOCK; j += 2) {
+      uint8_t lo = oracle_e2m1_code(ldexp(u[j], -e));
+      uint8_t hi = oracle_e2m1_code(ldexp(u[j + 1], -e));
+      data[j / 2] = (uint8_t)(lo | (hi << 4));
+    }
+    scales[g] = (uint8_t)(e + 127);
+  }
+  for (int j = 0; j < IDX_HEAD; ++j) n[j] = r[j];
+  return ST_WRITTEN;
+}
+
 static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn, double* n) {
   const int64_t CR = a->cr;
   /* gate */
@@ -294,7 +403,8 @@ static int oracle_token(const oracle_args* a, int64_t t, double* c, double* absn
   for (int j = 0; j < H; ++j) ss += c[j] * c[j];
   double rrms = 1.0 / sqrt(ss / H + a->eps);
   for (int j = 0; j < H; ++j) n[j] = c[j] * rrms * (double)a->rms_w[j];
-  if (a->indexer) return oracle_indexer_insert(a, t, pos, n);
+  if (a->indexer == FMT_INDEXER_MXFP4) return oracle_indexer_mxfp4_insert(a, t, pos, n);
+  if (a->indexer == FMT_INDEXER_FP8) return oracle_indexer_insert(a, t, pos, n);
 
   int64_t kv_slot = a->kv_slot_mapping[t];
   if (kv_slot < 0) return ST_NO_SLOT;
@@ -388,6 +498,7 @@ int oracle_compress_store_fmt(
       !cos_sin || !k_cache || !kv_slot_mapping || state_bs < 1 || kv_bs < 1 || T < 0 ||
       t_lo < 0 || t_hi > T || t_lo > t_hi || nthreads < 1 || compress_ratio < 1 ||
       (overlap != 0 && overlap != 1) || (1 + overlap) * compress_ratio > MAX_ROWS ||
+      indexer < FMT_SPARSE || indexer > FMT_INDEXER_MXFP4 ||
       (indexer ? head != IDX_HEAD : head != HEAD) || state_width < (1 + overlap) * head)
     return -1;
   oracle_args a = {head, indexer, compress_ratio, overlap, state_width, state, n_state_blocks, state_bs, s0, s1, block_table, bt_rows, bt_cols,
@@ -461,4 +572,10 @@ void oracle_e4m3_code_array(const double* x, uint8_t* out, int64_t n) {
 }
 void oracle_ue8m0_exponent_array(const double* absmax, int32_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_ue8m0_exponent(absmax[i]);
+}
+void oracle_e2m1_code_array(const double* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_code(x[i]);
+}
+void oracle_mxfp4_exponent_array(const double* absmax, int32_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_mxfp4_exponent(absmax[i]);
 }

@@ -23,6 +23,11 @@ is checked by ``compare_indexer`` with the same rules: untouched bytes bit-exact
 bit-exact unless the block's absmax sits on a knife edge (then excused and compared by
 dequantised value); codes within 1 step on at most 0.1% of the elements; the debug pooled
 vector within the compressed tolerance.
+
+The indexer's MXFP4 cache (64 bytes of E2M1 codes, two a byte with the even dim in the low
+nibble, then four UE8M0 bytes, one per 32-dim block) is checked by ``compare_indexer_mxfp4``
+with the same rules.  Its knife edge is the bf16 midpoint 1.50390625 * 2^k above 1.5 * 2^k,
+where absmax / 6 crosses a power of two.
 """
 
 from __future__ import annotations
@@ -112,12 +117,12 @@ def rope_band(wl, orc, t: int) -> tuple[np.ndarray, np.ndarray]:
     return z, tol
 
 
-def knife_edge(absmax: float) -> bool:
+def knife_edge(absmax: float, knife: float = KNIFE) -> bool:
     if absmax <= 0:
         return False
-    k = np.floor(np.log2(absmax / KNIFE))
+    k = np.floor(np.log2(absmax / knife))
     for kk in (k - 1, k, k + 1):
-        edge = KNIFE * 2.0 ** kk
+        edge = knife * 2.0 ** kk
         if abs(absmax - edge) <= KNIFE_REL * edge:
             return True
     return False
@@ -141,6 +146,9 @@ def compare(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
     """Compare the GPU k_cache bytes (the whole underlying buffer of the workload's
     k_cache view) with the oracle's, on ``tokens`` (indices; default all) and check
     that every byte outside the written records equals the initial buffer."""
+    if getattr(wl, "indexer_fp4", False):
+        return compare_indexer_mxfp4(wl, gpu_kc_base, orc, tokens, gpu_compressed,
+                                     initial_kc_base)
     if getattr(wl, "indexer", False):
         return compare_indexer(wl, gpu_kc_base, orc, tokens, gpu_compressed, initial_kc_base)
     kc = wl.k_cache
@@ -320,6 +328,107 @@ def compare_indexer(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compresse
         n_diff1 += int((d == 1).sum())
         if np.any(d > 1):
             rep["failures"].append(f"token {t}: code differs by {int(d.max())}")
+    rep["written"] = int(written[toks].sum())
+    rep["scale_mismatch"] = n_scale_bad
+    rep["excused_blocks"] = n_excused
+    rep["code_diff1"] = n_diff1
+    rep["code_diff1_frac"] = (n_diff1 / n_code) if n_code else 0.0
+    rep["code_fail"] = rep["code_diff1_frac"] > CODE_FRAC_MAX
+    if rep["code_fail"]:
+        rep["failures"].append(f"code diff-1 fraction {rep['code_diff1_frac']:.2e} > 1e-3")
+    if gpu_compressed is not None and orc.compressed is not None:
+        _compressed_check(wl, orc, toks, gpu_compressed, rep)
+    return rep
+
+
+FP4_RECORD = 64
+FP4_SCALES = 4
+FP4_BLOCK = 32
+KNIFE_FP4 = 1.50390625
+
+
+def fp4_offsets(slot: int, bs: int, stride0: int):
+    blk, off = slot // bs, slot % bs
+    return blk * stride0 + off * FP4_RECORD, blk * stride0 + bs * FP4_RECORD + off * FP4_SCALES
+
+
+def e2m1_unpack(b: np.ndarray) -> np.ndarray:
+    """128 codes from 64 bytes: dim 2p in the low nibble of byte p, dim 2p+1 in the high."""
+    out = np.empty(2 * b.size, np.uint8)
+    out[0::2] = b & 0xF
+    out[1::2] = b >> 4
+    return out
+
+
+def e2m1_ord(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int32)
+    mag = c & 7
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_val(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    e, m = (c >> 1) & 3, c & 1
+    v = np.where(e == 0, 0.5 * m, (1 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(c & 8, -v, v)
+
+
+def compare_indexer_mxfp4(wl, gpu_kc_base: np.ndarray, orc, tokens=None, gpu_compressed=None,
+                          initial_kc_base: np.ndarray | None = None) -> Report:
+    """``compare`` for the indexer's MXFP4 cache ([bs*64 packed codes][bs*4 UE8M0] blocks)."""
+    kc = wl.k_cache
+    bs = kc.shape[1]
+    stride0 = kc.strides[0]
+    init = wl.k_cache_base if initial_kc_base is None else initial_kc_base
+    assert gpu_kc_base.shape == init.shape
+    T = wl.num_tokens
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    written = wl.written_mask()
+    rep = Report(tokens=int(len(toks)), failures=[])
+
+    wmask = np.zeros(init.size, dtype=bool)
+    for s_ in wl.kv_slot_mapping[written]:
+        rec, scl = fp4_offsets(int(s_), bs, stride0)
+        wmask[rec:rec + FP4_RECORD] = True
+        wmask[scl:scl + FP4_SCALES] = True
+    diff = (gpu_kc_base != init) & ~wmask
+    rep["untouched_mismatch"] = int(diff.sum())
+    if rep["untouched_mismatch"]:
+        rep["failures"].append(f"{rep['untouched_mismatch']} bytes outside written records changed")
+
+    n_code = n_diff1 = n_scale_bad = n_excused = 0
+    for t in toks:
+        t = int(t)
+        if not written[t]:
+            continue
+        rec, scl = fp4_offsets(int(wl.kv_slot_mapping[t]), bs, stride0)
+        g_codes = e2m1_unpack(gpu_kc_base[rec:rec + FP4_RECORD])
+        o_codes = e2m1_unpack(orc.k_cache_base[rec:rec + FP4_RECORD])
+        g_sc = gpu_kc_base[scl:scl + FP4_SCALES]
+        o_sc = orc.k_cache_base[scl:scl + FP4_SCALES]
+        for g in range(FP4_SCALES):
+            sl = slice(FP4_BLOCK * g, FP4_BLOCK * (g + 1))
+            gc, oc = g_codes[sl], o_codes[sl]
+            n_code += FP4_BLOCK
+            if g_sc[g] != o_sc[g]:
+                # the block's fp64 absmax (orc.normed holds the rotated values)
+                amax = float(np.abs(orc.normed[t][sl]).max()) if orc.normed is not None else 0.0
+                if knife_edge(amax, KNIFE_FP4):
+                    n_excused += 1
+                    gv = e2m1_val(gc) * 2.0 ** (int(g_sc[g]) - 127)
+                    ov = e2m1_val(oc) * 2.0 ** (int(o_sc[g]) - 127)
+                    step = 2.0 * 2.0 ** (max(int(g_sc[g]), int(o_sc[g])) - 127)
+                    if np.any(np.abs(gv - ov) > step):
+                        rep["failures"].append(f"token {t} block {g}: excused block values differ")
+                    continue
+                n_scale_bad += 1
+                rep["failures"].append(
+                    f"token {t} block {g}: scale byte {int(g_sc[g])} != {int(o_sc[g])}")
+                continue
+            d = np.abs(e2m1_ord(gc) - e2m1_ord(oc))
+            n_diff1 += int((d == 1).sum())
+            if np.any(d > 1):
+                rep["failures"].append(f"token {t} block {g}: code differs by {int(d.max())}")
     rep["written"] = int(written[toks].sum())
     rep["scale_mismatch"] = n_scale_bad
     rep["excused_blocks"] = n_excused

@@ -206,6 +206,7 @@ class Workload:
     compress_ratio: int = 128
     overlap: int = 0
     indexer: bool = False
+    indexer_fp4: bool = False   # indexer cache in MXFP4 ([bs*64 packed][bs*4 UE8M0] blocks)
 
     @property
     def num_tokens(self) -> int:
@@ -464,15 +465,22 @@ INDEXER_ROW = 4 * INDEXER_HEAD   # kv (2 x 128) | score (2 x 128)
 INDEXER_RECORD = 128             # fp8 bytes per token
 INDEXER_SCALE = 4                # one fp32 scale per token
 INDEXER_SLOT = INDEXER_RECORD + INDEXER_SCALE
+INDEXER_FP4_RECORD = 64          # 128 E2M1 codes, two a byte
+INDEXER_FP4_SCALES = 4           # one UE8M0 byte per 32-dim block
+INDEXER_FP4_SLOT = INDEXER_FP4_RECORD + INDEXER_FP4_SCALES
 
 
-def alloc_indexer_cache(n_blocks: int, bs: int, block_pad: int = 0, fill: int = FILL):
+def alloc_indexer_cache(n_blocks: int, bs: int, block_pad: int = 0, fill: int = FILL,
+                        fp4: bool = False):
     """uint8 indexer k_cache view ``[n_blocks, bs, 132]``: each block holds ``bs`` records of 128
-    fp8 bytes, then ``bs`` fp32 scales; block stride ``bs*132 + block_pad`` bytes."""
-    stride0 = bs * INDEXER_SLOT + block_pad
+    fp8 bytes, then ``bs`` fp32 scales; block stride ``bs*132 + block_pad`` bytes.  ``fp4``:
+    the MXFP4 cache ``[n_blocks, bs, 68]``, ``bs`` records of 64 packed bytes, then ``bs`` x 4
+    UE8M0 bytes."""
+    slot = INDEXER_FP4_SLOT if fp4 else INDEXER_SLOT
+    stride0 = bs * slot + block_pad
     base = np.full(n_blocks * stride0, fill, dtype=np.uint8)
     view = np.lib.stride_tricks.as_strided(
-        base, shape=(n_blocks, bs, INDEXER_SLOT), strides=(stride0, INDEXER_SLOT, 1))
+        base, shape=(n_blocks, bs, slot), strides=(stride0, slot, 1))
     return base, view
 
 
@@ -480,11 +488,12 @@ def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k
                          table_cols: int, kv_bs: int, kv_blocks: int, cs_rows: int,
                          state_bs: int = 8, score_std: float = math.sqrt(2.0), k_min: int = 1,
                          kc_block_pad: int = 0, row_pad: int = 0, block_pad: int = 0,
-                         threads: int | None = None) -> Workload:
+                         threads: int | None = None, fp4: bool = False) -> Workload:
     """The indexer's compressor: one boundary token per request at position 4k-1, k ~
     U{k_min..k_max}, an 8-row overlapping window as for C4, head 128 (state rows [S, state_bs,
     512]: kv 2 x 128 | score 2 x 128).  Windows get state blocks of their own; kv slots are a
-    seeded injection into ``kv_blocks * kv_bs`` slots of a [B, kv_bs, 132] indexer cache."""
+    seeded injection into ``kv_blocks * kv_bs`` slots of a [B, kv_bs, 132] indexer cache
+    (``fp4``: the [B, kv_bs, 68] MXFP4 cache; the inputs are the same)."""
     T = num_tokens
     if T > kv_blocks * kv_bs:
         raise ValueError("not enough kv slots")
@@ -508,13 +517,13 @@ def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k
     state_base, state = alloc_state(n_blocks, row_width=INDEXER_ROW, rows_per_block=state_bs,
                                     row_pad=row_pad, block_pad=block_pad)
     fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * INDEXER_HEAD)
-    kc_base, kc = alloc_indexer_cache(kv_blocks, kv_bs, kc_block_pad)
+    kc_base, kc = alloc_indexer_cache(kv_blocks, kv_bs, kc_block_pad, fp4=fp4)
     w = (1.0 + 0.1 * normal(INDEXER_HEAD, seed, 3).astype(np.float64)).astype(np.float32)
     wl = Workload(name, state, bt, np.arange(T, dtype=np.int32), positions.astype(np.int32),
                   slot_mapping, w, 1e-6, rope_table(cs_rows), kc, kv_slots, seed, state_base,
-                  kc_base, compress_ratio=C4_RATIO, overlap=1, indexer=True)
-    wl.info = {"kind": "indexer decode", "tokens": T, "pool_blocks": n_blocks,
-               "state_bs": state_bs}
+                  kc_base, compress_ratio=C4_RATIO, overlap=1, indexer=True, indexer_fp4=fp4)
+    wl.info = {"kind": "indexer mxfp4 decode" if fp4 else "indexer decode", "tokens": T,
+               "pool_blocks": n_blocks, "state_bs": state_bs}
     return wl
 
 

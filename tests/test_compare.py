@@ -125,3 +125,75 @@ def test_indexer_flags_code_scale_and_stray_bytes(icase):
     body[rec] ^= 0xFF
     rep = compare(wl, body, orc)
     assert not rep.ok() and rep["untouched_mismatch"] == 1
+
+
+# ---------------------------------------------------------------- indexer MXFP4 cache
+
+@pytest.fixture(scope="module")
+def fcase():
+    wl = synth.indexer_decode_batch("fcmp", 8, 12, 60, 8, 8, kv_bs=4, kv_blocks=8, cs_rows=64,
+                                    fp4=True)
+    return wl, oracle.run(wl, 2)
+
+
+def fplanted(wl, orc, fn):
+    from oracle.compare import fp4_offsets
+    body = orc.k_cache_base.copy()
+    rec, scl = fp4_offsets(int(wl.kv_slot_mapping[5]), wl.k_cache.shape[1],
+                           wl.k_cache.strides[0])
+    fn(body, rec, scl)
+    return compare(wl, body, orc)
+
+
+def test_mxfp4_identical_output_passes(fcase):
+    wl, orc = fcase
+    rep = compare(wl, orc.k_cache_base.copy(), orc,
+                  gpu_compressed=orc.compressed.astype(np.float32))
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 12
+
+
+def _nudge(c, by):
+    """E2M1 code c moved by ``by`` steps in magnitude (within 0..7), sign kept."""
+    mag = c & 7
+    mag = mag - by if mag >= by else mag + by
+    return (c & 8) | mag
+
+
+def test_mxfp4_flags_codes_scales_and_stray_bytes(fcase):
+    wl, orc = fcase
+
+    def low_two(b, rec, scl):      # the even dim of byte 3 off by two steps
+        b[rec + 3] = (b[rec + 3] & 0xF0) | _nudge(int(b[rec + 3]) & 0xF, 2)
+
+    def high_two(b, rec, scl):     # the odd dim of byte 40 off by two steps
+        b[rec + 40] = (b[rec + 40] & 0x0F) | (_nudge(int(b[rec + 40]) >> 4, 2) << 4)
+
+    def one_step(b, rec, scl):     # one step on one dim: within the code tolerance
+        b[rec + 7] = (b[rec + 7] & 0xF0) | _nudge(int(b[rec + 7]) & 0xF, 1)
+
+    def scale(b, rec, scl):
+        b[scl + 2] += 1
+
+    assert not fplanted(wl, orc, low_two).ok()
+    assert not fplanted(wl, orc, high_two).ok()
+    rep = fplanted(wl, orc, one_step)
+    assert rep.ok() and rep["code_diff1"] == 1, rep.summary()
+    assert not fplanted(wl, orc, scale).ok()
+    from oracle.compare import fp4_offsets
+    free = sorted(set(range(32)) - set(int(x) for x in wl.kv_slot_mapping))[0]
+    rec, scl = fp4_offsets(free, wl.k_cache.shape[1], wl.k_cache.strides[0])
+    for off in (rec + 63, scl):
+        body = orc.k_cache_base.copy()
+        body[off] ^= 0xFF
+        rep = compare(wl, body, orc)
+        assert not rep.ok() and rep["untouched_mismatch"] == 1
+
+
+def test_mxfp4_knife_edge_excuses_a_flipped_scale():
+    """A block whose fp64 absmax sits on the bf16 midpoint 1.50390625 * 2^k may come out with
+    either exponent; the checker excuses a flipped scale there when the dequantised values agree
+    within one step, and flags it elsewhere."""
+    from oracle.compare import knife_edge, KNIFE_FP4
+    assert knife_edge(1.50390625 * 4, KNIFE_FP4) and knife_edge(1.50390625 * 2 ** -3, KNIFE_FP4)
+    assert not knife_edge(1.5 * 4, KNIFE_FP4) and not knife_edge(1.507 * 4, KNIFE_FP4)
