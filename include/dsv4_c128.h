@@ -1,7 +1,7 @@
 /*
  * dsv4_c128.h -- C ABI of the DeepSeek-V4 sparse-attention compress-store path on
  * MI355X (gfx950): the C128 compressor (below), the C4 compressor (dsv4_c4_*) and the
- * indexer's FP8 compressor (dsv4_indexer_*).
+ * indexer's compressor with its FP8 and MXFP4 caches (dsv4_indexer_*).
  *
  * What it computes (vLLM API page "fused_compress_quant_cache", DeepSeek-V4
  * common ops: the sparse-attention fused kernel
@@ -311,6 +311,48 @@ int dsv4_indexer_validate(const dsv4_tensor* state_cache, const dsv4_tensor* blo
                           const dsv4_tensor* kv_slot_mapping);
 
 /*
+ * The indexer's compressor with the MXFP4 cache (vLLM fused_compress_quant_cache page, kernel
+ * `_fused_kv_compress_norm_rope_insert_indexer_mxfp4_attn` and its MXFP4-format notes).  Steps
+ * 1-3 are those of dsv4_indexer_compress_store; then:
+ *   4. every rotated value (held in fp32; dims 0..63 unrotated) is rounded to bf16;
+ *   5. four blocks of 32 consecutive dims: absmax (floor 6 * 2^-126), e = ceil(log2(absmax *
+ *      fl32(1/6))) computed on the fp32 product, clamped to [-127, 127]; codes = E2M1(x * 2^-e),
+ *      rounded to nearest with ties to the even code, sign kept, saturating at 6 (the page
+ *      does not print its conversion; this is the OCP E2M1 format's round to nearest even);
+ *   6. if kv_slot_mapping[t] >= 0: with bs = k_cache.shape[1], blk = slot / bs, off = slot %
+ *      bs, 64 bytes at blk*k_cache.stride[0] + off*64, byte p holding dim 2p in its low
+ *      nibble and dim 2p+1 in its high nibble, and the 4 scale bytes e + 127 (one per block)
+ *      at blk*k_cache.stride[0] + bs*64 + off*4.
+ *
+ *   k_cache         u8  [B, bs, 68]    stride[2] == 1, stride[1] == 68, stride[0] >= bs*68 and
+ *                                      a multiple of 4; data 4-byte aligned
+ *   every other argument, the gate, the range checks and the errors as for
+ *   dsv4_indexer_compress_store; compressed_out of the debug entry point is [T, 128] fp32.
+ */
+int dsv4_indexer_mxfp4_compress_store(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    void* stream);
+
+/* dsv4_indexer_mxfp4_compress_store that also writes the fp32 pooled vectors ([T, 128],
+ * 16-byte aligned; rows of tokens that do not pass the gate are left unchanged; may be NULL). */
+int dsv4_indexer_mxfp4_compress_store_debug(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    float* compressed_out, void* stream);
+
+/* Host-only validation of MXFP4 indexer descriptors (as dsv4_c128_validate). */
+int dsv4_indexer_mxfp4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping);
+
+/*
  * Host-only validation of the descriptors, exactly as the compute entry
  * points do it.  Makes no HIP call and dereferences no `data` pointer, so it
  * runs without a GPU.  Returns DSV4_OK or the DSV4_ERR_* the compute entry
@@ -330,6 +372,13 @@ int dsv4_c128_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_
  * gfx950).
  */
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/*
+ * The E2M1 encoder of the MXFP4 cache as the kernel runs it, applied to n fp32 values:
+ * out[i] = code(in[i]) in the low nibble (bit 3 the sign), the high nibble 0.  Device pointers.
+ * For exhaustive tests of the encoder.
+ */
+int dsv4_e2m1_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* dsv4_last_error(void);

@@ -1,6 +1,6 @@
 """MI355X (gfx950) compress-store for the DeepSeek-V4 compressors: C128 (single pass, staged
 schedule from 2048 tokens, small-batch fan-out, compacted varlen schedule), C4 and the
-indexer's FP8 compressor.
+indexer's compressor with its FP8 and MXFP4 caches.
 
 Thin ctypes binding of ``libdsv4_c128.so`` (C ABI in ``include/dsv4_c128.h``).
 The binding only marshals torch tensors into descriptors and passes torch's
@@ -113,6 +113,16 @@ def library():
         lib.dsv4_indexer_compress_store_debug.restype = ctypes.c_int
         lib.dsv4_indexer_validate.argtypes = args10
         lib.dsv4_indexer_validate.restype = ctypes.c_int
+        lib.dsv4_indexer_mxfp4_compress_store.argtypes = args10 + [ctypes.c_void_p]
+        lib.dsv4_indexer_mxfp4_compress_store.restype = ctypes.c_int
+        lib.dsv4_indexer_mxfp4_compress_store_debug.argtypes = args10 + [ctypes.c_void_p,
+                                                                        ctypes.c_void_p]
+        lib.dsv4_indexer_mxfp4_compress_store_debug.restype = ctypes.c_int
+        lib.dsv4_indexer_mxfp4_validate.argtypes = args10
+        lib.dsv4_indexer_mxfp4_validate.restype = ctypes.c_int
+        lib.dsv4_e2m1_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p]
+        lib.dsv4_e2m1_encode.restype = ctypes.c_int
         lib.dsv4_c4_validate.argtypes = args10
         lib.dsv4_c4_validate.restype = ctypes.c_int
         lib.dsv4_c128_validate.argtypes = args10
@@ -315,6 +325,35 @@ def indexer_compress_store(state_cache, block_table, token_to_req, positions, sl
                                                        out_ptr, s))
 
 
+def indexer_mxfp4_compress_store(state_cache, block_table, token_to_req, positions,
+                                 slot_mapping, rms_w, eps, cos_sin, k_cache, kv_slot_mapping,
+                                 compressed_out=None, stream: int | None = None) -> None:
+    """The indexer's compressor with the MXFP4 cache (k_cache u8 [B, bs, 68]: bs records of 64
+    bytes of E2M1 codes, two a byte, then bs x 4 UE8M0 bytes); inputs as for
+    ``indexer_compress_store``."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    dev = _require_cuda(ts + ([compressed_out] if compressed_out is not None else []))
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 128)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 128] tensor")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_indexer_mxfp4_compress_store_debug(*refs[:6], float(eps), *refs[6:],
+                                                             out_ptr, s))
+
+
+def indexer_mxfp4_validate(state_cache, block_table, token_to_req, positions, slot_mapping,
+                           rms_w, eps, cos_sin, k_cache, kv_slot_mapping) -> int:
+    """Host-only validation of MXFP4 indexer descriptors; returns the status code."""
+    ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping)
+    _, refs = _descriptors(ts)
+    return library().dsv4_indexer_mxfp4_validate(*refs[:6], float(eps), *refs[6:])
+
+
 def indexer_validate(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
                      cos_sin, k_cache, kv_slot_mapping) -> int:
     """Host-only validation of indexer descriptors; returns the status code."""
@@ -345,9 +384,21 @@ def e4m3_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
     return out
 
 
+def e2m1_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
+    """The kernel's E2M1 encoder (nearest, ties to even, saturating at 6, sign in bit 3) on a
+    float32 device tensor; returns one uint8 code per value."""
+    if x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a float32 device tensor")
+    x = x.contiguous()
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = _stream(x.device) if stream is None else stream
+    _check(library().dsv4_e2m1_encode(x.data_ptr(), out.data_ptr(), x.numel(), s))
+    return out
+
+
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
            "fanout_workspace",
            "compress_store_varlen", "varlen_workspace_bytes", "c4_compress_store", "c4_validate",
-           "indexer_compress_store", "indexer_validate",
-           "validate", "e4m3_encode", "last_error",
+           "indexer_compress_store", "indexer_validate", "indexer_mxfp4_compress_store",
+           "indexer_mxfp4_validate", "validate", "e4m3_encode", "e2m1_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

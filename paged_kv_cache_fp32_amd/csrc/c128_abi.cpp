@@ -84,6 +84,8 @@ constexpr StateLayout kC4Layout{"C4", 4 * dsv4::kHead, 0, 1, dsv4::kHead, dsv4::
 // Indexer (head 128, overlapping window of ratio 4): kv 2 x 128 | score 2 x 128; 128 fp8
 // bytes + one fp32 scale per token.
 constexpr StateLayout kIndexerLayout{"indexer", 4 * 128, 0, 1, 128, 128 + 4, 4};
+// The same with the MXFP4 cache: 64 bytes of E2M1 codes + 4 UE8M0 bytes per token.
+constexpr StateLayout kIndexerMxfp4Layout{"indexer MXFP4", 4 * 128, 0, 1, 128, 64 + 4, 4};
 
 int validate_all(const dsv4_tensor* state, const dsv4_tensor* bt, const dsv4_tensor* t2r,
                  const dsv4_tensor* pos, const dsv4_tensor* slot, const dsv4_tensor* w, float eps,
@@ -416,6 +418,59 @@ int dsv4_indexer_compress_store(const dsv4_tensor* state_cache, const dsv4_tenso
   return dsv4_indexer_compress_store_debug(state_cache, block_table, token_to_req, positions,
                                            slot_mapping, rms_w, eps, cos_sin, k_cache,
                                            kv_slot_mapping, nullptr, stream);
+}
+
+int dsv4_indexer_mxfp4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+                                const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+                                const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w,
+                                float eps, const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache,
+                                const dsv4_tensor* kv_slot_mapping) {
+  return validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, eps,
+                      cos_sin, k_cache, kv_slot_mapping, nullptr, kIndexerMxfp4Layout);
+}
+
+int dsv4_indexer_mxfp4_compress_store_debug(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    float* compressed_out, void* stream) {
+  dsv4::C128Params p;
+  int32_t sbs = 0;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p, kIndexerMxfp4Layout, &sbs);
+  if (rc) return rc;
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  p.compressed_out = compressed_out;
+  hipError_t err =
+      dsv4::launch_indexer_mxfp4_compress_store(p, sbs, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  return DSV4_OK;
+}
+
+int dsv4_indexer_mxfp4_compress_store(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    void* stream) {
+  return dsv4_indexer_mxfp4_compress_store_debug(state_cache, block_table, token_to_req,
+                                                 positions, slot_mapping, rms_w, eps, cos_sin,
+                                                 k_cache, kv_slot_mapping, nullptr, stream);
+}
+
+int dsv4_e2m1_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return fail(DSV4_ERR_SHAPE, "n must be >= 0");
+  if (n == 0) return DSV4_OK;
+  if (!in || !out) return fail(DSV4_ERR_NULL, "in/out is NULL");
+  hipError_t err = dsv4::launch_e2m1_encode(in, out, n, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return DSV4_OK;
 }
 
 int dsv4_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -41,6 +41,10 @@ hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipSt
 // Indexer FP8 compressor (head 128, ratio 4, overlapping window): indexer_kernel.hip.
 hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,
                                          hipStream_t stream);
+// The same compressor with the MXFP4 cache, and its E2M1 encoder on an array: indexer_kernel.hip.
+hipError_t launch_indexer_mxfp4_compress_store(const C128Params& p, int32_t state_bs,
+                                               hipStream_t stream);
+hipError_t launch_e2m1_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace dsv4

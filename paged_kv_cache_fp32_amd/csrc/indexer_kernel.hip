@@ -11,11 +11,18 @@
 // x * 2^-e, and the scale 2^e as one fp32.  A cache block holds bs records of 128 code bytes,
 // then bs fp32 scales.
 //
+// The MXFP4 variant (same page, kernel `_fused_kv_compress_norm_rope_insert_indexer_mxfp4_attn`)
+// shares everything up to the rotated, bf16-rounded values, then quantises four blocks of 32
+// consecutive dims: e = ceil(log2(absmax / 6)) (absmax floored at 6 * 2^-126), E2M1 codes of
+// x * 2^-e, two a byte with the even dim in the low nibble, and one UE8M0 byte e + 127 per
+// block.  A cache block holds bs records of 64 bytes, then bs x 4 scale bytes.
+//
 // A state row is kv[0:256] | score[256:512]; a token reads 8 rows x 1 KiB = 8 KiB.
 //
 //  * One wave per token.  Lane l owns columns 2l, 2l+1 (8-byte vectors: each wave-wide load
 //    is a 512-byte contiguous segment of a row), so lanes 32..63 hold exactly the 32 RoPE
-//    pairs, and the RMSNorm sum and the quantisation absmax are single wave reductions.
+//    pairs, and the RMSNorm sum and the quantisation absmax are single wave reductions.  An
+//    MXFP4 block is the 16 lanes 16b..16b+15, and lane l packs byte l of the record.
 //  * A wave takes 1 to 8 consecutive tokens (enough waves for 8 per SIMD first); their gate,
 //    block ids and range checks are resolved up front, one lane per (token, window row).
 //  * Records go to the wave's LDS stage and reach the cache after the wave's last state read,
@@ -40,6 +47,11 @@ constexpr int kIdxSlot = kIdxRecord + kIdxScale;
 constexpr int kIdxWavesPerGroup = 4;
 constexpr int kIdxMaxTokensPerWave = 8;     // 8 tokens x 8 window rows = the 64 lanes
 constexpr int kIdxTargetWaves = 8192;       // 8 waves per SIMD on 256 CUs (57-59 VGPRs)
+constexpr int kFp4Record = 64;              // E2M1 bytes per token, two dims a byte
+constexpr int kFp4Scales = 4;               // one UE8M0 byte per 32-dim block
+constexpr int kFp4Slot = kFp4Record + kFp4Scales;
+constexpr float kFp4AbsmaxFloor = 0x1.8p-124f;  // 6 * 2^-126
+constexpr float kInvFp4Max = 1.0f / 6.0f;       // fl32(1/6)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -54,11 +66,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <bool kDebug>
+// E2M1 code of x in the low nibble: the nearest of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// ties to the even code, beyond 6 saturating to 6; bit 3 is the sign of x.  Each comparison
+// is one midpoint between neighbouring magnitudes: strict where the code below it is the even
+// one, inclusive where the code above it is.
+__device__ __forceinline__ uint32_t e2m1(float x) {
+  const float a = __builtin_fabsf(x);
+  const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <bool kDebug, bool kFp4>
 __global__ void __launch_bounds__(64 * kIdxWavesPerGroup)
     indexer_compress_store_kernel(const C128Params p, int32_t state_bs, int32_t state_bs_log2,
                                   int32_t tokens_per_wave) {
-  __shared__ __align__(16) uint8_t stage_all[kIdxWavesPerGroup][kIdxMaxTokensPerWave * kIdxSlot];
+  constexpr int kSlot = kFp4 ? kFp4Slot : kIdxSlot;
+  __shared__ __align__(16) uint8_t stage_all[kIdxWavesPerGroup][kIdxMaxTokensPerWave * kSlot];
   __shared__ int32_t slot_all[kIdxWavesPerGroup][kIdxMaxTokensPerWave];
 
   const int lane = threadIdx.x & 63;
@@ -156,17 +182,31 @@ __global__ void __launch_bounds__(64 * kIdxWavesPerGroup)
           make_float2(c0, c1);
     if (kv_slot < 0 || kv_slot >= p.n_kv_slots) continue;
 
-    // ---- RoPE (lanes 32..63), then one quantisation block over all 128 dims
+    // ---- RoPE (lanes 32..63), then the quantisation
     const float r0 = rope_lane ? n0 * cosv - n1 * sinv : n0;
     const float r1 = rope_lane ? n1 * cosv + n0 * sinv : n1;
     const float u0 = bf16_round(r0), u1 = bf16_round(r1);
+    if constexpr (kFp4) {
+      // four 32-dim blocks of 16 lanes; lane l writes byte l, lane 16b the scale of block b
+      const float amax = group16_max(__builtin_fmaxf(__builtin_fabsf(u0), __builtin_fabsf(u1)));
+      const float raw = __builtin_fmaxf(amax, kFp4AbsmaxFloor) * kInvFp4Max;
+      const uint32_t rb = __float_as_uint(raw);
+      int e = static_cast<int>((rb >> 23) & 0xffu) - 127 + ((rb & 0x7fffffu) != 0u);
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      const float inv = __builtin_ldexpf(1.0f, -e);
+      uint8_t* rec = stage + k * kSlot;
+      rec[lane] = static_cast<uint8_t>(e2m1(u0 * inv) | (e2m1(u1 * inv) << 4));
+      if ((lane & 15) == 0) rec[kFp4Record + (lane >> 4)] = static_cast<uint8_t>(e + 127);
+      if (lane == 0) slot_of[k] = kv_slot;
+      continue;
+    }
     const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(u0), __builtin_fabsf(u1)));
     const float raw = __builtin_fmaxf(amax, kAbsmaxFloor) * kInvFp8Max;
     const uint32_t rb = __float_as_uint(raw);
     const int e = static_cast<int>((rb >> 23) & 0xffu) - 127 + ((rb & 0x7fffffu) != 0u);
     const float inv = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);  // 2^-e
     const uint32_t codes = e4m3x4(u0 * inv, u1 * inv, 0.0f, 0.0f) & 0xffffu;
-    uint8_t* rec = stage + k * kIdxSlot;
+    uint8_t* rec = stage + k * kSlot;
     *reinterpret_cast<uint16_t*>(rec + col) = static_cast<uint16_t>(codes);
     if (lane == 0) {
       *reinterpret_cast<uint32_t*>(rec + kIdxRecord) = static_cast<uint32_t>(e + 127) << 23;
@@ -182,15 +222,22 @@ __global__ void __launch_bounds__(64 * kIdxWavesPerGroup)
     const int32_t kb = kv_slot / p.kv_bs;
     const int32_t ko = kv_slot - kb * p.kv_bs;
     uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
-    const uint8_t* rec = stage + k * kIdxSlot;
-    if (lane < kIdxRecord / 4)
-      *reinterpret_cast<uint32_t*>(blockp + static_cast<int64_t>(ko) * kIdxRecord + 4 * lane) =
+    const uint8_t* rec = stage + k * kSlot;
+    constexpr int kRec = kFp4 ? kFp4Record : kIdxRecord;  // data bytes; then 4 scale bytes
+    if (lane < kRec / 4)
+      *reinterpret_cast<uint32_t*>(blockp + static_cast<int64_t>(ko) * kRec + 4 * lane) =
           *reinterpret_cast<const uint32_t*>(rec + 4 * lane);
-    else if (lane == kIdxRecord / 4)
-      *reinterpret_cast<uint32_t*>(blockp + static_cast<int64_t>(p.kv_bs) * kIdxRecord +
-                                   static_cast<int64_t>(ko) * kIdxScale) =
-          *reinterpret_cast<const uint32_t*>(rec + kIdxRecord);
+    else if (lane == kRec / 4)
+      *reinterpret_cast<uint32_t*>(blockp + static_cast<int64_t>(p.kv_bs) * kRec +
+                                   static_cast<int64_t>(ko) * 4) =
+          *reinterpret_cast<const uint32_t*>(rec + kRec);
   }
+}
+
+__global__ void __launch_bounds__(256) e2m1_encode_kernel(const float* in, uint8_t* out,
+                                                          int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = static_cast<uint8_t>(e2m1(in[i]));
 }
 
 int indexer_tokens_per_wave(int64_t num_tokens) {
@@ -198,10 +245,8 @@ int indexer_tokens_per_wave(int64_t num_tokens) {
   return static_cast<int>(k < 1 ? 1 : (k > kIdxMaxTokensPerWave ? kIdxMaxTokensPerWave : k));
 }
 
-}  // namespace
-
-hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,
-                                         hipStream_t stream) {
+template <bool kFp4>
+hipError_t launch_indexer(const C128Params& p, int32_t state_bs, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
   const int32_t kpw = indexer_tokens_per_wave(p.num_tokens);
   const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
@@ -210,9 +255,28 @@ hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,
   const dim3 block(64 * kIdxWavesPerGroup);
   const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
   if (p.compressed_out)
-    indexer_compress_store_kernel<true><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
+    indexer_compress_store_kernel<true, kFp4><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
   else
-    indexer_compress_store_kernel<false><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
+    indexer_compress_store_kernel<false, kFp4><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,
+                                         hipStream_t stream) {
+  return launch_indexer<false>(p, state_bs, stream);
+}
+
+hipError_t launch_indexer_mxfp4_compress_store(const C128Params& p, int32_t state_bs,
+                                               hipStream_t stream) {
+  return launch_indexer<true>(p, state_bs, stream);
+}
+
+hipError_t launch_e2m1_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  e2m1_encode_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(in, out, n);
   return hipGetLastError();
 }
 

@@ -55,13 +55,16 @@ class DeviceWorkload:
         """One call; splits None = the plain entry points, else compress_store_ex with that
         split count (0 = automatic) and a workspace of the size it needs; varlen = the
         compacted schedule (compress_store_varlen).  A C4 workload (compress ratio 4) always
-        goes to c4_compress_store, an indexer workload to indexer_compress_store."""
+        goes to c4_compress_store, an indexer workload to indexer_compress_store (or
+        indexer_mxfp4_compress_store for the MXFP4 cache)."""
         comp = None
         indexer = getattr(self.wl, "indexer", False)
         if debug:
             comp = torch.full((self.wl.num_tokens, 128 if indexer else 512), float("nan"),
                               dtype=torch.float32, device=self.state.device)
-        if indexer:
+        if indexer and getattr(self.wl, "indexer_fp4", False):
+            c128.indexer_mxfp4_compress_store(*self.args(), compressed_out=comp)
+        elif indexer:
             c128.indexer_compress_store(*self.args(), compressed_out=comp)
         elif getattr(self.wl, "compress_ratio", 128) == 4:
             c128.c4_compress_store(*self.args(), compressed_out=comp)

@@ -182,7 +182,8 @@ def descriptors_with_tokens(a, T):
 
 @pytest.mark.parametrize("fn,args", [("dsv4_c128_validate", valid_args),
                                      ("dsv4_c4_validate", lambda: c4_args()),
-                                     ("dsv4_indexer_validate", lambda: idx_args())])
+                                     ("dsv4_indexer_validate", lambda: idx_args()),
+                                     ("dsv4_indexer_mxfp4_validate", lambda: fp4_args())])
 def test_token_count_limit(fn, args):
     """DSV4_MAX_TOKENS tokens pass validation; one more is DSV4_ERR_SHAPE with a message that
     names the limit, for every compressor."""
@@ -414,6 +415,61 @@ def test_indexer_layout_errors():
                                     (532, 132, 1))
     assert idx_validate(a) == 0
     assert c4_validate(idx_args()) == -4
+
+
+def fp4_args(T=4, S=16, sbs=8, bs=4):
+    a = idx_args(T=T, S=S, sbs=sbs, bs=bs)
+    a["k_cache"] = torch.zeros(2, bs, 68, dtype=torch.uint8)
+    return a
+
+
+def fp4_validate(a):
+    return c128.indexer_mxfp4_validate(a["state_cache"], a["block_table"], a["token_to_req"],
+                                       a["positions"], a["slot_mapping"], a["rms_w"], a["eps"],
+                                       a["cos_sin"], a["k_cache"], a["kv_slot_mapping"])
+
+
+@pytest.mark.parametrize("sbs", [1, 4, 8, 64])
+def test_indexer_mxfp4_accepts_layout(sbs):
+    assert fp4_validate(fp4_args(sbs=sbs)) == 0, c128.last_error()
+
+
+def test_indexer_mxfp4_layout_errors():
+    """k_cache [B, bs, 68] (64 code bytes + 4 scale bytes) with 4-byte alignment; the FP8
+    indexer's 132-byte slots are rejected, and the MXFP4 cache by the FP8 entry point."""
+    a = fp4_args()
+    a["k_cache"] = torch.zeros(2, 4, 132, dtype=torch.uint8)
+    assert fp4_validate(a) == -4 and "68" in c128.last_error()
+    assert idx_validate(fp4_args()) == -4
+    a = fp4_args()
+    a["k_cache"] = torch.zeros(2 * 4 * 68 + 2, dtype=torch.uint8)[2:].view(2, 4, 68)
+    assert fp4_validate(a) == -6
+    a = fp4_args()
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * 274, dtype=torch.uint8), (2, 4, 68),
+                                    (274, 68, 1))
+    assert fp4_validate(a) == -6
+    a = fp4_args()
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * 276, dtype=torch.uint8), (2, 4, 68),
+                                    (276, 68, 1))
+    assert fp4_validate(a) == 0
+    a = fp4_args()
+    a["k_cache"] = torch.as_strided(torch.zeros(2 * 272, dtype=torch.uint8), (2, 4, 68),
+                                    (268, 68, 1))
+    assert fp4_validate(a) == -5          # stride[0] below bs * 68
+    a = fp4_args()
+    a["rms_w"] = torch.ones(512)
+    assert fp4_validate(a) == -4
+
+
+def test_indexer_mxfp4_rejects_before_any_hip_call():
+    lib = c128.library()
+    a = fp4_args()
+    a["k_cache"] = torch.zeros(2, 4, 132, dtype=torch.uint8)
+    ds = [ctypes.byref(c128.describe(a[k])) for k in ARG_ORDER]
+    assert lib.dsv4_indexer_mxfp4_compress_store(*ds[:6], 1e-6, *ds[6:], None) == -4
+    assert lib.dsv4_e2m1_encode(None, None, 0, None) == 0
+    assert lib.dsv4_e2m1_encode(None, None, -1, None) == -4
+    assert lib.dsv4_e2m1_encode(None, None, 4, None) == -1
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
