@@ -15,6 +15,7 @@ Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
 oracle's time beside each workload: the C128 decode sweep 1..4096 tokens, the
 single-token, decode-batch and varlen-prefill workloads on every entry point
 (plain: single pass or staged; fan-out; compacted), and the C4 and indexer compressors
+(the indexer with its FP8 and its MXFP4 cache)
 (``--sweep-filter REGEX`` keeps matching workloads; ``--mode sweep`` skips the
 large-batch line).  ``--mode copy`` times a plain device-to-device copy (the
 counter-calibration kernel for rocprofv3); ``--mode read`` times streaming and
@@ -65,6 +66,8 @@ C4_TOKEN_BYTES = 8 + 256 + 584
 # the 128-byte record and its 4-byte scale
 IDX_ROW_BYTES = 2 * 128 * 4
 IDX_TOKEN_BYTES = 8 + 256 + 132
+# its MXFP4 cache: a 64-byte record and 4 scale bytes instead
+IDX_FP4_TOKEN_BYTES = 8 + 256 + 68
 
 
 def algorithmic_bytes(wl) -> int:
@@ -73,8 +76,8 @@ def algorithmic_bytes(wl) -> int:
         pos = wl.positions[act].astype(np.int64)
         bs = wl.state.shape[1]
         first = np.maximum(pos - 7, 0)
-        per = (pos - first + 1) * IDX_ROW_BYTES + (pos // bs - first // bs + 1) * 4 + \
-            IDX_TOKEN_BYTES
+        tok = IDX_FP4_TOKEN_BYTES if getattr(wl, "indexer_fp4", False) else IDX_TOKEN_BYTES
+        per = (pos - first + 1) * IDX_ROW_BYTES + (pos // bs - first // bs + 1) * 4 + tok
         return int(per.sum()) + wl.num_tokens * ANY_TOKEN_BYTES + 128 * 4
     if getattr(wl, "compress_ratio", 128) == 4:
         pos = wl.positions[act].astype(np.int64)
@@ -315,7 +318,10 @@ def sweep(args, path):
         """splits None: the single-pass entry point; else compress_store_ex with that split
         count (0 = automatic) and a workspace per window set; varlen: the compacted schedule
         (compress_store_varlen) with a workspace per window set."""
-        if getattr(dws[0].wl, "indexer", False):
+        if getattr(dws[0].wl, "indexer_fp4", False):
+            calls = [(lambda d=d: c128.indexer_mxfp4_compress_store(*d.args(), stream=sid))
+                     for d in dws]
+        elif getattr(dws[0].wl, "indexer", False):
             calls = [(lambda d=d: c128.indexer_compress_store(*d.args(), stream=sid))
                      for d in dws]
         elif getattr(dws[0].wl, "compress_ratio", 128) == 4:
@@ -340,7 +346,8 @@ def sweep(args, path):
         reg, per = time_calls(torch, stream, calls, steps, max(3, len(calls)))
         rec = {"workload": name, "tokens": wl.num_tokens,
                "active_tokens": int(wl.active_mask().sum()), "window_sets": len(dws),
-               "entry": ("indexer" if getattr(wl, "indexer", False) else
+               "entry": ("indexer mxfp4" if getattr(wl, "indexer_fp4", False) else
+                         "indexer" if getattr(wl, "indexer", False) else
                          "c4" if getattr(wl, "compress_ratio", 128) == 4 else
                          "varlen (compacted)" if varlen else
                          ("staged" if wl.num_tokens >= STAGED_MIN_TOKENS else "single pass")
@@ -411,6 +418,7 @@ def sweep(args, path):
     torch.cuda.empty_cache()
     c4_sweep(want, measure, dev)
     indexer_sweep(want, measure, dev)
+    indexer_sweep(want, measure, dev, fp4=True)
     out.close()
 
 
@@ -428,16 +436,18 @@ def c4_slices(wl, T, n_sets):
     return out
 
 
-def indexer_sweep(want, measure, dev):
-    """Indexer compressor: decode batches cut from one 16384-token batch (512 MiB pool)."""
+def indexer_sweep(want, measure, dev, fp4=False):
+    """Indexer compressor: decode batches cut from one 16384-token batch (512 MiB pool); fp4:
+    the same inputs into the MXFP4 cache."""
     import synth
     from synth.device import DeviceWorkload
     sizes = (1, 128, 1024, 4096, 16384)
-    names = [f"indexer decode T={T}" for T in sizes]
+    kind = "indexer mxfp4" if fp4 else "indexer"
+    names = [f"{kind} decode T={T}" for T in sizes]
     if not any(want(n) for n in names):
         return
-    big = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024, 512,
-                                     kv_bs=64, kv_blocks=256, cs_rows=4096)
+    big = synth.indexer_decode_batch(f"{kind} decode T=16384", 1006, 16384, 16384 * 2, 1024,
+                                     512, kv_bs=64, kv_blocks=256, cs_rows=4096, fp4=fp4)
     pool_dev = None
     for T, name in zip(sizes, names):
         if not want(name):
