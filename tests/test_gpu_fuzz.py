@@ -33,9 +33,11 @@ def perturb(wl, rng, ratio):
     wl.kv_slot_mapping[rng.random(T) < rng.uniform(0.0, 0.2)] = -1
 
 
-def draw(case):
+def draw(case, path=None):
+    """A random batch of one path: ``path`` None takes PATHS[case % len(PATHS)]; "mxfp4" is
+    the indexer with its MXFP4 cache."""
     rng = np.random.default_rng(9000 + case)
-    path = PATHS[case % len(PATHS)]
+    path = PATHS[case % len(PATHS)] if path is None else path
     T = int(rng.choice([1, 2, 3, 7, 16, 33, 64, 100, 257]))
     kv_bs = int(rng.choice([1, 2, 5, 16, 64]))
     kv_blocks = -(-2 * T // kv_bs) + 1
@@ -60,10 +62,11 @@ def draw(case):
     cols = -(-4 * k_max // state_bs) + 1
     gen = synth.c4_decode_batch if path == "c4" else synth.indexer_decode_batch
     pad = 8 if path == "c4" else 4
+    fmt = {"fp4": True} if path == "mxfp4" else {}
     wl = gen(f"fuzz {case}", seed, T, T * (-(-8 // state_bs) + 1) + 4, k_max, cols, kv_bs=kv_bs,
              kv_blocks=kv_blocks, cs_rows=4 * k_max + 4, state_bs=state_bs, score_std=score_std,
              row_pad=int(rng.choice([0, 16])), block_pad=int(rng.choice([0, 32])),
-             kc_block_pad=(kc_pad // pad) * pad)
+             kc_block_pad=(kc_pad // pad) * pad, **fmt)
     perturb(wl, rng, 4)
     return path, wl, {}
 
@@ -73,6 +76,17 @@ def test_fuzz(case):
     path, wl, kw = draw(case)
     announce(f"fuzz case {case}: {path} T={wl.num_tokens} kv_bs={wl.k_cache.shape[1]} "
              f"state_bs={wl.state.shape[1]} {kw}")
+    body, comp, guards_ok = run_gpu(wl, debug=True, **kw)
+    assert guards_ok, "k_cache guard bands were written"
+    rep = compare(wl, body, oracle.run(wl, 4), gpu_compressed=comp)
+    assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fuzz_mxfp4(case):
+    path, wl, kw = draw(100 + case, "mxfp4")
+    announce(f"fuzz case {100 + case}: mxfp4 T={wl.num_tokens} kv_bs={wl.k_cache.shape[1]} "
+             f"state_bs={wl.state.shape[1]}")
     body, comp, guards_ok = run_gpu(wl, debug=True, **kw)
     assert guards_ok, "k_cache guard bands were written"
     rep = compare(wl, body, oracle.run(wl, 4), gpu_compressed=comp)

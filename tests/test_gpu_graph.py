@@ -89,3 +89,8 @@ def test_graph_c4_and_indexer():
     d = DeviceWorkload(ix)
     announce("graph: indexer")
     capture_and_replay(d, lambda: c128.indexer_compress_store(*d.args()))
+    fx = synth.indexer_decode_batch("graph indexer mxfp4", 1305, 300, 700, 16, 16, kv_bs=16,
+                                    kv_blocks=40, cs_rows=128, fp4=True)
+    d = DeviceWorkload(fx)
+    announce("graph: indexer mxfp4")
+    capture_and_replay(d, lambda: c128.indexer_mxfp4_compress_store(*d.args()))
