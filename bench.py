@@ -314,31 +314,57 @@ def sweep(args, path):
     out = open(path, "w")
     cpu_seen = {}  # workload name -> its oracle timing (taken once per workload)
 
+    def make_calls(dws, splits, varlen, st):
+        """One call per window set, on stream handle ``st`` (None: torch's current stream, as
+        graph capture needs)."""
+        kw = {} if st is None else {"stream": st}
+        if getattr(dws[0].wl, "indexer_fp4", False):
+            return [(lambda d=d: c128.indexer_mxfp4_compress_store(*d.args(), **kw))
+                    for d in dws]
+        if getattr(dws[0].wl, "indexer", False):
+            return [(lambda d=d: c128.indexer_compress_store(*d.args(), **kw)) for d in dws]
+        if getattr(dws[0].wl, "compress_ratio", 128) == 4:
+            return [(lambda d=d: c128.c4_compress_store(*d.args(), **kw)) for d in dws]
+        if varlen:
+            wss = [torch.empty(max(16, c128.varlen_workspace_bytes(d.wl.num_tokens)),
+                               dtype=torch.uint8, device=dev) for d in dws]
+            return [(lambda d=d, w=w: c128.compress_store_varlen(*d.args(), workspace=w, **kw))
+                    for d, w in zip(dws, wss)]
+        if splits is None:
+            return [(lambda d=d: c128.compress_store(*d.args(), **kw)) for d in dws]
+        wss = [c128.fanout_workspace(d.wl.num_tokens, splits, dev) for d in dws]
+        return [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w, splits=splits,
+                                                         **kw))
+                for d, w in zip(dws, wss)]
+
+    def graph_us_per_call(calls):
+        """Per-call time of the calls captured back to back in one graph (at least 32, cycling
+        over the window sets), replayed 20 times after 3 untimed replays: what a serving loop
+        that captures its decode step pays, without the per-launch host cost."""
+        n = max(32, len(calls))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                calls[i % len(calls)]()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (20 * n)
+        del g
+        return us
+
     def measure(name, dws, steps, warm_only=False, splits=None, varlen=False):
         """splits None: the single-pass entry point; else compress_store_ex with that split
         count (0 = automatic) and a workspace per window set; varlen: the compacted schedule
-        (compress_store_varlen) with a workspace per window set."""
-        if getattr(dws[0].wl, "indexer_fp4", False):
-            calls = [(lambda d=d: c128.indexer_mxfp4_compress_store(*d.args(), stream=sid))
-                     for d in dws]
-        elif getattr(dws[0].wl, "indexer", False):
-            calls = [(lambda d=d: c128.indexer_compress_store(*d.args(), stream=sid))
-                     for d in dws]
-        elif getattr(dws[0].wl, "compress_ratio", 128) == 4:
-            calls = [(lambda d=d: c128.c4_compress_store(*d.args(), stream=sid)) for d in dws]
-        elif varlen:
-            wss = [torch.empty(max(16, c128.varlen_workspace_bytes(d.wl.num_tokens)),
-                               dtype=torch.uint8, device=dev) for d in dws]
-            calls = [(lambda d=d, w=w: c128.compress_store_varlen(*d.args(), workspace=w,
-                                                                  stream=sid))
-                     for d, w in zip(dws, wss)]
-        elif splits is None:
-            calls = [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
-        else:
-            wss = [c128.fanout_workspace(d.wl.num_tokens, splits, dev) for d in dws]
-            calls = [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w,
-                                                              splits=splits, stream=sid))
-                     for d, w in zip(dws, wss)]
+        (compress_store_varlen) with a workspace per window set.  Batches of up to 1024 tokens
+        are also timed inside a graph."""
+        calls = make_calls(dws, splits, varlen, sid)
         if args.sweep_steps:
             steps = min(steps, args.sweep_steps)
         wl = dws[0].wl
@@ -361,6 +387,9 @@ def sweep(args, path):
             rec["cold_us_median"] = round(float(np.median(percold)) * 1e3, 2)
             rec["cold_gbs"] = round(nbytes / (rec["cold_us_median"] * 1e-6) / 1e9, 1)
         rec["pct_peak_hbm_warm"] = round(100 * rec["warm_gbs"] / PEAK_GBS, 2)
+        if wl.num_tokens <= 1024:
+            rec["graph_us_per_call"] = round(graph_us_per_call(make_calls(dws, splits, varlen,
+                                                                          None)), 2)
         if not args.no_cpu_baseline:
             if name not in cpu_seen:
                 cpu_seen[name] = oracle_timing(wl, nbytes)
