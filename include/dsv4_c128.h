@@ -30,7 +30,9 @@
  *   Every other byte of k_cache stays unchanged.
  *
  * Tensor views.  Each argument is a dsv4_tensor: a caller-owned pointer, a
- * dtype code, a rank and shape/stride arrays.  Strides are in ELEMENTS.
+ * dtype code, a rank and shape/stride arrays.  Strides are in ELEMENTS; the
+ * stride of every dimension longer than 1 is non-negative, and a tensor
+ * spans at most 2^48 bytes from its first to its last element.
  * For the compute entry points every `data` pointer is device memory of the
  * current HIP device; the library never allocates, frees or keeps a pointer
  * after the call returns.  k_cache is written in place; every other tensor
@@ -94,7 +96,7 @@ enum dsv4_status {
                            block table < 16 columns, token arrays of different length,
                            more than DSV4_MAX_TOKENS tokens, or a size above INT32_MAX */
   DSV4_ERR_STRIDE = -5, /* inner stride != 1, overlapping rows/blocks, k_cache stride[0]
-                           below bs*584 */
+                           below bs*584, a negative stride, or a span above 2^48 bytes */
   DSV4_ERR_ALIGN = -6,  /* a pointer or stride breaks the alignment stated above */
   DSV4_ERR_LAUNCH = -7, /* the HIP runtime reported an error at launch */
   DSV4_ERR_ARG = -8     /* an argument outside its documented set (splits, workspace size) */

@@ -32,6 +32,10 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int64_t kI32Max = 2147483647;
+// Largest span of a tensor, first to last element, in bytes: far beyond any device
+// allocation, and small enough that no index times stride the kernels form can overflow
+// 64-bit address arithmetic.
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 48;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -49,6 +53,18 @@ int check_tensor(const dsv4_tensor* t, const char* name, int dtype, int ndim) {
   int64_t numel = 1;
   for (int d = 0; d < ndim; ++d) numel *= t->shape[d];
   if (numel > 0 && !t->data) return fail(DSV4_ERR_NULL, "%s: data pointer is NULL", name);
+  // strides of dimensions longer than 1: non-negative, and a span below kMaxSpanBytes
+  const int64_t esize = dtype == DSV4_U8 ? 1 : 4;
+  int64_t span = 0;
+  for (int d = 0; d < ndim; ++d) {
+    if (t->shape[d] <= 1) continue;
+    if (t->stride[d] < 0)
+      return fail(DSV4_ERR_STRIDE, "%s: stride[%d] = %lld is negative", name, d,
+                  static_cast<long long>(t->stride[d]));
+    if (t->stride[d] > kMaxSpanBytes / esize / (t->shape[d] - 1) ||
+        (span += (t->shape[d] - 1) * t->stride[d] * esize) > kMaxSpanBytes)
+      return fail(DSV4_ERR_STRIDE, "%s: the strides span more than 2^48 bytes", name);
+  }
   return DSV4_OK;
 }
 

@@ -472,6 +472,33 @@ def test_indexer_mxfp4_rejects_before_any_hip_call():
     assert lib.dsv4_e2m1_encode(None, None, 4, None) == -1
 
 
+def test_negative_and_overflowing_strides_are_rejected():
+    """A negative stride on a dimension longer than 1, or strides whose span passes 2^48 bytes,
+    is DSV4_ERR_STRIDE before any launch (no index times stride can then overflow); the same
+    strides on a dimension of length 1 are never multiplied by a nonzero index and pass."""
+    lib = c128.library()
+    for k, dim, stride in (("state_cache", 0, 1 << 50), ("state_cache", 0, -8192),
+                           ("block_table", 0, 1 << 47), ("cos_sin", 0, -64),
+                           ("k_cache", 0, 1 << 48)):
+        ds = [c128.describe(valid_args()[n]) for n in ARG_ORDER]
+        ds[ARG_ORDER.index(k)].stride[dim] = stride
+        refs = [ctypes.byref(d) for d in ds]
+        assert lib.dsv4_c128_validate(*refs[:6], 1e-6, *refs[6:]) == -5, (k, stride)
+        assert "stride" in c128.last_error() or "span" in c128.last_error()
+    a = valid_args()
+    a["block_table"] = torch.zeros(1, 64, dtype=torch.int32)
+    ds = [c128.describe(a[n]) for n in ARG_ORDER]
+    ds[ARG_ORDER.index("block_table")].stride[0] = -(1 << 60)
+    refs = [ctypes.byref(d) for d in ds]
+    assert lib.dsv4_c128_validate(*refs[:6], 1e-6, *refs[6:]) == 0, c128.last_error()
+    # the largest span that passes: 2^48 bytes of k_cache blocks
+    ds = [c128.describe(valid_args()[n]) for n in ARG_ORDER]
+    kc = ds[ARG_ORDER.index("k_cache")]
+    kc.stride[0] = ((1 << 48) - 3 * 584 - 583) // (kc.shape[0] - 1) // 8 * 8
+    refs = [ctypes.byref(d) for d in ds]
+    assert lib.dsv4_c128_validate(*refs[:6], 1e-6, *refs[6:]) == 0, c128.last_error()
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without the built library every entry point raises: there is no fallback path."""
     monkeypatch.setattr(c128, "LIBRARY_PATH", str(tmp_path / "libdsv4_c128.so"))
