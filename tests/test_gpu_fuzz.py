@@ -98,7 +98,7 @@ def draw_large(case):
     small shared pool, with random paddings and the same gate and slot perturbations."""
     rng = np.random.default_rng(9500 + case)
     T = int(rng.choice([2048, 3001, 5555, 8192, 9001, 12345, 16500]))
-    kv_bs = int(rng.choice([16, 64]))
+    kv_bs = int(rng.choice([1, 7, 16, 64]))
     wl = synth.shared_pool_batch(f"fuzz large {case}", 9500 + case, T, 2048, 8, kv_bs,
                                  -(-T // kv_bs) + 2, 1024,
                                  score_std=float(rng.choice([0.5, 2 ** 0.5, 4.0])),
@@ -109,7 +109,7 @@ def draw_large(case):
     return wl
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(8))
 def test_fuzz_staged(case):
     wl = draw_large(case)
     announce(f"fuzz staged case {case}: T={wl.num_tokens} kv_bs={wl.k_cache.shape[1]}")
