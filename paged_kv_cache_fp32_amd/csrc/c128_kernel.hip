@@ -227,20 +227,18 @@ hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.num_tokens));
   const dim3 block(128 * kRowGroups);
   if (p.compressed_out)
-    c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, true>
-        <<<grid, block, 0, stream>>>(p);
-  else
-    c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, false>
-        <<<grid, block, 0, stream>>>(p);
-  return hipGetLastError();
+    return launch_kernel(c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, true>,
+                         grid, block, stream, p);
+  return launch_kernel(c128_compress_store_kernel<kRowGroups, kStageRows, kWavesPerSimd, false>,
+                       grid, block, stream, p);
 }
 
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t threads = (n + 3) / 4;
   const int64_t blocks = (threads + 255) / 256;
-  e4m3_encode_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(in, out, n);
-  return hipGetLastError();
+  return launch_kernel(e4m3_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), stream,
+                       in, out, n);
 }
 
 }  // namespace dsv4

@@ -6,9 +6,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 #include "c128_params.h"
 
 namespace dsv4 {
+
+// Launch `kernel` on `stream` and return the status of this launch alone.  (hipGetLastError after
+// a <<<>>> launch would also report, and clear, an earlier error of the calling thread.)  The
+// arguments are converted to the kernel's parameter types before their addresses are taken.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                         A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<std::decay_t<P>...> vals(std::forward<A>(args)...);
+  return std::apply(
+      [&](auto&... v) {
+        void* argv[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0,
+                               stream);
+      },
+      vals);
+}
 
 // Single pass and encoder: c128_kernel.hip.  Every launcher returns the hipError_t of its launch.
 // Batches of kStagedMinTokens and more go to the staged schedule.

@@ -633,12 +633,10 @@ hipError_t launch_fanout(const C128Params& p, void* ws, hipStream_t stream) {
   float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kFanoutCounterBytes);
   const dim3 grid(static_cast<unsigned>(p.num_tokens), S);
   if (p.compressed_out)
-    c128_fanout_kernel<RG, NBW, kStageRows, true>
-        <<<grid, dim3(128 * RG), 0, stream>>>(p, partials, counters);
-  else
-    c128_fanout_kernel<RG, NBW, kStageRows, false>
-        <<<grid, dim3(128 * RG), 0, stream>>>(p, partials, counters);
-  return hipGetLastError();
+    return launch_kernel(c128_fanout_kernel<RG, NBW, kStageRows, true>, grid, dim3(128 * RG),
+                         stream, p, partials, counters);
+  return launch_kernel(c128_fanout_kernel<RG, NBW, kStageRows, false>, grid, dim3(128 * RG),
+                       stream, p, partials, counters);
 }
 
 }  // namespace
@@ -702,19 +700,16 @@ hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stre
   compacted_schedule(p.num_tokens, &chunk, &nblocks);
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* list = counts + kMaxScanBlocks;
-  c128_gate_scan_kernel<<<dim3(static_cast<unsigned>(nblocks)), dim3(kScanThreads), 0, stream>>>(
-      p, chunk, counts, list);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_kernel(c128_gate_scan_kernel, dim3(static_cast<unsigned>(nblocks)),
+                                 dim3(kScanThreads), stream, p, chunk, counts, list);
   if (err != hipSuccess) return err;
   const unsigned grid =
       static_cast<unsigned>(p.num_tokens < kCompactedGrid ? p.num_tokens : kCompactedGrid);
   if (p.compressed_out)
-    c128_compacted_kernel<true><<<dim3(grid), dim3(128 * kRowGroups), 0, stream>>>(
-        p, counts, list, chunk, nblocks);
-  else
-    c128_compacted_kernel<false><<<dim3(grid), dim3(128 * kRowGroups), 0, stream>>>(
-        p, counts, list, chunk, nblocks);
-  return hipGetLastError();
+    return launch_kernel(c128_compacted_kernel<true>, dim3(grid), dim3(128 * kRowGroups), stream,
+                         p, counts, list, chunk, nblocks);
+  return launch_kernel(c128_compacted_kernel<false>, dim3(grid), dim3(128 * kRowGroups), stream,
+                       p, counts, list, chunk, nblocks);
 }
 
 namespace {
@@ -749,12 +744,12 @@ hipError_t launch_c128_staged(const C128Params& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(groups));
   const dim3 block(128 * kStagedRowGroups);
   if (p.compressed_out)
-    c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, true>
-        <<<grid, block, 0, stream>>>(p, per_group);
-  else
-    c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, false>
-        <<<grid, block, 0, stream>>>(p, per_group);
-  return hipGetLastError();
+    return launch_kernel(
+        c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, true>,
+        grid, block, stream, p, per_group);
+  return launch_kernel(
+      c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, false>,
+      grid, block, stream, p, per_group);
 }
 
 }  // namespace dsv4

@@ -283,12 +283,10 @@ hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipSt
   const dim3 block(64 * kC4WavesPerGroup);
   const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
   if (p.compressed_out)
-    c4_compress_store_kernel<true, kC4WavesPerSimd><<<grid, block, 0, stream>>>(p, state_bs, lg,
-                                                                                 kpw);
-  else
-    c4_compress_store_kernel<false, kC4WavesPerSimd><<<grid, block, 0, stream>>>(p, state_bs, lg,
-                                                                                  kpw);
-  return hipGetLastError();
+    return launch_kernel(c4_compress_store_kernel<true, kC4WavesPerSimd>, grid, block, stream, p,
+                         state_bs, lg, kpw);
+  return launch_kernel(c4_compress_store_kernel<false, kC4WavesPerSimd>, grid, block, stream, p,
+                       state_bs, lg, kpw);
 }
 
 }  // namespace dsv4

@@ -255,10 +255,10 @@ hipError_t launch_indexer(const C128Params& p, int32_t state_bs, hipStream_t str
   const dim3 block(64 * kIdxWavesPerGroup);
   const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
   if (p.compressed_out)
-    indexer_compress_store_kernel<true, kFp4><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
-  else
-    indexer_compress_store_kernel<false, kFp4><<<grid, block, 0, stream>>>(p, state_bs, lg, kpw);
-  return hipGetLastError();
+    return launch_kernel(indexer_compress_store_kernel<true, kFp4>, grid, block, stream, p,
+                         state_bs, lg, kpw);
+  return launch_kernel(indexer_compress_store_kernel<false, kFp4>, grid, block, stream, p,
+                       state_bs, lg, kpw);
 }
 
 }  // namespace
@@ -276,8 +276,8 @@ hipError_t launch_indexer_mxfp4_compress_store(const C128Params& p, int32_t stat
 hipError_t launch_e2m1_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256;
-  e2m1_encode_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(in, out, n);
-  return hipGetLastError();
+  return launch_kernel(e2m1_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), stream,
+                       in, out, n);
 }
 
 }  // namespace dsv4

@@ -602,3 +602,43 @@ def test_state_pool_beyond_2_31_floats():
     finally:
         del pool
         torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- error attribution
+
+def loaded_hip_runtime():
+    """The HIP runtime library already mapped into this process (the one the library uses)."""
+    import ctypes
+    paths = sorted({line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line})
+    assert len(paths) == 1, paths
+    return ctypes.CDLL(paths[0])
+
+
+def test_earlier_hip_error_is_not_reported_as_a_launch_failure():
+    """A failed HIP call before the compress call (hipSetDevice on a device that does not exist)
+    leaves an error in the thread's last-error slot.  Every entry point reports only the status
+    of its own launches, so the call succeeds, writes the same bytes, and the earlier error is
+    still there for whoever made it."""
+    import paged_kv_cache_fp32_amd as c128
+    hip = loaded_hip_runtime()
+    wl = small(T=9, seed=77)
+    d = DeviceWorkload(wl)
+    ws = c128.fanout_workspace(wl.num_tokens, 4)
+    vws = torch.empty(c128.varlen_workspace_bytes(wl.num_tokens), dtype=torch.uint8,
+                      device="cuda")
+    torch.cuda.synchronize()
+    announce("earlier HIP error, then the entry points")
+    for label, call in (("plain", lambda: c128.compress_store(*d.args())),
+                        ("fan-out", lambda: c128.compress_store_ex(*d.args(), workspace=ws,
+                                                                   splits=4)),
+                        ("compacted", lambda: c128.compress_store_varlen(*d.args(),
+                                                                         workspace=vws))):
+        planted = hip.hipSetDevice(12345)
+        assert planted != 0
+        call()                                   # raises if the call reported an error
+        assert hip.hipGetLastError() == planted, label   # read (and clear) the planted error
+        torch.cuda.synchronize()
+    body, guards_ok = d.k_cache_bytes()
+    assert guards_ok
+    rep = compare(wl, body, oracle.run(wl, THREADS))
+    assert rep.ok(), rep.summary()
