@@ -105,6 +105,31 @@ int main(void) {
   b.w.data = NULL;
   CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_NULL);
 
+  /* Strides: negative on a dimension longer than 1, or a span beyond 2^48 bytes, whatever the
+     products of shape and stride would be in 64 bits. */
+  b = a;
+  b.state.stride[0] = -8192;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_STRIDE);
+  b = a;
+  b.state.stride[0] = INT64_MAX;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_STRIDE);
+  b = a;
+  b.kc.stride[0] = INT64_MAX / 2;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_STRIDE);
+  b = a;
+  b.table.shape[0] = INT32_MAX;
+  b.table.stride[0] = (int64_t)1 << 40;
+  b.req.shape[0] = b.pos.shape[0] = b.slot.shape[0] = b.kvslot.shape[0] = DSV4_MAX_TOKENS;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_STRIDE);
+  b.table.stride[0] = 64;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_OK);
+  b.req.shape[0] = b.pos.shape[0] = b.slot.shape[0] = b.kvslot.shape[0] = DSV4_MAX_TOKENS + 1;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_ERR_SHAPE);
+  b = a;
+  b.table.shape[0] = 1; /* a row stride of a single row is never used */
+  b.table.stride[0] = INT64_MIN;
+  CHECK(run(dsv4_c128_validate, &b) == DSV4_OK);
+
   /* A passing call clears the message. */
   CHECK(run(dsv4_c128_validate, &a) == DSV4_OK);
   CHECK(strcmp(dsv4_last_error(), "") == 0);

@@ -35,10 +35,12 @@ def test_c_consumer(lang, tmp_path):
 
 
 def test_c_consumer_under_address_sanitizer(tmp_path):
-    """The host validation code (c128_abi.cpp) built with AddressSanitizer on its host pass only
-    (-Xarch_host -fsanitize=address: no GPU code is instrumented) and linked into the plain C
-    consumer, the kernels' launchers coming from the built library: every validation path the
-    consumer drives runs without an out-of-bounds access or a use after free."""
+    """The host validation code (c128_abi.cpp) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host pass only (-Xarch_host before each -fsanitize: no GPU
+    code is instrumented) and linked into the plain C consumer, the kernels' launchers coming
+    from the built library: every validation path the consumer drives, the stride-span guards
+    against 64-bit overflow included, runs without an out-of-bounds access, a use after free or
+    undefined behaviour."""
     hipcc = "/opt/rocm/bin/hipcc"
     if shutil.which("gcc") is None or not os.path.exists(hipcc):
         pytest.skip("gcc or hipcc not found")
@@ -47,12 +49,13 @@ def test_c_consumer_under_address_sanitizer(tmp_path):
     csrc = os.path.join(ROOT, "paged_kv_cache_fp32_amd", "csrc")
     abi_o, cons_o, exe = tmp_path / "abi.o", tmp_path / "consumer.o", tmp_path / "consumer_asan"
     subprocess.run([hipcc, "-std=c++17", "-O1", "-g", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
                     "-fno-omit-frame-pointer", "-I", INCLUDE, "-I", csrc, "-c",
                     os.path.join(csrc, "c128_abi.cpp"), "-o", str(abi_o)],
                    check=True, capture_output=True, text=True)
     subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address", "-I", INCLUDE, "-c", SRC,
                     "-o", str(cons_o)], check=True, capture_output=True, text=True)
-    subprocess.run(["g++", "-fsanitize=address", str(cons_o), str(abi_o), f"-L{lib_dir}",
+    subprocess.run(["g++", "-fsanitize=address,undefined", str(cons_o), str(abi_o), f"-L{lib_dir}",
                     "-ldsv4_c128", "-L/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{lib_dir}",
                     "-Wl,-rpath,/opt/rocm/lib", "-o", str(exe)],
                    check=True, capture_output=True, text=True)
