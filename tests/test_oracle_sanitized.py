@@ -1,0 +1,29 @@
+"""The CPU oracle (oracle/c128_oracle.c) built with AddressSanitizer and
+UndefinedBehaviorSanitizer (gcc, host code only) and driven by tests/oracle_driver.c through the
+four cache formats (C128, C4, indexer FP8, indexer MXFP4) and every early exit: a non-boundary
+position, a negative state slot, an out-of-range request, an out-of-range block id, a negative
+and an out-of-range kv slot.  The run must be free of memory errors, undefined behaviour and
+leaks, give each token its expected status and leave every other cache byte unchanged."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "oracle_driver"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                    os.path.join(ROOT, "tests", "oracle_driver.c"),
+                    os.path.join(ROOT, "oracle", "c128_oracle.c"), "-lm", "-lpthread",
+                    "-o", str(exe)], check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1")
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0, out.stderr[-4000:]
+    assert out.stdout.strip() == "oracle driver ok"
