@@ -1,4 +1,4 @@
-"""The CPU oracle (oracle/c128_oracle.c) built with AddressSanitizer and
+"""Sanitizer runs of the C test infrastructure.  The CPU oracle (oracle/c128_oracle.c) built with AddressSanitizer and
 UndefinedBehaviorSanitizer (gcc, host code only) and driven by tests/oracle_driver.c through the
 four cache formats (C128, C4, indexer FP8, indexer MXFP4) and every early exit: a non-boundary
 position, a negative state slot, an out-of-range request, an out-of-range block id, a negative
@@ -27,3 +27,22 @@ def test_oracle_under_sanitizers(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
     assert out.returncode == 0, out.stderr[-4000:]
     assert out.stdout.strip() == "oracle driver ok"
+
+
+def test_input_generator_under_sanitizers(tmp_path):
+    """The seeded input generator (synth/synth_gen.c) under the same sanitizers, driven by
+    tests/synth_driver.c: a padded pool filled with 1 and with 5 threads gives identical values
+    and leaves every padding element alone; the other fill functions stay inside their
+    outputs."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "synth_driver"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                    os.path.join(ROOT, "tests", "synth_driver.c"),
+                    os.path.join(ROOT, "synth", "synth_gen.c"), "-lm", "-lpthread",
+                    "-o", str(exe)], check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1")
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0, out.stderr[-4000:]
+    assert out.stdout.strip() == "synth driver ok"
