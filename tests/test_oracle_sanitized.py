@@ -1,9 +1,12 @@
-"""Sanitizer runs of the C test infrastructure.  The CPU oracle (oracle/c128_oracle.c) built with AddressSanitizer and
-UndefinedBehaviorSanitizer (gcc, host code only) and driven by tests/oracle_driver.c through the
-four cache formats (C128, C4, indexer FP8, indexer MXFP4) and every early exit: a non-boundary
-position, a negative state slot, an out-of-range request, an out-of-range block id, a negative
-and an out-of-range kv slot.  The run must be free of memory errors, undefined behaviour and
-leaks, give each token its expected status and leave every other cache byte unchanged."""
+"""Sanitizer runs of the C test infrastructure (gcc, host code only, AddressSanitizer and
+UndefinedBehaviorSanitizer).
+
+The CPU oracle (oracle/c128_oracle.c), driven by tests/oracle_driver.c through the four cache
+formats (C128, C4, indexer FP8, indexer MXFP4) and every early exit: a non-boundary position, a
+negative state slot, an out-of-range request, an out-of-range block id, a negative and an
+out-of-range kv slot.  The run must be free of memory errors, undefined behaviour and leaks,
+give each token its expected status and leave every other cache byte unchanged.  Then the seeded
+input generator (synth/synth_gen.c), driven by tests/synth_driver.c."""
 
 import os
 import shutil
