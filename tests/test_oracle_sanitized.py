@@ -49,3 +49,22 @@ def test_input_generator_under_sanitizers(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
     assert out.returncode == 0, out.stderr[-4000:]
     assert out.stdout.strip() == "synth driver ok"
+
+
+@pytest.mark.parametrize("driver,sources", [
+    ("oracle_driver.c", [os.path.join("oracle", "c128_oracle.c")]),
+    ("synth_driver.c", [os.path.join("synth", "synth_gen.c")])])
+def test_threads_under_thread_sanitizer(driver, sources, tmp_path):
+    """Both C modules split their work over pthreads (the oracle by token, the generator by
+    block); under ThreadSanitizer the same drivers run without a data race."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / (driver[:-2] + "_tsan")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fsanitize=thread",
+                    os.path.join(ROOT, "tests", driver),
+                    *[os.path.join(ROOT, s) for s in sources], "-lm", "-lpthread",
+                    "-o", str(exe)], check=True, capture_output=True, text=True)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0, out.stderr[-4000:]
+    assert "ThreadSanitizer" not in out.stderr
