@@ -84,6 +84,14 @@ __device__ __forceinline__ void load_rows(float4 (&kv)[CH], float4 (&sc)[CH], co
 template <int C, bool kFirst, int CH>
 __device__ __forceinline__ void update_column(const float4 (&kv)[CH], const float4 (&sc)[CH],
                                               float& ml, float& l, float& acc) {
+  // No contraction in here: the stage maximum cm = fl(max(s) * log2 e) must stay a rounded
+  // product.  Every weight of the stage is exp2(s * log2 e - cm) with one shared cm, so the
+  // rounding of cm cancels when the weights are normalised; a later stage rescales this one by
+  // exp2(ml - mn) with ml == cm.  Under -ffp-contract=fast the compiler may fuse the multiply
+  // into that subtraction, which then sees the exact product instead of cm, and the rounding of
+  // cm (half an ulp of s * log2 e) stops cancelling between the stages.  The explicit fmaf
+  // calls below stay fused.
+#pragma clang fp contract(off)
   float s[CH];
 #pragma unroll
   for (int r = 0; r < CH; ++r) s[r] = lane_of<C>(sc[r]);

@@ -176,6 +176,24 @@ def test_peaky_and_near_constant_scores():
     check(wl, label="near-constant windows")
 
 
+@pytest.mark.parametrize("score_std", [1e2, 1e4, 1e6])
+def test_extreme_scores(score_std):
+    """Scores spread so far (std 1e2 to 1e6) that each column's softmax is one-hot or nearly so:
+    the max-subtracted exponentials must neither overflow nor produce NaN, on the single pass
+    (16 tokens), the staged schedule (2048 tokens) and the fan-out."""
+    wl = small(T=16, seed=19, score_std=score_std)
+    check(wl, label=f"scores std {score_std:g}, single pass")
+    announce(f"scores std {score_std:g}, fan-out")
+    body, comp, guards_ok = run_gpu(wl, debug=True, splits=8)
+    assert guards_ok
+    rep = compare(wl, body, oracle.run(wl, THREADS), gpu_compressed=comp)
+    assert rep.ok(), rep.summary()
+    big = synth.shared_pool_batch(f"scores std {score_std:g}", 5300, 2048, 2048, 8, 64, 34,
+                                  1024, score_std=score_std)
+    rep, *_ = check(big, label=f"scores std {score_std:g}, staged")
+    assert rep["written"] == 2048
+
+
 def test_out_of_range_device_indices_write_nothing():
     """Indices that live in device memory and are out of range (request, block id, kv slot,
     RoPE row) make the kernel skip the token: nothing is written, no fault."""
