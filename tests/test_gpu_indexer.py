@@ -165,3 +165,12 @@ def test_indexer_state_pool_beyond_2_31_floats():
     finally:
         del pool
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("score_std", [1e2, 1e4])
+def test_indexer_extreme_scores(score_std):
+    """Scores spread so far that each column's softmax is one-hot or nearly so: no overflow, no
+    NaN, and near ties within the compressed tolerance."""
+    wl = idx_batch(300, 950 + int(score_std), score_std=score_std)
+    rep, *_ = check(wl, f"indexer scores std {score_std:g}")
+    assert rep["written"] == 300
