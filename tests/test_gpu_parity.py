@@ -194,6 +194,20 @@ def test_extreme_scores(score_std):
     assert rep["written"] == 2048
 
 
+@pytest.mark.parametrize("scale", [1e-4, 1e4])
+def test_kv_magnitudes(scale):
+    """kv scaled by 1e-4 (mean(c^2) far below eps = 1e-6, so eps sets the norm and the codes
+    shrink towards the scale floor) and by 1e4 (sums of squares near 1e10): the single pass and
+    the staged schedule agree with the oracle."""
+    wl = small(T=16, seed=23)
+    wl.state[:, :, :512] *= np.float32(scale)
+    check(wl, label=f"kv x {scale:g}, single pass")
+    big = synth.shared_pool_batch(f"kv x {scale:g}", 5400, 2048, 2048, 8, 64, 34, 1024)
+    big.state[:, :, :512] *= np.float32(scale)
+    rep, *_ = check(big, label=f"kv x {scale:g}, staged")
+    assert rep["written"] == 2048
+
+
 def test_out_of_range_device_indices_write_nothing():
     """Indices that live in device memory and are out of range (request, block id, kv slot,
     RoPE row) make the kernel skip the token: nothing is written, no fault."""
