@@ -10,7 +10,13 @@ request, position 128k-1, k ~ U{1..64}), each gathering 16 distinct blocks of a
 RMSNorm, UE8M0/E4M3 quantisation, RoPE and the paged insert into a
 KV-block-size-64 k_cache.  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline).
+Prints one JSON line (metric, value = algorithmic GB/s, roofline, cpu_baseline, sweep).
+After the timed region, one call through the debug entry point gives the fp32 pooled vectors
+for the parity leg (its k_cache bytes must equal the timed calls').  ``sweep`` holds the
+metric's token range, cold (a 1 GiB read before each call): decode batches of 1, 128 and 1024
+tokens on the decode sweep's pool and the varlen prefill workload, each on the plain entry
+point and on the fastest one for that batch (the fan-out up to 128 tokens, the compacted
+schedule for prefill; at 1024 tokens the plain entry point is the fastest).
 ``--sweep PATH`` also writes per-workload JSONL with warm and cold timings and the
 oracle's time beside each workload: the C128 decode sweep 1..4096 tokens, the
 single-token, decode-batch and varlen-prefill workloads on every entry point
@@ -201,6 +207,15 @@ def main_line(args):
     traffic = measured_traffic()
 
     body, guards_ok = d.k_cache_bytes()
+    # Outside the timed region: one call through the debug entry point, whose fp32 pooled
+    # vectors the parity leg checks; its k_cache bytes must equal the timed calls'.
+    comp = torch.full((wl.num_tokens, 512), float("nan"), dtype=torch.float32, device=dev)
+    c128.compress_store_debug(*d.args(), comp, stream=sid)
+    torch.cuda.synchronize()
+    body_debug, _ = d.k_cache_bytes()
+    comp = comp.cpu().numpy()
+    debug_bytes_equal = bool(np.array_equal(body, body_debug))
+    del body_debug
     T = wl.num_tokens
     line = {
         "metric": METRIC,
@@ -240,18 +255,31 @@ def main_line(args):
     }
     if not guards_ok:
         line["error"] = "k_cache guard bands were written"
+    if not debug_bytes_equal:
+        line["error"] = "the debug entry point wrote other k_cache bytes than the timed calls"
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, body, nbytes)
-    del d
+        line["cpu_baseline"] = cpu_baseline(wl, body, nbytes, comp)
+    del d, comp
     torch.cuda.empty_cache()
+    if not args.no_range:
+        line["sweep"] = range_sweep(args)
     if args.sweep:
         sweep(args, args.sweep)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, gpu_body, nbytes):
+def host_cpus() -> int:
+    """CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, gpu_body, nbytes, gpu_compressed=None):
     """The oracle on the host cores, on the same resident host inputs; also checks the GPU
-    bytes of this run against it (outside the timer)."""
+    bytes (and, when given, the GPU's fp32 pooled vectors) of this run against it, outside the
+    timer.  Threads: one per visible CPU, at most 16 (a one-GPU share of the host)."""
     import oracle
     import synth
     from oracle.compare import compare
@@ -261,20 +289,98 @@ def cpu_baseline(wl, gpu_body, nbytes):
     orc = oracle.run(wl, threads)
     dt = time.perf_counter() - t0
     act = int(wl.active_mask().sum())
-    rep = compare(wl, gpu_body, orc)
+    rep = compare(wl, gpu_body, orc, gpu_compressed=gpu_compressed)
     log(f"[bench] oracle: {dt:.2f}s on {threads} threads; parity vs GPU: "
         f"{'ok' if rep.ok() else 'FAIL'} ({rep.summary()})")
     return {
         "value": round(nbytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
+        "host_cpus_visible": host_cpus(),
         "kind": "oracle",
         "sample": f"the full workload: all {wl.num_tokens} tokens ({act} active), fp64, "
                   f"{threads} threads",
         "seconds": round(dt, 3),
         "compressed_tokens_per_s": round(act / dt, 1),
         "parity_vs_gpu": "ok" if rep.ok() else "FAIL",
+        "parity_detail": {k: rep.get(k) for k in (
+            "scale_mismatch", "excused_blocks", "code_diff1_frac", "rope_max_ulp", "rope_band",
+            "rope_band_max_use", "compressed_max_ratio")},
     }
+
+
+def range_sweep(args):
+    """The metric's token range in the bench line: cold calls (a 1 GiB read before each one
+    evicts the L2s and the MALL) of decode batches of 1, 128 and 1024 tokens on the decode
+    sweep's 65536-block pool and of the varlen prefill workload, each on the plain entry point
+    and on the fastest entry point for that batch; median over the calls, per-call event time
+    on the launch stream."""
+    import torch
+
+    import paged_kv_cache_fp32_amd as c128
+    import synth
+    from synth.device import DeviceWorkload
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        torch.sum(scratch, dim=0, out=sink)
+
+    def entry(dws, kind):
+        if kind == "fan-out":
+            wss = [c128.fanout_workspace(d.wl.num_tokens, 0, dev) for d in dws]
+            return [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w, splits=0,
+                                                             stream=sid))
+                    for d, w in zip(dws, wss)]
+        if kind == "compacted":
+            wss = [torch.empty(c128.varlen_workspace_bytes(d.wl.num_tokens), dtype=torch.uint8,
+                               device=dev) for d in dws]
+            return [(lambda d=d, w=w: c128.compress_store_varlen(*d.args(), workspace=w,
+                                                                 stream=sid))
+                    for d, w in zip(dws, wss)]
+        return [(lambda d=d: c128.compress_store(*d.args(), stream=sid)) for d in dws]
+
+    out = []
+
+    def measure(name, dws, kinds):
+        wl = dws[0].wl
+        nbytes = algorithmic_bytes(wl)
+        for kind in kinds:
+            _, per = time_calls(torch, stream, entry(dws, kind), args.range_steps, 3,
+                                flush=flush)
+            us = float(np.median(per)) * 1e3
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out.append({"workload": name, "tokens": wl.num_tokens,
+                        "active": int(wl.active_mask().sum()), "entry": kind,
+                        "us_cold": round(us, 2), "gbs": round(gbs, 1),
+                        "frac": round(gbs / PEAK_GBS, 4)})
+            log(f"[range] {json.dumps(out[-1])}")
+
+    t0 = time.time()
+    _, pool = synth.config3_pool()
+    pool_dev = None
+    for T, best in ((1, "fan-out"), (128, "fan-out"), (1024, None)):
+        dws = []
+        for s in range(4):
+            d = DeviceWorkload(synth.config3(T, state=pool, window_set=s), device=dev,
+                               state=pool_dev)
+            pool_dev = (d.state_buf, d.state)
+            dws.append(d)
+        measure(f"decode T={T}", dws, ["plain"] + ([best] if best else []))
+        del dws
+    del pool, pool_dev
+    torch.cuda.empty_cache()
+    d2 = DeviceWorkload(synth.config2(), device=dev)
+    measure("varlen prefill", [d2], ["plain", "compacted"])
+    del d2, scratch
+    torch.cuda.empty_cache()
+    log(f"[range] done in {time.time() - t0:.1f}s")
+    return {"mode": "cold, median of per-call event times", "calls": args.range_steps,
+            "points": out}
 
 
 def oracle_timing(wl, nbytes, threads=None):
@@ -597,6 +703,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-range", action="store_true",
+                    help="leave out the cold token-range points (decode 1/128/1024 tokens, "
+                         "varlen prefill) of the bench line")
+    ap.add_argument("--range-steps", type=int, default=30,
+                    help="cold calls per token-range point")
     ap.add_argument("--sweep-filter", default=None,
                     help="only the sweep workloads whose name matches this regular expression")
     ap.add_argument("--sweep-steps", type=int, default=0,

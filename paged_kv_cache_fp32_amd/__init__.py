@@ -264,13 +264,19 @@ def compress_store_varlen(state_cache, block_table, token_to_req, positions, slo
             compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
             tuple(compressed_out.shape) != (positions.shape[0], 512)):
         raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    s = _stream(dev) if stream is None else stream
     if workspace is None:
-        workspace = torch.empty(max(varlen_workspace_bytes(positions.shape[0]), 16),
-                                dtype=torch.uint8, device=dev)
+        # Allocated on the launch stream: torch's caching allocator then reuses this memory
+        # only in that stream's order, after the two kernels that use it.
+        nbytes = max(varlen_workspace_bytes(positions.shape[0]), 16)
+        if stream is None or stream == _stream(dev):
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        else:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=dev)):
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     elif not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     _, refs = _descriptors(ts)
-    s = _stream(dev) if stream is None else stream
     out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
     _check(library().dsv4_c128_compress_store_varlen(
         *refs[:6], float(eps), *refs[6:], out_ptr, workspace.data_ptr(),

@@ -197,3 +197,171 @@ def test_mxfp4_knife_edge_excuses_a_flipped_scale():
     from oracle.compare import knife_edge, KNIFE_FP4
     assert knife_edge(1.50390625 * 4, KNIFE_FP4) and knife_edge(1.50390625 * 2 ** -3, KNIFE_FP4)
     assert not knife_edge(1.5 * 4, KNIFE_FP4) and not knife_edge(1.507 * 4, KNIFE_FP4)
+
+
+# ---------------------------------------------------------------- C128 knife edge
+
+def _fake_result(orc):
+    """A copy of an oracle result whose arrays a test may edit."""
+    return oracle.OracleResult(orc.k_cache_base.copy(), None, orc.compressed.copy(),
+                               orc.absnorm.copy(), orc.normed.copy(), orc.status.copy())
+
+
+def _bf16(x):
+    """Round-to-nearest-even bf16 of fp64 values through fp32, as the quantiser's input."""
+    b = oracle.bf16_bits(np.asarray(x, np.float64).astype(np.float32).astype(np.float64))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _encode_block(u, e):
+    """E4M3FN codes of the bf16 values ``u`` under the block scale 2^e, and the scale byte."""
+    return oracle.e4m3_codes(np.clip(u * 2.0 ** -e, -448.0, 448.0)), np.uint8(e + 127)
+
+
+def _knife_case(case, rel_offset):
+    """Token 5's quantisation block 2 scaled so that its fp64 absmax is the bf16 midpoint
+    1.75390625 * 2^k times (1 + rel_offset).  Returns (fake oracle result with that block
+    encoded as the oracle encodes it, GPU bytes with the block encoded as if fp32 rounding had
+    put bf16(absmax) on the other side of the midpoint, offsets)."""
+    wl, orc = case
+    t, g = 5, 2
+    res = _fake_result(orc)
+    v = res.normed[t, 64 * g:64 * (g + 1)]
+    amax = float(np.abs(v).max())
+    k = np.floor(np.log2(amax / 1.75390625))
+    v *= 1.75390625 * 2.0 ** k * (1.0 + rel_offset) / amax
+    res.normed[t, 64 * g:64 * (g + 1)] = v
+    rec, scl = record_offsets(int(wl.kv_slot_mapping[t]), wl.k_cache.shape[1],
+                              wl.k_cache.strides[0])
+    u = _bf16(v)
+    e_orc = int(oracle.ue8m0_exponents(np.array([np.abs(u).max()]))[0])
+    codes, byte = _encode_block(u, e_orc)
+    res.k_cache_base[rec + 64 * g:rec + 64 * (g + 1)] = codes
+    res.k_cache_base[scl + g] = byte
+    # the GPU's bf16 absmax lands on the other neighbour of the midpoint
+    i = int(np.argmax(np.abs(v)))
+    ug = u.copy()
+    up = 1.7578125 * 2.0 ** k
+    ug[i] = np.sign(v[i]) * (up if abs(u[i]) < up else 1.75 * 2.0 ** k)
+    e_gpu = int(oracle.ue8m0_exponents(np.array([np.abs(ug).max()]))[0])
+    assert e_gpu != e_orc
+    body = res.k_cache_base.copy()
+    gcodes, gbyte = _encode_block(ug, e_gpu)
+    body[rec + 64 * g:rec + 64 * (g + 1)] = gcodes
+    body[scl + g] = gbyte
+    return res, body, rec + 64 * g
+
+
+def test_knife_edge_excuses_a_flipped_c128_scale(case):
+    """At a true knife edge (absmax on the bf16 midpoint 1.75390625 * 2^k) a scale byte one
+    step off is excused when every dequantised value lies within one code step of the coarser
+    scale at its own binade."""
+    wl, _ = case
+    res, body, _ = _knife_case(case, 0.0)
+    rep = compare(wl, body, res)
+    assert rep.ok(), rep.summary()
+    assert rep["excused_blocks"] == 1 and rep["scale_mismatch"] == 0
+
+
+def test_knife_edge_flags_a_flip_outside_the_band(case):
+    """The same flip with the absmax 2e-5 (relative) away from the midpoint is not excused."""
+    wl, _ = case
+    res, body, _ = _knife_case(case, 2e-5)
+    rep = compare(wl, body, res)
+    assert not rep.ok() and rep["scale_mismatch"] == 1 and rep["excused_blocks"] == 0
+
+
+def test_knife_edge_flags_values_two_steps_off(case):
+    """An excused block still fails when one of its elements is two code steps off at its own
+    binade (a small element: the step there is far below the top binade's)."""
+    wl, _ = case
+    res, body, start = _knife_case(case, 0.0)
+    codes = body[start:start + 64]
+    mags = codes & 0x7F
+    j = int(np.nonzero((mags > 8) & (mags < 0x40))[0][0])   # a small normal element
+    body[start + j] = (codes[j] & 0x80) | (mags[j] + 2)
+    rep = compare(wl, body, res)
+    assert not rep.ok() and rep["excused_blocks"] == 1
+    assert any("excused block values differ" in f for f in rep["failures"])
+
+
+def test_knife_edge_band_limits():
+    from oracle.compare import knife_edge
+    for k in (-20, -3, 0, 5, 30):
+        edge = 1.75390625 * 2.0 ** k
+        assert knife_edge(edge) and knife_edge(edge * (1 + 9e-6)) and knife_edge(edge * (1 - 9e-6))
+        assert not knife_edge(edge * (1 + 1.1e-5)) and not knife_edge(edge * (1 - 1.1e-5))
+        assert not knife_edge(1.75 * 2.0 ** k) and not knife_edge(1.7578125 * 2.0 ** k)
+
+
+# ---------------------------------------------------------------- RoPE band
+
+def _rope_cancel_case(case):
+    """Token 5 of the case with its pooled pair (448, 449) replaced so that the first rotated
+    value cancels to about 1e-6 of its inputs.  Returns (fake oracle result encoding that
+    token's RoPE exactly, the GPU's pooled rows (fp32) with element 448 moved by 3e-6 of its
+    value, the GPU bytes with RoPE computed in fp64 from those rows, the byte offset of the
+    token's RoPE values)."""
+    from oracle.compare import bf16_ulp
+    wl, orc = case
+    t = 5
+    res = _fake_result(orc)
+    P = (int(wl.positions[t]) // 128) * 128
+    C, S = (float(x) for x in wl.cos_sin[P, [0, 32]])
+    w = wl.rms_w.astype(np.float64)
+    c = res.compressed[t].copy()
+    c[449] = c[448] * (w[448] / w[449]) * (C / S) * (1 + 1e-6)
+    res.compressed[t] = c
+
+    def rope(cv):
+        n = cv / np.sqrt(np.mean(cv * cv) + float(wl.eps)) * w
+        x, y = n[448::2], n[449::2]
+        cs = wl.cos_sin[P].astype(np.float64)
+        z = np.empty(64)
+        z[0::2] = x * cs[:32] - y * cs[32:]
+        z[1::2] = y * cs[:32] + x * cs[32:]
+        return z
+
+    res.normed[t] = c / np.sqrt(np.mean(c * c) + float(wl.eps)) * w
+    rec, _ = record_offsets(int(wl.kv_slot_mapping[t]), wl.k_cache.shape[1], wl.k_cache.strides[0])
+    z_orc = rope(c)
+    res.k_cache_base[rec + 448:rec + 576] = oracle.bf16_bits(z_orc).view(np.uint8)
+    gc = res.compressed.astype(np.float32)
+    gc[t, 448] *= np.float32(1 + 3e-6)
+    z_gpu = rope(gc[t].astype(np.float64))
+    body = res.k_cache_base.copy()
+    body[rec + 448:rec + 576] = oracle.bf16_bits(z_gpu).view(np.uint8)
+    # the planted cancellation really moves the first value by many ulps
+    assert abs(z_gpu[0] - z_orc[0]) > 4 * bf16_ulp(np.array([z_orc[0]]))[0]
+    return res, gc, body, rec + 448
+
+
+def test_rope_band_follows_the_gpu_pooled_vector(case):
+    """Under cancellation a RoPE value far (in ulps) from the oracle's passes when it is the
+    rotation of the GPU's own pooled vector, which is within the compressed tolerance; the
+    report counts it and gives the band's use."""
+    wl, _ = case
+    res, gc, body, _ = _rope_cancel_case(case)
+    rep = compare(wl, body, res, gpu_compressed=gc)
+    assert rep.ok(), rep.summary()
+    assert rep["rope_band"] >= 1 and rep["rope_max_ulp"] > 4
+    assert rep["rope_band_basis"] == "gpu pooled vector"
+    assert 0.0 <= rep["rope_band_max_use"] <= 1.0
+    assert rep["compressed_max_ratio"] <= 1e-5
+
+
+def test_rope_band_flags_a_value_off_its_own_rotation(case):
+    """The same element moved three band widths away from the rotation of the GPU's pooled
+    vector fails.  That band (the epilogue's fp32 error around the rotation) is several times
+    narrower than the band the compressed tolerance alone would allow."""
+    from oracle.compare import rope_band
+    wl, _ = case
+    res, gc, body, off = _rope_cancel_case(case)
+    z, tol = rope_band(wl, res, 5, gc[5])
+    _, tol_loose = rope_band(wl, res, 5)
+    assert tol[0] < tol_loose[0] / 4
+    v = body[off:off + 2].view("<u2")
+    v[0] = oracle.bf16_bits(np.array([z[0] + 3 * tol[0]]))[0]
+    rep = compare(wl, body, res, gpu_compressed=gc)
+    assert not rep.ok()
+    assert any("cancellation band" in f for f in rep["failures"])

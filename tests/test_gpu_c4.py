@@ -112,7 +112,7 @@ def test_c4_large_batch():
     """The 16384-token C4 decode batch of the bench, every token against the oracle."""
     wl = synth.c4_decode_batch("c4 decode T=16384", 1005, 16384, 16384 * 2, 1024, 512,
                                kv_bs=64, kv_blocks=256, cs_rows=4096)
-    rep, *_ = check(wl, "c4 decode T=16384", debug=False)
+    rep, *_ = check(wl, "c4 decode T=16384")
     assert rep["written"] == 16384
 
 

@@ -86,7 +86,7 @@ def test_indexer_gate_and_bad_indices():
 def test_indexer_large_batch():
     wl = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024, 512,
                                     kv_bs=64, kv_blocks=256, cs_rows=4096)
-    rep, *_ = check(wl, "indexer decode T=16384", debug=False)
+    rep, *_ = check(wl, "indexer decode T=16384")
     assert rep["written"] == 16384
 
 

@@ -106,7 +106,7 @@ def test_mxfp4_gate_and_bad_indices():
 def test_mxfp4_large_batch():
     wl = synth.indexer_decode_batch("mxfp4 decode T=16384", 1106, 16384, 16384 * 2, 1024, 512,
                                     kv_bs=64, kv_blocks=256, cs_rows=4096, fp4=True)
-    rep, *_ = check(wl, "mxfp4 decode T=16384", debug=False)
+    rep, *_ = check(wl, "mxfp4 decode T=16384")
     assert rep["written"] == 16384
 
 

@@ -123,11 +123,27 @@ def test_config3_rotated_window_sets(sweep_pool):
 
 
 def test_config4_full_size():
-    """16384 boundary tokens over the 8.59 GB pool, in the bench's launch configuration;
-    every token compared against the oracle."""
+    """16384 boundary tokens over the 8.59 GB pool, in the bench's launch configuration (the
+    staged schedule): every record and, through the debug entry point, every fp32 pooled vector
+    compared against the oracle (half the windows have near-constant scores).  The debug call
+    writes the same k_cache bytes as the plain call."""
     wl = synth.config4()
-    rep, *_ = check(wl, debug=False)
+    announce(f"{wl.name} (debug entry point, then the plain one)")
+    d = DeviceWorkload(wl)
+    comp = d.run(debug=True).cpu().numpy()
+    body_debug, ok_debug = d.k_cache_bytes()
+    d.kc_buf[d.guard:d.guard + wl.k_cache_base.size].copy_(torch.from_numpy(wl.k_cache_base))
+    d.run(debug=False)
+    body, ok = d.k_cache_bytes()
+    del d
+    torch.cuda.empty_cache()
+    assert ok and ok_debug, "k_cache guard bands were written"
+    assert np.array_equal(body, body_debug)
+    rep = compare(wl, body, oracle.run(wl, THREADS), gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
     assert rep["written"] == 16384
+    assert rep["compressed_max_ratio"] is not None and rep["compressed_max_ratio"] <= 1e-5
 
 
 # ---------------------------------------------------------------- edge cases
@@ -274,6 +290,26 @@ def test_stream_argument_is_used():
     assert ok and rep.ok(), rep.summary()
 
 
+def test_varlen_on_a_side_stream_without_workspace():
+    """The compacted schedule launched on an explicit side stream with the workspace left to the
+    binding (allocated on that stream), while the current stream allocates and fills other
+    memory: the result is there after the side stream synchronises."""
+    import paged_kv_cache_fp32_amd as c128
+    wl = small(T=40, seed=33, kv_bs=16, kv_blocks=6)
+    announce("compacted schedule on a side stream, binding-allocated workspace")
+    d = DeviceWorkload(wl)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    c128.compress_store_varlen(*d.args(), stream=side.cuda_stream)
+    junk = [torch.full((1 << 16,), 7, dtype=torch.int32, device="cuda") for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    body, ok = d.k_cache_bytes()
+    rep = compare(wl, body, oracle.run(wl, 2))
+    assert ok and rep.ok(), rep.summary()
+
+
 # ---------------------------------------------------------------- small-batch fan-out
 
 def check_ex(wl, splits, label, debug=True):
@@ -361,7 +397,7 @@ def batch_4096():
 def test_fanout_largest_batch(batch_4096, splits):
     """4096 tokens, the most the fan-out takes: the last arrival counter of the workspace's
     counter region is used, and every token agrees with the oracle."""
-    rep, *_ = check_ex(batch_4096, splits, "decode T=4096", debug=False)
+    rep, *_ = check_ex(batch_4096, splits, "decode T=4096")
     assert rep["written"] == 4096
 
 
@@ -409,6 +445,17 @@ def test_staged_threshold_and_rounds(T):
     entry point agrees with the oracle."""
     rep, *_ = check(shared(T, 5000 + T), label=f"shared pool T={T}")
     assert rep["written"] == T
+
+
+def test_staged_near_constant_score_windows():
+    """The staged schedule on the large batch's score mix at 3000 tokens (a ragged share per
+    workgroup): half the windows score N(0,1), half near-constant (c_w + 1e-3 N(0,1)), so many
+    columns pool with almost uniform weights.  Records and pooled vectors agree with the
+    oracle."""
+    wl = synth.decode_batch("staged score mix T=3000", 5500, 3000, 48000, 64, 1024, kv_bs=64,
+                            kv_blocks=48, cs_rows=8192, score_std=1.0, score_mix=True)
+    rep, *_ = check(wl, label="staged score mix T=3000")
+    assert rep["written"] == 3000
 
 
 def test_staged_padded_strides_and_largest_position():
@@ -481,8 +528,8 @@ def test_varlen_config2_and_plain_entry_point():
     rep, body, _ = check_varlen(wl, "cfg2 varlen prefill")
     assert rep["written"] == int(wl.written_mask().sum()) > 100
     announce("cfg2 varlen prefill (plain entry point)")
-    plain, _, ok = run_gpu(wl, debug=False)
-    rep2 = compare(wl, plain, oracle.run(wl, THREADS))
+    plain, comp, ok = run_gpu(wl, debug=True)
+    rep2 = compare(wl, plain, oracle.run(wl, THREADS), gpu_compressed=comp)
     assert ok and rep2.ok(), rep2.summary()
 
 
