@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 7
+#define DSV4_ABI_VERSION 8
 
 /* Most tokens one call takes (2^27).  The largest launch grid, the staged schedule's 16
    work-items per token, then stays within half of the 32-bit work-item count of a dispatch.
@@ -219,6 +219,34 @@ int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
  * list); 0 for num_tokens <= 0.  Host-only; no HIP call.
  */
 size_t dsv4_c128_varlen_workspace_bytes(int64_t num_tokens);
+
+/* Most tokens dsv4_c128_compress_store_varlen_noalloc takes in one call (2^20). */
+#define DSV4_VARLEN_NOALLOC_MAX_TOKENS 1048576
+
+/*
+ * dsv4_c128_compress_store_varlen without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The same two kernels and the same results, bit for bit; the scan counts and the compacted
+ * token list live in a fixed array inside the library instead: 4 * (1024 + 2^20) bytes
+ * (4 MiB + 4 KiB) of device memory on each device the library runs on, held until the process
+ * ends.  The call allocates and frees nothing.
+ *
+ *   T               at most DSV4_VARLEN_NOALLOC_MAX_TOKENS, else DSV4_ERR_ARG before any HIP
+ *                   call (split longer batches: tokens are independent).
+ *   compressed_out  NULL, or as in dsv4_c128_compress_store_debug.
+ *
+ * The array needs no initialisation: each call's scan writes every count and list entry that
+ * the same call reads.  All calls on one device share the array, so calls that overlap in time
+ * on one device race (two streams, or two host threads); order them on one stream.  The first
+ * call on a device looks up the array's device address (hipGetSymbolAddress) with that device
+ * current; make it outside graph capture.  An error of that lookup is DSV4_ERR_LAUNCH.
+ */
+int dsv4_c128_compress_store_varlen_noalloc(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    float* compressed_out, void* stream);
 
 /*
  * The C4 compressor: the same fused computation with compress ratio 4 and an overlapping

@@ -100,6 +100,9 @@ def library():
         lib.dsv4_c128_compress_store_varlen.argtypes = args10 + [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.dsv4_c128_compress_store_varlen.restype = ctypes.c_int
+        lib.dsv4_c128_compress_store_varlen_noalloc.argtypes = args10 + [ctypes.c_void_p,
+                                                                        ctypes.c_void_p]
+        lib.dsv4_c128_compress_store_varlen_noalloc.restype = ctypes.c_int
         lib.dsv4_c128_varlen_workspace_bytes.argtypes = [ctypes.c_int64]
         lib.dsv4_c128_varlen_workspace_bytes.restype = ctypes.c_size_t
         lib.dsv4_c4_compress_store.argtypes = args10 + [ctypes.c_void_p]
@@ -283,6 +286,30 @@ def compress_store_varlen(state_cache, block_table, token_to_req, positions, slo
         workspace.numel() * workspace.element_size(), s))
 
 
+VARLEN_NOALLOC_MAX_TOKENS = 1 << 20
+
+
+def compress_store_varlen_noalloc(state_cache, block_table, token_to_req, positions,
+                                  slot_mapping, rms_w, eps, cos_sin, k_cache, kv_slot_mapping,
+                                  compressed_out=None, stream: int | None = None) -> None:
+    """``compress_store_varlen`` with no workspace and no allocation: its scratch is a fixed
+    array of the library on each device (at most ``VARLEN_NOALLOC_MAX_TOKENS`` tokens per call;
+    calls that overlap on one device race).  ``compressed_out`` as in
+    ``compress_store_debug``."""
+    ts = [state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
+          k_cache, kv_slot_mapping]
+    dev = _require_cuda(ts + ([compressed_out] if compressed_out is not None else []))
+    if compressed_out is not None and (
+            compressed_out.dtype != torch.float32 or not compressed_out.is_contiguous() or
+            tuple(compressed_out.shape) != (positions.shape[0], 512)):
+        raise ValueError("compressed_out must be a contiguous float32 [T, 512] tensor")
+    _, refs = _descriptors(ts)
+    s = _stream(dev) if stream is None else stream
+    out_ptr = compressed_out.data_ptr() if compressed_out is not None else None
+    _check(library().dsv4_c128_compress_store_varlen_noalloc(*refs[:6], float(eps), *refs[6:],
+                                                             out_ptr, s))
+
+
 def c4_compress_store(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
                       eps, cos_sin, k_cache, kv_slot_mapping, compressed_out=None,
                       stream: int | None = None) -> None:
@@ -404,7 +431,8 @@ def e2m1_encode(x: torch.Tensor, stream: int | None = None) -> torch.Tensor:
 
 __all__ = ["compress_store", "compress_store_debug", "compress_store_ex", "workspace_bytes",
            "fanout_workspace",
-           "compress_store_varlen", "varlen_workspace_bytes", "c4_compress_store", "c4_validate",
+           "compress_store_varlen", "varlen_workspace_bytes", "compress_store_varlen_noalloc",
+           "VARLEN_NOALLOC_MAX_TOKENS", "c4_compress_store", "c4_validate",
            "indexer_compress_store", "indexer_validate", "indexer_mxfp4_compress_store",
            "indexer_mxfp4_validate", "validate", "e4m3_encode", "e2m1_encode", "last_error",
            "abi_version", "library", "describe", "Tensor", "Dsv4Error", "LIBRARY_PATH"]

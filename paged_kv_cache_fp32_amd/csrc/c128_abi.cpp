@@ -353,6 +353,34 @@ int dsv4_c128_compress_store_varlen(const dsv4_tensor* state_cache,
   return DSV4_OK;
 }
 
+int dsv4_c128_compress_store_varlen_noalloc(
+    const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
+    const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
+    const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,
+    const dsv4_tensor* cos_sin, const dsv4_tensor* k_cache, const dsv4_tensor* kv_slot_mapping,
+    float* compressed_out, void* stream) {
+  static_assert(dsv4::kStaticCompactedMaxTokens == DSV4_VARLEN_NOALLOC_MAX_TOKENS,
+                "the header states the library's limit");
+  dsv4::C128Params p;
+  int rc = validate_all(state_cache, block_table, token_to_req, positions, slot_mapping, rms_w,
+                        eps, cos_sin, k_cache, kv_slot_mapping, &p);
+  if (rc) return rc;
+  if (compressed_out && !aligned16(compressed_out))
+    return fail(DSV4_ERR_ALIGN, "compressed_out must be 16-byte aligned");
+  if (p.num_tokens == 0) return DSV4_OK;
+  if (p.num_tokens > dsv4::kStaticCompactedMaxTokens)
+    return fail(DSV4_ERR_ARG,
+                "the allocation-free compacted schedule takes at most %lld tokens (got %d); "
+                "use dsv4_c128_compress_store_varlen with a workspace",
+                static_cast<long long>(dsv4::kStaticCompactedMaxTokens), p.num_tokens);
+  p.compressed_out = compressed_out;
+  hipError_t err = dsv4::launch_c128_compacted_static(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(DSV4_ERR_LAUNCH, "scratch lookup or kernel launch failed: %s",
+                hipGetErrorString(err));
+  return DSV4_OK;
+}
+
 int dsv4_c4_validate(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
                      const dsv4_tensor* token_to_req, const dsv4_tensor* positions,
                      const dsv4_tensor* slot_mapping, const dsv4_tensor* rms_w, float eps,

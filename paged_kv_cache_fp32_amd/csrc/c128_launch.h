@@ -56,6 +56,12 @@ size_t fanout_workspace_bytes(int64_t num_tokens, int splits);
 // that pass.
 hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stream);
 size_t compacted_workspace_bytes(int64_t num_tokens);
+// The same schedule with its counts and token list in a fixed device array of the library (no
+// workspace, no allocation), for at most kStaticCompactedMaxTokens tokens.  Calls that overlap
+// on one device share the array and race.
+constexpr int kStaticCompactedScanBlocks = 1024;
+constexpr int64_t kStaticCompactedMaxTokens = int64_t(1) << 20;
+hipError_t launch_c128_compacted_static(const C128Params& p, hipStream_t stream);
 // C4 compressor (ratio 4, overlapping 8-row window), one wave per token: c4_kernel.hip.
 // state_bs is the state cache's rows per block.
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream);

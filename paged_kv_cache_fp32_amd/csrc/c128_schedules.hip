@@ -14,9 +14,18 @@
 //    not land in the middle of the state stream.
 
 #include <atomic>
+#include <mutex>
 
 #include "c128_device.h"
 #include "c128_launch.h"
+
+// Scratch of the allocation-free compacted schedule (launch_c128_compacted_static): the scan
+// blocks' counts, then the compacted token list, for at most kStaticCompactedMaxTokens tokens
+// (4 MiB + 4 KiB).  Each device holds its own copy for the life of the process.  Host code must
+// not pass this name to a kernel (on the host it is only a stand-in for the symbol): it takes
+// the device address from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) int32_t
+    scratch[dsv4::kStaticCompactedScanBlocks + dsv4::kStaticCompactedMaxTokens];
 
 namespace dsv4 {
 namespace {
@@ -710,6 +719,49 @@ hipError_t launch_c128_compacted(const C128Params& p, void* ws, hipStream_t stre
                          p, counts, list, chunk, nblocks);
   return launch_kernel(c128_compacted_kernel<false>, dim3(grid), dim3(128 * kRowGroups), stream,
                        p, counts, list, chunk, nblocks);
+}
+
+namespace {
+
+// Device address of `scratch` on each device, resolved with that device current on the first
+// call there.  Written once under the mutex, then read without it.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!addr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!addr) {
+      err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return err;
+      if (!addr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(addr, std::memory_order_release);
+    }
+  }
+  *out = addr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+static_assert(kStaticCompactedScanBlocks == kMaxScanBlocks,
+              "the static scratch starts with one count per scan block");
+
+hipError_t launch_c128_compacted_static(const C128Params& p, hipStream_t stream) {
+  if (p.num_tokens <= 0) return hipSuccess;
+  if (p.num_tokens > kStaticCompactedMaxTokens) return hipErrorInvalidValue;
+  if (compacted_workspace_bytes(p.num_tokens) > sizeof(scratch)) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t err = static_scratch(&ws);
+  if (err != hipSuccess) return err;
+  return launch_c128_compacted(p, ws, stream);
 }
 
 namespace {

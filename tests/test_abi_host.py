@@ -330,6 +330,26 @@ def test_varlen_argument_errors_before_launch():
     assert varlen_call(e) == 0
 
 
+def test_varlen_noalloc_errors_before_launch():
+    """The allocation-free compacted schedule validates like the others, then rejects more
+    tokens than its fixed scratch holds (DSV4_ERR_ARG, naming the limit), all before any HIP
+    call; T == 0 is a no-op."""
+    lib = c128.library()
+    limit = header_constant("DSV4_VARLEN_NOALLOC_MAX_TOKENS")
+    assert limit == 1 << 20 == c128.VARLEN_NOALLOC_MAX_TOKENS
+    head, tail = descriptors_with_tokens(valid_args(), limit + 1)
+    assert lib.dsv4_c128_compress_store_varlen_noalloc(*head, 1e-6, *tail, None, None) == -8
+    assert f"at most {limit}" in c128.last_error()
+    bad = valid_args()
+    bad["k_cache"] = torch.zeros(2, 4, 576, dtype=torch.uint8)
+    head, tail = descriptors_with_tokens(bad, 4)
+    assert lib.dsv4_c128_compress_store_varlen_noalloc(*head, 1e-6, *tail, None, None) == -4
+    head, tail = descriptors_with_tokens(valid_args(), 4)
+    assert lib.dsv4_c128_compress_store_varlen_noalloc(*head, 1e-6, *tail, 8, None) == -6
+    head, tail = descriptors_with_tokens(valid_args(T=0), 0)
+    assert lib.dsv4_c128_compress_store_varlen_noalloc(*head, 1e-6, *tail, None, None) == 0
+
+
 def c4_args(T=4, S=16, sbs=8, bs=4):
     a = valid_args(T=T, S=S, bs=bs)
     a["state_cache"] = torch.zeros(S, sbs, 2048, dtype=torch.float32)

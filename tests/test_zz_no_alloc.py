@@ -1,0 +1,85 @@
+"""The allocation-free compacted schedule (dsv4_c128_compress_store_varlen_noalloc) against the
+compacted schedule with a caller workspace (dsv4_c128_compress_store_varlen), through the C ABI:
+identical k_cache bytes and pooled vectors on two calls in a row, the second on a smaller
+batch, both also within the oracle's pass criteria.  Nothing of the first call's scratch
+contents may leak into the second."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.compare import compare
+from synth.device import DeviceWorkload
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_both(wl):
+    """(bytes, pooled vectors) of the workspace entry point, then of the allocation-free one,
+    each on a fresh copy of the workload's k_cache."""
+    import paged_kv_cache_fp32_amd as c128
+    out = []
+    for noalloc in (False, True):
+        d = DeviceWorkload(wl)
+        comp = torch.full((wl.num_tokens, 512), float("nan"), dtype=torch.float32,
+                          device="cuda")
+        torch.cuda.synchronize()
+        if noalloc:
+            before = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+            c128.compress_store_varlen_noalloc(*d.args(), compressed_out=comp)
+            after = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+            assert after == before, "the binding allocated device memory"
+        else:
+            ws = torch.empty(c128.varlen_workspace_bytes(wl.num_tokens), dtype=torch.uint8,
+                             device="cuda")
+            c128.compress_store_varlen(*d.args(), compressed_out=comp, workspace=ws)
+        torch.cuda.synchronize()
+        body, ok = d.k_cache_bytes()
+        assert ok, "k_cache guard bands were written"
+        out.append((body, comp.cpu().numpy()))
+        del d
+    return out
+
+
+def test_noalloc_matches_the_workspace_entry_point():
+    big = synth.config2()
+    smaller = synth.varlen_prefill("varlen prefill, 16 requests", 1203, 16, 700, 2048, 8192,
+                                   kv_bs=16, cs_rows=4096)
+    assert smaller.num_tokens < big.num_tokens
+    for wl in (big, smaller):
+        announce(f"no-alloc vs workspace: {wl.name} T={wl.num_tokens}")
+        (ref, ref_c), (got, got_c) = run_both(wl)
+        assert np.array_equal(got, ref)
+        assert np.array_equal(np.isnan(got_c), np.isnan(ref_c))
+        assert np.array_equal(np.nan_to_num(got_c), np.nan_to_num(ref_c))
+        rep = compare(wl, got, oracle.run(wl, synth.default_threads()), gpu_compressed=got_c)
+        print(rep.summary(), flush=True)
+        assert rep.ok(), rep.summary()
+        assert rep["written"] == int(wl.written_mask().sum()) > 20
+
+
+def test_noalloc_rejects_more_tokens_than_its_scratch_holds():
+    import paged_kv_cache_fp32_amd as c128
+    announce("no-alloc token limit")
+    wl = synth.decode_batch("limit", 5, 1, 32, 1, 16, kv_bs=4, kv_blocks=1, cs_rows=256)
+    d = DeviceWorkload(wl)
+    n = c128.VARLEN_NOALLOC_MAX_TOKENS + 1
+    big = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    args = list(d.args())
+    for i in (2, 3, 4, 9):   # token_to_req, positions, slot_mapping, kv_slot_mapping
+        args[i] = big
+    before = d.kc_buf.clone()
+    with pytest.raises(c128.Dsv4Error) as e:
+        c128.compress_store_varlen_noalloc(*args)
+    assert e.value.code == -8 and "at most 1048576" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d.kc_buf)
