@@ -116,11 +116,15 @@ typedef struct dsv4_tensor {
  * `eps` is the RMSNorm epsilon.
  *
  * Below 2048 tokens one workgroup handles each token (the single pass).  From
- * 2048 tokens on, a workgroup takes up to 64 tokens and inserts their records
- * after its last state read (the staged schedule), which keeps the k_cache
- * writes out of the state stream.  It merges 8 partial row groups per token
- * instead of 4, so a code can differ from the single pass's by one step of
- * fp32 rounding; both agree with the definition to the same tolerance.
+ * 2048 tokens on, one workgroup per compute unit tests the gate of every token,
+ * ranks the tokens that pass, and takes an equal share of them, so a batch in
+ * which few tokens close a window (chunked prefill) spreads as evenly as one in
+ * which all do; it streams its share in stages of up to 64 tokens and inserts a
+ * stage's records after the stage's last state read, which keeps the k_cache
+ * writes out of the state stream (the staged schedule).  It merges 8 partial
+ * row groups per token instead of 4, so a code can differ from the single
+ * pass's by one step of fp32 rounding; both agree with the definition to the
+ * same tolerance.  No scratch memory, one kernel launch.
  */
 int dsv4_c128_compress_store(const dsv4_tensor* state_cache, const dsv4_tensor* block_table,
                              const dsv4_tensor* token_to_req, const dsv4_tensor* positions,

@@ -179,7 +179,8 @@ def compress_store(state_cache, block_table, token_to_req, positions, slot_mappi
                    cos_sin, k_cache, kv_slot_mapping, stream: int | None = None) -> None:
     """Fused C128 compress -> RMSNorm -> FP8/UE8M0 quant -> RoPE -> paged insert (in place
     on ``k_cache``), enqueued on ``stream`` (default: torch's current stream).  One kernel
-    launch: a workgroup per token below 2048 tokens, the staged schedule from 2048 on."""
+    launch: a workgroup per token below 2048 tokens; from 2048 on, the staged schedule (a
+    workgroup per CU, each taking an equal share of the tokens that close a window)."""
     ts = (state_cache, block_table, token_to_req, positions, slot_mapping, rms_w, cos_sin,
           k_cache, kv_slot_mapping)
     dev = _require_cuda(ts)

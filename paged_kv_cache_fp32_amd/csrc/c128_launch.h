@@ -34,8 +34,9 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
 // Single pass and encoder: c128_kernel.hip.  Every launcher returns the hipError_t of its launch.
 // Batches of kStagedMinTokens and more go to the staged schedule.
 hipError_t launch_c128_compress_store(const C128Params& p, hipStream_t stream);
-// Staged schedule for large batches (c128_schedules.hip): a workgroup of kStagedRowGroups row
-// groups takes up to kStagedMaxTokens tokens and inserts their records after its last state read.
+// Staged schedule for large batches (c128_schedules.hip): one workgroup of kStagedRowGroups row
+// groups per CU takes an equal share of the tokens that pass the gate and streams it in stages
+// of up to kStagedMaxTokens tokens, inserting a stage's records after its last state read.
 constexpr int64_t kStagedMinTokens = 2048;
 constexpr int kStagedMaxTokens = 64;
 constexpr int kStagedRowGroups = 8;

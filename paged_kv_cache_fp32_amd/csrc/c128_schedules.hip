@@ -471,31 +471,99 @@ __global__ void __launch_bounds__(128 * kRowGroups)
 
 
 // ---------------------------------------------------------------------------------------------
-// Staged schedule for large batches.  With one workgroup per token, each token's 584-byte record
-// reaches HBM on its own, in the middle of the state stream; on MI355X those scattered writes
-// cost about 4.5% of the large-batch call (measured: the single pass with its stores switched off
-// runs at the rate of a pure read of the same gather).  Here a workgroup of 8 row groups (16
-// waves, one window block per wave) takes `tokens_per_group` tokens, keeps their records in LDS
-// and inserts them all after its last state read, so the k_cache writes arrive in one burst at
-// the end of the call.
+// Staged schedule (the plain entry point from 2048 tokens on).  With one workgroup per token,
+// each token's 584-byte record reaches HBM on its own, in the middle of the state stream; on
+// MI355X those scattered writes cost about 4.5% of the large-batch call (measured: the single
+// pass with its stores switched off runs at the rate of a pure read of the same gather).  Here a
+// workgroup of 8 row groups (16 waves, one window block per wave at a time) streams a share of
+// the active tokens, keeps their records in LDS and inserts them after the last state read of
+// each stage of up to KMAX tokens, so the k_cache writes leave the state stream.
 //
-//  * Token assignment: with G = gridDim.x, step k of workgroup b takes token k*G + ((b + 3k) mod
-//    G), a permutation of each row of G tokens.  A dense run of active tokens, or prefill window
-//    ends 128 tokens apart, spread over all workgroups instead of queueing on a few.
-//  * Prologue: one thread per (token, window block) resolves the gate, request, window column,
-//    RoPE row and block id of every token of the workgroup at once, into LDS, and one wave lists
-//    the tokens that go on.  Inside the token loop every per-token value then comes from LDS: a
-//    global load after a workgroup barrier cannot be a scalar load (the barrier's fence counts
-//    as a possible write), and a chain of vector loads with full waits in front of every token
-//    costs more than the staging gains.
+//  * One round: the grid is one workgroup per CU (the LDS stage allows no second one), so no
+//    workgroup ever waits for a CU to free up.
+//  * Balanced by rank.  Every workgroup tests the gate of every token (position and state slot:
+//    8 bytes a token, served from L2 once the first workgroups have fetched them) and counts the
+//    tokens that pass per count block of `block_tokens` consecutive tokens, in LDS; the
+//    exclusive prefix of those counts gives each passing token its rank, its index in token
+//    order among the passing tokens, the same in every workgroup.  Workgroup b of G takes ranks
+//    [A*b/G, A*(b+1)/G) of the A passing tokens: every workgroup streams the same number of
+//    windows, within one, whether every token closes a window (a decode batch: 64 consecutive
+//    tokens each at 16384) or one in 128 does (chunked prefill: one or two each).
+//  * A stage takes up to KMAX of the workgroup's ranks.  Its tokens are located by reading the
+//    gates of only the count blocks that hold those ranks again.  Then one thread per (token,
+//    window block) resolves request, window column, RoPE row and block id into LDS, and wave 0
+//    lists the tokens whose indices are all in range.  Inside the token loop every per-token
+//    value comes from LDS: a global load after a workgroup barrier cannot be a scalar load (the
+//    barrier's fence counts as a possible write), and a chain of vector loads with full waits in
+//    front of every token costs more than the staging gains.
 //  * Per token, the same steps as the single pass (stream, row-group merge, fused epilogue);
 //    8 row groups instead of 4, so the fp32 summation order differs from the single pass's.
+constexpr int kStagedCountBlocks = 4096;  // most count blocks (LDS: one int32 each)
+constexpr int kCountUnroll = 8;           // 256-token chunks a wave gates at once
+constexpr int kMaskChunks = 1280;         // batches of up to this many chunks keep gate masks
+constexpr int kLocateUnroll = 4;
+
+__device__ __forceinline__ bool gate_of(int32_t pos, int32_t slot) {
+  return (slot >= 0) & (pos >= 0) & ((pos & (kRatio - 1)) == kRatio - 1);
+}
+
+__device__ __forceinline__ bool gate_open(const C128Params& p, int32_t t) {
+  return gate_of(p.positions[t], p.slot_mapping[t]);
+}
+
+// Gates of U sub-tiles of 64 tokens, sub-tile u starting at token first + u * stride (lane l:
+// token + l).  Every load is issued before any result is used: indices past the batch are
+// clamped to its last token and their gate is closed afterwards.
+template <int U>
+__device__ __forceinline__ void gate_tiles(const C128Params& p, int32_t T, int32_t first,
+                                           int32_t stride, int32_t end, int lane,
+                                           bool (&act)[U]) {
+  int32_t pos[U], slot[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t t = first + u * stride + lane;
+    const int32_t tc = t < T ? t : T - 1;
+    pos[u] = p.positions[tc];
+    slot[u] = p.slot_mapping[tc];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) act[u] = (first + u * stride + lane < end) & gate_of(pos[u], slot[u]);
+}
+
+// The work-item id passed through an empty asm statement.  Per-thread addresses computed from it
+// inside a loop are recomputed there (a few VALU instructions) instead of being hoisted out and
+// kept live, or spilled to scratch, across the window stream.
+__device__ __forceinline__ int fresh_tid() {
+  int t = static_cast<int>(__builtin_amdgcn_workitem_id_x());
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// The last count block whose first rank is <= r, the block that holds rank r (r < A), by one
+// wave in two ballot steps over the non-decreasing prefix: lane l first tests block l * step
+// (step = ceil(nblocks / 64) <= 64), then block c1 + l within the step that holds the answer.
+__device__ __forceinline__ int block_of_rank(const int32_t* pre, int nblocks, int32_t r,
+                                             int lane) {
+  const int step = (nblocks + 63) >> 6;
+  const int c = lane * step;
+  const uint64_t m1 = __builtin_amdgcn_ballot_w64(c < nblocks && pre[c < nblocks ? c : 0] <= r);
+  const int c1 = (63 - __builtin_clzll(m1)) * step;  // pre[0] = 0 <= r: m1 has bit 0
+  const int c2 = c1 + lane;
+  const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && c2 < nblocks &&
+                                                  pre[c2 < nblocks ? c2 : 0] <= r);
+  return c1 + (63 - __builtin_clzll(m2));              // lane 0 (block c1) always passes
+}
+
 template <int RG, int CH, int WPE, int KMAX, bool kDebug>
 __global__ void __launch_bounds__(128 * RG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-c128_staged_kernel(const C128Params p, int32_t tokens_per_group) {
+c128_staged_kernel(const C128Params p, int32_t block_tokens, int32_t nblocks) {
   static_assert(kWindowBlocks % RG == 0, "row groups must split the 16 window blocks");
   static_assert(kStateBlock % CH == 0, "a stage must not straddle two state blocks");
-  static_assert(KMAX * kWindowBlocks <= 128 * RG, "one prologue thread per (token, block)");
+  static_assert(KMAX * kWindowBlocks <= 128 * RG, "one resolve thread per (token, block)");
+  static_assert(KMAX <= 64, "wave 0 lists a stage's tokens, one lane each");
+  static_assert(kStagedCountBlocks <= 4 * 128 * RG, "the prefix takes four counts a thread");
+  constexpr int NW = 2 * RG;    // waves
+  constexpr int NT = 64 * NW;   // threads
   constexpr int NB = kWindowBlocks / RG;  // state blocks per wave
   constexpr int NCH = NB * kStateBlock / CH;
   constexpr int kStagesPerBlock = kStateBlock / CH;
@@ -505,33 +573,203 @@ c128_staged_kernel(const C128Params p, int32_t tokens_per_group) {
   __shared__ float4 lds_l[RG][2][64];
   __shared__ float4 lds_acc[RG][2][64];
   __shared__ float lds_ss[2];
+  __shared__ int32_t lds_pre[kStagedCountBlocks];  // per count block: passing tokens, then the
+                                                   // rank of its first passing token
+  __shared__ int32_t lds_wsum[NW];
+  __shared__ uint64_t lds_mask[kMaskChunks][4];  // per 256-token chunk: ballot j holds the gate of
+                                                 // token 4l + j in bit l
   __shared__ __align__(16) int32_t lds_ids[KMAX][kWindowBlocks];  // -1: out of range
+  __shared__ int32_t lds_tok[KMAX];   // the stage's tokens, in rank order
   __shared__ int32_t lds_rope[KMAX];  // RoPE row; -1: the token is skipped
   __shared__ int32_t lds_kv[KMAX];    // kv slot of a staged record; -1: none
-  __shared__ int32_t lds_list[KMAX];  // the tokens that go on, in order
-  __shared__ int32_t lds_count;
+  __shared__ int32_t lds_list[KMAX];  // 1: the stage entry has every index in range
   __shared__ __align__(16) uint8_t lds_stage[KMAX][kSlotBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = wave & 1;
   const int rg = wave >> 1;
-  const int64_t G = gridDim.x;
-  auto token_of = [&](int k) -> int64_t {
-    return static_cast<int64_t>(k) * G + (static_cast<int64_t>(blockIdx.x) + 3 * k) % G;
-  };
+  const int32_t T = p.num_tokens;  // at most 2^27: tokens and ranks fit in 32 bits
 
-  // ---- prologue: thread (k, i) resolves window block i of the workgroup's k-th token
+  // ---- count pass: tokens that pass the gate, per count block.  Wave w gates the 256-token
+  // chunks w, w + NW, ... of the batch, kCountUnroll of them at a time, every load issued before
+  // any gate is evaluated.  A lane reads 4 consecutive positions and 4 state slots with one
+  // 16-byte load each: per-lane 4-byte loads cost the address unit as much per instruction and
+  // bring a quarter of the bytes, which made the pass 4x slower.  Chunks that end past the batch,
+  // and arrays that are not 16-byte aligned, take 4-byte loads of the tokens that exist.  Each
+  // workgroup starts its walk at its own chunk, spread over the batch.
+  const int32_t nchunk = (T + 255) >> 8;
+  // Up to kMaskChunks chunks (count blocks of one chunk each), the pass keeps every chunk's gate
+  // masks in LDS, and the stages rank their tokens from them; beyond, it adds counts per block
+  // and the stages read the gates of their blocks again.
+  const bool masked = nchunk <= kMaskChunks && block_tokens == 256;
+  if (!masked)
+    for (int c = threadIdx.x; c < nblocks; c += NT) lds_pre[c] = 0;
+  __syncthreads();
   {
-    const int k = threadIdx.x / kWindowBlocks, i = threadIdx.x % kWindowBlocks;
-    if (k < tokens_per_group) {
-      int32_t rope = -1, id = -1;
-      const int64_t t = token_of(k);
-      if (t < p.num_tokens) {
-        const int32_t pos = p.positions[t];
-        const int32_t slot = p.slot_mapping[t];
-        if (slot >= 0 && pos >= 0 && (pos & (kRatio - 1)) == kRatio - 1) {
-          const int32_t win = pos >> 7;
+    const int32_t chunk_per_block = block_tokens >> 8;
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.positions) |
+                       reinterpret_cast<uintptr_t>(p.slot_mapping)) & 15) == 0;
+    const int32_t start =
+        static_cast<int32_t>(static_cast<int64_t>(nchunk) * blockIdx.x / gridDim.x);
+    const int32_t mine = (nchunk - wave + NW - 1) / NW;  // chunks wave + NW*k below nchunk
+    for (int32_t k0 = 0; k0 < mine; k0 += kCountUnroll) {
+      int32_t chunk[kCountUnroll];
+      int4 pos[kCountUnroll], slot[kCountUnroll];
+#pragma unroll
+      for (int u = 0; u < kCountUnroll; ++u) {
+        const int32_t cv = wave + NW * (k0 + u) + start;
+        chunk[u] = cv >= nchunk ? cv - nchunk : cv;
+        const int32_t t0 = chunk[u] * 256 + 4 * lane;
+        if (k0 + u < mine) {  // wave-uniform
+          if (vec && chunk[u] * 256 + 256 <= T) {
+            pos[u] = *reinterpret_cast<const int4*>(p.positions + t0);
+            slot[u] = *reinterpret_cast<const int4*>(p.slot_mapping + t0);
+          } else {
+            int32_t pv[4], sv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int32_t tc = t0 + j < T ? t0 + j : T - 1;
+              pv[j] = p.positions[tc];
+              sv[j] = t0 + j < T ? p.slot_mapping[tc] : -1;
+            }
+            pos[u] = make_int4(pv[0], pv[1], pv[2], pv[3]);
+            slot[u] = make_int4(sv[0], sv[1], sv[2], sv[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCountUnroll; ++u) {
+        if (k0 + u < mine) {
+          const uint64_t m0 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].x, slot[u].x));
+          const uint64_t m1 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].y, slot[u].y));
+          const uint64_t m2 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].z, slot[u].z));
+          const uint64_t m3 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].w, slot[u].w));
+          if (masked) {
+            if (lane < 4) lds_mask[chunk[u]][lane] = lane == 0 ? m0 : lane == 1 ? m1 : lane == 2 ? m2 : m3;
+          } else {
+            const int n = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
+                          __builtin_popcountll(m2) + __builtin_popcountll(m3);
+            if (n != 0 && lane == 0) atomicAdd(&lds_pre[chunk[u] / chunk_per_block], n);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- exclusive prefix of the counts (with masks: of the chunks' popcounts): thread i owns
+  // blocks 4i .. 4i + 3
+  int32_t A;
+  {
+    int32_t v[4];
+    int32_t own = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = threadIdx.x * 4 + k;
+      v[k] = c >= nblocks ? 0
+             : masked     ? __builtin_popcountll(lds_mask[c][0]) +
+                                __builtin_popcountll(lds_mask[c][1]) +
+                                __builtin_popcountll(lds_mask[c][2]) +
+                                __builtin_popcountll(lds_mask[c][3])
+                          : lds_pre[c];
+      own += v[k];
+    }
+    int32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) lds_wsum[wave] = incl;
+    __syncthreads();
+    int32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int32_t x = lds_wsum[w];
+      if (w < wave) before += x;
+      total += x;
+    }
+    int32_t run = before + incl - own;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = threadIdx.x * 4 + k;
+      if (c < nblocks) lds_pre[c] = run;
+      run += v[k];
+    }
+    A = __builtin_amdgcn_readfirstlane(total);
+    if (threadIdx.x < KMAX) lds_tok[threadIdx.x] = -1;  // entries the locate pass does not fill
+  }
+  __syncthreads();
+
+  const int64_t G = gridDim.x;
+  const int32_t lo = static_cast<int32_t>(static_cast<int64_t>(A) * blockIdx.x / G);
+  const int32_t hi = static_cast<int32_t>(static_cast<int64_t>(A) * (blockIdx.x + 1) / G);
+  const int col = half * 256 + lane * 4;
+  const uint32_t ucol = static_cast<uint32_t>(col);
+  const int64_t s0 = p.s0, s1 = p.s1;
+
+  for (int32_t r0 = lo; r0 < hi; r0 += KMAX) {
+    const int32_t r1 = r0 + KMAX < hi ? r0 + KMAX : hi;
+    const int n = r1 - r0;
+    const int tid = fresh_tid();
+    const int slane = tid & 63;
+    // ---- locate the stage's tokens: the waves share the count blocks that hold ranks
+    // r0 .. r1 - 1 and gate their tokens again, in token order
+    {
+      const int cA = __builtin_amdgcn_readfirstlane(block_of_rank(lds_pre, nblocks, r0, slane));
+      const int cB =
+          __builtin_amdgcn_readfirstlane(block_of_rank(lds_pre, nblocks, r1 - 1, slane));
+      for (int c = cA + wave; c <= cB; c += NW) {
+        int32_t run = __builtin_amdgcn_readfirstlane(lds_pre[c]);
+        if (masked) {
+          // lane l holds tokens 4l .. 4l + 3 of the chunk; their ranks follow the passing tokens
+          // of the lanes below, then its own earlier ones
+          const uint64_t below = (uint64_t(1) << slane) - 1;
+          uint64_t m[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m[j] = lds_mask[c][j];
+          int32_t rank = run;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rank += __builtin_popcountll(m[j] & below);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if ((m[j] >> slane) & 1) {
+              if (rank >= r0 && rank < r1) lds_tok[rank - r0] = c * 256 + 4 * slane + j;
+              ++rank;
+            }
+          }
+          continue;
+        }
+        const int32_t b0 = c * block_tokens;
+        const int32_t b1 = b0 + block_tokens < T ? b0 + block_tokens : T;
+        for (int32_t base = b0; base < b1 && run < r1; base += 64 * kLocateUnroll) {
+          bool act[kLocateUnroll];
+          gate_tiles<kLocateUnroll>(p, T, base, 64, b1, slane, act);
+#pragma unroll
+          for (int u = 0; u < kLocateUnroll; ++u) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(act[u]);
+            const int32_t rank = run + static_cast<int32_t>(__builtin_amdgcn_mbcnt_hi(
+                                           static_cast<uint32_t>(m >> 32),
+                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m),
+                                                                     0u)));
+            if (act[u] && rank >= r0 && rank < r1) lds_tok[rank - r0] = base + 64 * u + slane;
+            run += __builtin_popcountll(m);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- resolve: thread (k, i) takes window block i of the stage's k-th token.  The 16
+    // threads of a token are 16 consecutive lanes of one wave, so whether all its indices are in
+    // range is a 16-lane ballot, with no further barrier.
+    {
+      const int k = tid / kWindowBlocks, i = tid % kWindowBlocks;
+      bool ok = false;
+      if (k < n) {
+        int32_t rope = -1, id = -1;
+        const int32_t t = lds_tok[k];
+        if (t >= 0 && t < T && gate_open(p, t)) {
+          const int32_t win = p.positions[t] >> 7;  // window rows 128*win .. 128*win + 127
           const int32_t req = p.token_to_req[t];
           if (req >= 0 && req < p.bt_rows &&
               static_cast<int64_t>(win + 1) * kWindowBlocks <= p.bt_cols &&
@@ -542,89 +780,74 @@ c128_staged_kernel(const C128Params p, int32_t tokens_per_group) {
             id = static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks) ? b : -1;
           }
         }
+        lds_ids[k][i] = id;
+        ok = id >= 0 && rope >= 0;
+        if (i == 0) {
+          lds_rope[k] = rope;
+          lds_kv[k] = -1;
+        }
       }
-      lds_ids[k][i] = id;
-      if (i == 0) {
-        lds_rope[k] = rope;
-        lds_kv[k] = -1;
+      const uint64_t okm = __builtin_amdgcn_ballot_w64(ok);
+      const uint32_t group = static_cast<uint32_t>(okm >> (slane & 48)) & 0xffffu;
+      if (k < n && i == 0) lds_list[k] = group == 0xffffu;  // 1: the entry goes on
+    }
+    __syncthreads();
+
+    for (int k = 0; k < n; ++k) {
+      // every value below is workgroup-uniform (LDS), so all waves meet the barriers
+      if (!__builtin_amdgcn_readfirstlane(lds_list[k])) continue;
+      const int32_t rope_row = __builtin_amdgcn_readfirstlane(lds_rope[k]);
+      int32_t mybt[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        mybt[b] = __builtin_amdgcn_readfirstlane(lds_ids[k][rg * NB + b]);
+      auto rowptr = [&](int ch) {  // wave-uniform
+        return p.state + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
+               static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
+      };
+
+      float ml[4], l[4], acc[4];
+      float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
+      load_rows<CH>(kvA, scA, rowptr(0), s1, ucol);
+#pragma unroll
+      for (int ch = 0; ch < NCH; ch += 2) {
+        load_rows<CH>(kvB, scB, rowptr(ch + 1), s1, ucol);
+        if (ch == 0)
+          update<true, CH>(kvA, scA, ml, l, acc);
+        else
+          update<false, CH>(kvA, scA, ml, l, acc);
+        if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1, ucol);
+        update<false, CH>(kvB, scB, ml, l, acc);
       }
+      const int tl = fresh_tid() & 63;  // epilogue addresses are recomputed per token
+      merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, tl, ml, l, acc);
+      const int32_t t = __builtin_amdgcn_readfirstlane(lds_tok[k]);
+      const int32_t kv = finish_token<kDebug, true>(p, t, rope_row, rg == 0, half, tl,
+                                                    half * 256 + tl * 4, l, acc, lds_ss,
+                                                    lds_stage[k]);
+      if (rg == 0 && half == 0 && tl == 0) lds_kv[k] = kv;
+      // No barrier here: the next token's merge writes lds_ml/l/acc only, which the epilogue
+      // waves have finished reading, and its lds_ss writes follow that merge's barrier.
     }
-  }
-  __syncthreads();
-  // ---- wave 0 lists the tokens that pass the gate with every block id in range (lane k: token
-  // k), so that a sparse group (a prefill batch: about one token in 128 closes a window) costs
-  // only its prologue
-  if (wave == 0) {
-    bool go = false;
-    if (lane < tokens_per_group && lds_rope[lane] >= 0) {
-      const int4* idv = reinterpret_cast<const int4*>(lds_ids[lane]);
-      const int4 a0 = idv[0], a1 = idv[1], a2 = idv[2], a3 = idv[3];
-      go = (a0.x | a0.y | a0.z | a0.w | a1.x | a1.y | a1.z | a1.w | a2.x | a2.y | a2.z | a2.w |
-            a3.x | a3.y | a3.z | a3.w) >= 0;
+
+    // ---- insert the stage's records (8-byte stores: 72 record chunks, then the scale chunk)
+    __syncthreads();
+    constexpr int kChunks = kSlotBytes / 8;
+    for (int idx = tid; idx < n * kChunks; idx += NT) {
+      const int k = idx / kChunks, c = idx - k * kChunks;
+      const int32_t kv_slot = lds_kv[k];  // -1 for entries that did not go on
+      if (kv_slot < 0) continue;
+      const int32_t kb = kv_slot / p.kv_bs;
+      const int32_t ko = kv_slot - kb * p.kv_bs;
+      uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+      uint8_t* dst = c < kRecordBytes / 8
+                         ? blockp + static_cast<int64_t>(ko) * kRecordBytes + 8 * c
+                         : blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+                               static_cast<int64_t>(ko) * kScaleBytes;
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&lds_stage[k][8 * c]);
     }
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(go);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-        static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-    if (go) lds_list[below] = lane;
-    if (lane == 0) lds_count = __builtin_popcountll(mask);
-  }
-  __syncthreads();
-  const int count = __builtin_amdgcn_readfirstlane(lds_count);
-  if (count == 0) return;  // uniform: nothing to stream, nothing to insert
-
-  const int col = half * 256 + lane * 4;
-  const uint32_t ucol = static_cast<uint32_t>(col);
-  const int64_t s0 = p.s0, s1 = p.s1;
-  for (int j = 0; j < count; ++j) {
-    // every value below is workgroup-uniform (LDS), so all waves meet the barriers
-    const int k = __builtin_amdgcn_readfirstlane(lds_list[j]);
-    const int32_t rope_row = __builtin_amdgcn_readfirstlane(lds_rope[k]);
-    int32_t mybt[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) mybt[b] = __builtin_amdgcn_readfirstlane(lds_ids[k][rg * NB + b]);
-    auto rowptr = [&](int ch) {  // wave-uniform
-      return p.state + static_cast<int64_t>(mybt[ch / kStagesPerBlock]) * s0 +
-             static_cast<int64_t>((ch % kStagesPerBlock) * CH) * s1;
-    };
-
-    float ml[4], l[4], acc[4];
-    float4 kvA[CH], scA[CH], kvB[CH], scB[CH];
-    load_rows<CH>(kvA, scA, rowptr(0), s1, ucol);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ch += 2) {
-      load_rows<CH>(kvB, scB, rowptr(ch + 1), s1, ucol);
-      if (ch == 0)
-        update<true, CH>(kvA, scA, ml, l, acc);
-      else
-        update<false, CH>(kvA, scA, ml, l, acc);
-      if (ch + 2 < NCH) load_rows<CH>(kvA, scA, rowptr(ch + 2), s1, ucol);
-      update<false, CH>(kvB, scB, ml, l, acc);
-    }
-    merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
-    const int32_t t = static_cast<int32_t>(token_of(k));
-    const int32_t kv = finish_token<kDebug, true>(p, t, rope_row, rg == 0, half, lane, col, l,
-                                                  acc, lds_ss, lds_stage[k]);
-    if (rg == 0 && half == 0 && lane == 0) lds_kv[k] = kv;
-    // No barrier here: the next token's merge writes lds_ml/l/acc only, which the epilogue
-    // waves have finished reading, and its lds_ss writes follow that merge's barrier.
-  }
-
-  // ---- insert the staged records (8-byte stores: 72 record chunks, then the scale chunk)
-  __syncthreads();
-  constexpr int kChunks = kSlotBytes / 8;
-  for (int idx = threadIdx.x; idx < count * kChunks; idx += 128 * RG) {
-    const int j = idx / kChunks, c = idx - j * kChunks;
-    const int k = lds_list[j];
-    const int32_t kv_slot = lds_kv[k];
-    if (kv_slot < 0) continue;
-    const int32_t kb = kv_slot / p.kv_bs;
-    const int32_t ko = kv_slot - kb * p.kv_bs;
-    uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
-    uint8_t* dst = c < kRecordBytes / 8
-                       ? blockp + static_cast<int64_t>(ko) * kRecordBytes + 8 * c
-                       : blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
-                             static_cast<int64_t>(ko) * kScaleBytes;
-    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&lds_stage[k][8 * c]);
+    if (tid < KMAX) lds_tok[tid] = -1;  // read last by this stage's resolve
+    __syncthreads();  // the next stage rewrites the stage's LDS
   }
 }
 
@@ -786,22 +1009,21 @@ int staged_cu_count() {
 
 hipError_t launch_c128_staged(const C128Params& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  // One round = one workgroup per CU (the LDS stage allows no second one); as many rounds as
-  // kStagedMaxTokens tokens per workgroup need, then the tokens spread evenly over them.
-  const int64_t cus = staged_cu_count();
-  const int64_t per_round = cus * kStagedMaxTokens;
-  const int64_t rounds = (p.num_tokens + per_round - 1) / per_round;
-  const int64_t groups = cus * rounds;
-  const int32_t per_group = static_cast<int32_t>((p.num_tokens + groups - 1) / groups);
+  // One round: a workgroup per CU (the LDS stage allows no second one).  Count blocks of 256
+  // tokens, doubled until at most kStagedCountBlocks of them cover the batch.
+  const int64_t groups = staged_cu_count();
+  int64_t block_tokens = 256;
+  while ((p.num_tokens + block_tokens - 1) / block_tokens > kStagedCountBlocks) block_tokens *= 2;
+  const int32_t nblocks = static_cast<int32_t>((p.num_tokens + block_tokens - 1) / block_tokens);
   const dim3 grid(static_cast<unsigned>(groups));
   const dim3 block(128 * kStagedRowGroups);
   if (p.compressed_out)
     return launch_kernel(
         c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, true>,
-        grid, block, stream, p, per_group);
+        grid, block, stream, p, static_cast<int32_t>(block_tokens), nblocks);
   return launch_kernel(
       c128_staged_kernel<kStagedRowGroups, kStageRows, kStagedWavesPerSimd, kStagedMaxTokens, false>,
-      grid, block, stream, p, per_group);
+      grid, block, stream, p, static_cast<int32_t>(block_tokens), nblocks);
 }
 
 }  // namespace dsv4

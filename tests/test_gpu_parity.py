@@ -439,10 +439,10 @@ def shared(T, seed):
 
 
 @pytest.mark.parametrize("T", [2047, 2048, 8192, 20000])
-def test_staged_threshold_and_rounds(T):
-    """2047 tokens take the single pass and 2048 the staged schedule (one round, 8 tokens per
-    workgroup); 8192 take one round of 32 and 20000 two rounds of 40.  Every record and every pooled vector of the debug
-    entry point agrees with the oracle."""
+def test_staged_threshold_and_stages(T):
+    """2047 tokens take the single pass and 2048 the staged schedule (8 tokens per workgroup of
+    256, one stage); 8192 give 32 tokens each, and 20000 give 78 or 79 each, in two stages.
+    Every record and every pooled vector of the debug entry point agrees with the oracle."""
     rep, *_ = check(shared(T, 5000 + T), label=f"shared pool T={T}")
     assert rep["written"] == T
 
@@ -562,6 +562,85 @@ def test_varlen_many_scan_blocks():
     print(rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
     assert rep["written"] == int(wl.written_mask().sum()) > 1500
+
+
+def test_plain_entry_point_on_the_scattered_batch():
+    """The scattered 262,400-token batch (1,025 chunks of 256 tokens: the staged schedule keeps
+    every chunk's gate masks in LDS) through the plain entry point; the oracle runs on the
+    tokens that close a window."""
+    import dataclasses
+    wl = synth.scattered_batch("scattered", 61, 262400, 8, 64, 1024, kv_bs=64, kv_blocks=64,
+                               cs_rows=8192)
+    announce("scattered T=262400 (plain entry point)")
+    body, _, guards_ok = run_gpu(wl, debug=False)
+    assert guards_ok
+    act = np.nonzero(wl.active_mask())[0]
+    sub = dataclasses.replace(wl, token_to_req=wl.token_to_req[act], positions=wl.positions[act],
+                              slot_mapping=wl.slot_mapping[act],
+                              kv_slot_mapping=wl.kv_slot_mapping[act])
+    rep = compare(sub, body, oracle.run(sub, THREADS))
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == int(wl.written_mask().sum()) > 1500
+
+
+def compare_token_range(wl, body, lo, hi):
+    """Parity of the records of tokens lo .. hi - 1, and of every byte outside all written
+    records, without the oracle's diagnostics for the whole batch: the oracle runs on the
+    sub-batch, and the records of the other written tokens are taken from the GPU bytes into
+    the initial image (so only bytes outside every record are held to it)."""
+    import dataclasses
+    from oracle.compare import written_byte_mask
+    sl = slice(lo, hi)
+    sub = dataclasses.replace(wl, token_to_req=wl.token_to_req[sl], positions=wl.positions[sl],
+                              slot_mapping=wl.slot_mapping[sl],
+                              kv_slot_mapping=wl.kv_slot_mapping[sl])
+    others = wl.written_mask().copy()
+    others[sl] = False
+    init = wl.k_cache_base.copy()
+    m = written_byte_mask(init.size, wl.kv_slot_mapping[others], wl.k_cache.shape[1],
+                          wl.k_cache.strides[0])
+    init[m] = body[m]
+    return compare(sub, body, oracle.run(sub, THREADS), initial_kc_base=init)
+
+
+@pytest.mark.parametrize("T", [327680, 330017])
+def test_staged_beyond_the_gate_masks(T):
+    """Batches at and beyond the largest one whose gate masks fit in LDS (1280 chunks of 256
+    tokens): at 330,017 tokens the staged schedule counts per block and reads the gates of the
+    blocks that hold a stage's tokens again.  Every token is active, so each workgroup runs
+    about 1,290 tokens in stages of 64 (windows share the blocks of a 2048-block pool).  The
+    oracle checks token ranges spread over several workgroups and stages, and every byte
+    outside the written records."""
+    wl = synth.shared_pool_batch(f"shared pool T={T}", 5600, T, 2048, 4, 64, -(-T // 64), 512)
+    announce(f"staged schedule, every token active, T={T}")
+    body, _, guards_ok = run_gpu(wl, debug=False)
+    assert guards_ok
+    for lo, hi in ((0, 1500), (T // 2 - 700, T // 2 + 800), (T - 1500, T)):
+        rep = compare_token_range(wl, body, lo, hi)
+        print(rep.summary(), flush=True)
+        assert rep.ok(), rep.summary()
+        assert rep["written"] == hi - lo
+
+
+def test_staged_sparse_beyond_the_gate_masks():
+    """A 400,000-token scattered batch (about 2,900 tokens close a window) through the plain
+    entry point: beyond the gate masks, with count blocks of 256 tokens, the stages locate their
+    tokens by reading gates again."""
+    import dataclasses
+    wl = synth.scattered_batch("scattered 400k", 71, 400000, 8, 64, 1024, kv_bs=64,
+                               kv_blocks=64, cs_rows=8192)
+    announce("scattered T=400000 (plain entry point)")
+    body, _, guards_ok = run_gpu(wl, debug=False)
+    assert guards_ok
+    act = np.nonzero(wl.active_mask())[0]
+    sub = dataclasses.replace(wl, token_to_req=wl.token_to_req[act], positions=wl.positions[act],
+                              slot_mapping=wl.slot_mapping[act],
+                              kv_slot_mapping=wl.kv_slot_mapping[act])
+    rep = compare(sub, body, oracle.run(sub, THREADS))
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == int(wl.written_mask().sum()) > 2500
 
 
 def test_varlen_nothing_active():
