@@ -499,7 +499,7 @@ __global__ void __launch_bounds__(128 * kRowGroups)
 //  * Per token, the same steps as the single pass (stream, row-group merge, fused epilogue);
 //    8 row groups instead of 4, so the fp32 summation order differs from the single pass's.
 constexpr int kStagedCountBlocks = 4096;  // most count blocks (LDS: one int32 each)
-constexpr int kCountUnroll = 8;           // 256-token chunks a wave gates at once
+constexpr int kCountUnroll = 12;          // 256-token chunks a wave gates at once
 constexpr int kMaskChunks = 1280;         // batches of up to this many chunks keep gate masks
 constexpr int kLocateUnroll = 4;
 
@@ -591,70 +591,73 @@ c128_staged_kernel(const C128Params p, int32_t block_tokens, int32_t nblocks) {
   const int rg = wave >> 1;
   const int32_t T = p.num_tokens;  // at most 2^27: tokens and ranks fit in 32 bits
 
-  // ---- count pass: tokens that pass the gate, per count block.  Wave w gates the 256-token
-  // chunks w, w + NW, ... of the batch, kCountUnroll of them at a time, every load issued before
-  // any gate is evaluated.  A lane reads 4 consecutive positions and 4 state slots with one
-  // 16-byte load each: per-lane 4-byte loads cost the address unit as much per instruction and
-  // bring a quarter of the bytes, which made the pass 4x slower.  Chunks that end past the batch,
-  // and arrays that are not 16-byte aligned, take 4-byte loads of the tokens that exist.  Each
-  // workgroup starts its walk at its own chunk, spread over the batch.
-  const int32_t nchunk = (T + 255) >> 8;
+  // ---- count pass: tokens that pass the gate, per count block.  The batch is read in chunks of
+  // 256 tokens: lane l gates tokens 4l .. 4l + 3 of a chunk with one 16-byte load of positions
+  // and one of state slots (per-lane 4-byte loads cost the address unit as much per instruction
+  // for a quarter of the bytes, which made the pass 4x slower).  Wave w takes the full chunks
+  // w, w + NW, ..., kCountUnroll of them at a time, every load issued before any gate is
+  // evaluated; each workgroup starts its walk at its own chunk, spread over the batch.  Wave 0
+  // then gates the last, partial chunk; arrays that are not 16-byte aligned take 4-byte loads.
   // Up to kMaskChunks chunks (count blocks of one chunk each), the pass keeps every chunk's gate
-  // masks in LDS, and the stages rank their tokens from them; beyond, it adds counts per block
+  // masks in LDS and the stages rank their tokens from them; beyond, it adds counts per block
   // and the stages read the gates of their blocks again.
+  const int32_t nchunk = (T + 255) >> 8;
+  const int32_t nfull = T >> 8;
   const bool masked = nchunk <= kMaskChunks && block_tokens == 256;
+  const int32_t chunk_per_block = block_tokens >> 8;
   if (!masked)
     for (int c = threadIdx.x; c < nblocks; c += NT) lds_pre[c] = 0;
   __syncthreads();
-  {
-    const int32_t chunk_per_block = block_tokens >> 8;
-    const bool vec = ((reinterpret_cast<uintptr_t>(p.positions) |
-                       reinterpret_cast<uintptr_t>(p.slot_mapping)) & 15) == 0;
+  auto record = [&](int32_t chunk, bool g0, bool g1, bool g2, bool g3) {
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(g0);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(g1);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(g2);
+    const uint64_t m3 = __builtin_amdgcn_ballot_w64(g3);
+    if (masked) {
+      if (lane < 4) lds_mask[chunk][lane] = lane == 0 ? m0 : lane == 1 ? m1 : lane == 2 ? m2 : m3;
+    } else {
+      const int n = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
+                    __builtin_popcountll(m2) + __builtin_popcountll(m3);
+      if (n != 0 && lane == 0) atomicAdd(&lds_pre[chunk / chunk_per_block], n);
+    }
+  };
+  // 4-byte gates of the tokens of one chunk that exist
+  auto scalar_chunk = [&](int32_t chunk) {
+    bool g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t t = chunk * 256 + 4 * lane + j;
+      g[j] = t < T && gate_open(p, t);
+    }
+    record(chunk, g[0], g[1], g[2], g[3]);
+  };
+  if (((reinterpret_cast<uintptr_t>(p.positions) |
+        reinterpret_cast<uintptr_t>(p.slot_mapping)) & 15) == 0) {
     const int32_t start =
-        static_cast<int32_t>(static_cast<int64_t>(nchunk) * blockIdx.x / gridDim.x);
-    const int32_t mine = (nchunk - wave + NW - 1) / NW;  // chunks wave + NW*k below nchunk
+        static_cast<int32_t>(static_cast<int64_t>(nfull) * blockIdx.x / gridDim.x);
+    const int32_t mine = (nfull - wave + NW - 1) / NW;  // full chunks wave + NW*k
     for (int32_t k0 = 0; k0 < mine; k0 += kCountUnroll) {
       int32_t chunk[kCountUnroll];
       int4 pos[kCountUnroll], slot[kCountUnroll];
 #pragma unroll
       for (int u = 0; u < kCountUnroll; ++u) {
         const int32_t cv = wave + NW * (k0 + u) + start;
-        chunk[u] = cv >= nchunk ? cv - nchunk : cv;
-        const int32_t t0 = chunk[u] * 256 + 4 * lane;
+        chunk[u] = cv >= nfull ? cv - nfull : cv;
         if (k0 + u < mine) {  // wave-uniform
-          if (vec && chunk[u] * 256 + 256 <= T) {
-            pos[u] = *reinterpret_cast<const int4*>(p.positions + t0);
-            slot[u] = *reinterpret_cast<const int4*>(p.slot_mapping + t0);
-          } else {
-            int32_t pv[4], sv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int32_t tc = t0 + j < T ? t0 + j : T - 1;
-              pv[j] = p.positions[tc];
-              sv[j] = t0 + j < T ? p.slot_mapping[tc] : -1;
-            }
-            pos[u] = make_int4(pv[0], pv[1], pv[2], pv[3]);
-            slot[u] = make_int4(sv[0], sv[1], sv[2], sv[3]);
-          }
+          const int32_t t0 = chunk[u] * 256 + 4 * lane;
+          pos[u] = *reinterpret_cast<const int4*>(p.positions + t0);
+          slot[u] = *reinterpret_cast<const int4*>(p.slot_mapping + t0);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kCountUnroll; ++u) {
-        if (k0 + u < mine) {
-          const uint64_t m0 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].x, slot[u].x));
-          const uint64_t m1 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].y, slot[u].y));
-          const uint64_t m2 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].z, slot[u].z));
-          const uint64_t m3 = __builtin_amdgcn_ballot_w64(gate_of(pos[u].w, slot[u].w));
-          if (masked) {
-            if (lane < 4) lds_mask[chunk[u]][lane] = lane == 0 ? m0 : lane == 1 ? m1 : lane == 2 ? m2 : m3;
-          } else {
-            const int n = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
-                          __builtin_popcountll(m2) + __builtin_popcountll(m3);
-            if (n != 0 && lane == 0) atomicAdd(&lds_pre[chunk[u] / chunk_per_block], n);
-          }
-        }
-      }
+      for (int u = 0; u < kCountUnroll; ++u)
+        if (k0 + u < mine)
+          record(chunk[u], gate_of(pos[u].x, slot[u].x), gate_of(pos[u].y, slot[u].y),
+                 gate_of(pos[u].z, slot[u].z), gate_of(pos[u].w, slot[u].w));
     }
+    if (wave == 0 && nfull < nchunk) scalar_chunk(nfull);
+  } else {
+    for (int32_t c = wave; c < nchunk; c += NW) scalar_chunk(c);
   }
   __syncthreads();
   // ---- exclusive prefix of the counts (with masks: of the chunks' popcounts): thread i owns
