@@ -493,7 +493,7 @@ def sweep(args, path):
             rec["cold_us_median"] = round(float(np.median(percold)) * 1e3, 2)
             rec["cold_gbs"] = round(nbytes / (rec["cold_us_median"] * 1e-6) / 1e9, 1)
         rec["pct_peak_hbm_warm"] = round(100 * rec["warm_gbs"] / PEAK_GBS, 2)
-        if wl.num_tokens <= 1024:
+        if wl.num_tokens <= 1024 and not args.sweep_no_graph:
             rec["graph_us_per_call"] = round(graph_us_per_call(make_calls(dws, splits, varlen,
                                                                           None)), 2)
         if not args.no_cpu_baseline:
@@ -625,7 +625,8 @@ def c4_sweep(want, measure, dev):
 
 def read_line(args):
     """Attainable-bandwidth references on this machine (bench_support probes): a sequential
-    streaming read of 4 GiB (best of a few launch shapes), and a read of the 16-block windows
+    streaming read of 4 GiB (grid-stride, best of a few launch shapes), a sequential read of the
+    same 4 GiB in contiguous chunks per workgroup (best of 30 shapes), and a read of the 16-block windows
     of the 16384-token workload with the compress kernel's lane mapping but none of its
     arithmetic; each with plain loads and with the non-temporal hint."""
     import ctypes
@@ -655,6 +656,23 @@ def read_line(args):
             rec[f"stream{tag}_gbs_{blocks}x{threads}"] = round(gbs, 1)
             best = gbs if best is None else max(best, gbs)
         rec[f"stream{tag}_gbs_best"] = round(best, 1)
+    # contiguous chunks per workgroup: grid x threads x loads per lane (chunk = loads*threads*16 B)
+    out = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+    for nt, tag in ((0, ""), (1, "_nt")):
+        best = None
+        for blocks in (256, 512, 1024, 2048, 4096):
+            for threads in (256, 512):
+                for loads in (4, 8, 16):
+                    def call(b=blocks, t=threads, u=loads, nt=nt):
+                        assert L.probe_stream_chunks(src.data_ptr(), 4 * n, out.data_ptr(), b, t,
+                                                     u, nt, sid) == 0
+                    _, per = time_calls(torch, stream, [call], args.steps, args.warmup)
+                    gbs = 4 * n / (float(np.median(per)) * 1e-3) / 1e9
+                    rec[f"chunks{tag}_gbs_{blocks}x{threads}x{loads}"] = round(gbs, 1)
+                    if best is None or gbs > best[0]:
+                        best = (gbs, f"{blocks}x{threads}x{loads}")
+        rec[f"chunks{tag}_gbs_best"] = round(best[0], 1)
+        rec[f"chunks{tag}_best_shape"] = best[1]
     del src
     torch.cuda.empty_cache()
     wl = synth.config4()
@@ -676,6 +694,82 @@ def read_line(args):
         rec[f"gather{tag}_us"] = round(ms * 1e3, 2)
         rec[f"gather{tag}_gbs"] = round(T * 128 * 4096 / (ms * 1e-3) / 1e9, 1)
     print(json.dumps(rec), flush=True)
+
+
+def read_small_line(args):
+    """Small decode batches (1, 32, 128 and 256 tokens on the decode sweep's pool): the time of a
+    pure read of exactly their windows over every launch shape of the split window-gather probe
+    (S workgroups per window, W waves, L loads in flight per lane; bench_support), next to the
+    plain entry point and the fan-out on the same windows.  Cold (a 1 GiB read before each call)
+    and warm (4 window sets in turn); medians of the per-call event times.  One JSON line per
+    batch size."""
+    import ctypes
+
+    import torch
+
+    import bench_support
+    import paged_kv_cache_fp32_amd as c128
+    import synth
+    from synth.device import DeviceWorkload
+
+    L = bench_support.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    out = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+
+    def med(calls, cold):
+        _, per = time_calls(torch, stream, calls, args.steps, args.warmup,
+                            flush=(lambda: torch.sum(scratch, dim=0, out=sink)) if cold else None)
+        return round(float(np.median(per)) * 1e3, 2)
+
+    _, pool = synth.config3_pool()
+    pool_dev = None
+    for T in (1, 32, 128, 256):
+        dws = []
+        for s in range(4):
+            d = DeviceWorkload(synth.config3(T, state=pool, window_set=s), device=dev,
+                               state=pool_dev)
+            pool_dev = (d.state_buf, d.state)
+            dws.append(d)
+        ids = []
+        for d in dws:
+            wl = d.wl
+            cols = (wl.positions.astype(np.int64) // 128)[:, None] * 16 + np.arange(16)[None, :]
+            idv = np.ascontiguousarray(wl.block_table[np.arange(T)[:, None], cols]).astype(np.int32)
+            assert idv.min() >= 0 and idv.max() < wl.state.shape[0]
+            ids.append(torch.from_numpy(idv).to(dev))
+        s0 = dws[0].state.stride(0)
+        rec = {"mode": "read-small", "tokens": T, "bytes_per_call": T * 128 * 4096}
+        for cold in (False, True):
+            tag = "cold" if cold else "warm"
+            best = None
+            for S in (1, 2, 4, 8):
+                for W in (4, 8, 16):
+                    for Lf in (4, 8, 16, 32):
+                        n = 512 // (S * W)
+                        if Lf > n or n % Lf:
+                            continue
+                        calls = [(lambda i=i, S=S, W=W, Lf=Lf: L.probe_window_read_split(
+                            dws[0].state.data_ptr(), s0, i.data_ptr(), T, S, W, Lf,
+                            out.data_ptr(), sid)) for i in ids]
+                        us = med(calls, cold)
+                        rec[f"read_{tag}_us_S{S}W{W}L{Lf}"] = us
+                        if best is None or us < best[0]:
+                            best = (us, f"S{S}W{W}L{Lf}")
+            rec[f"read_{tag}_best_us"], rec[f"read_{tag}_best_shape"] = best
+            rec[f"plain_{tag}_us"] = med([(lambda d=d: c128.compress_store(*d.args(), stream=sid))
+                                          for d in dws], cold)
+            if T <= 128:
+                wss = [c128.fanout_workspace(T, 0, dev) for _ in dws]
+                rec[f"fanout_{tag}_us"] = med(
+                    [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w, splits=0,
+                                                              stream=sid))
+                     for d, w in zip(dws, wss)], cold)
+        print(json.dumps(rec), flush=True)
+        del dws, ids
 
 
 def copy_line(args):
@@ -712,12 +806,16 @@ def main():
                     help="only the sweep workloads whose name matches this regular expression")
     ap.add_argument("--sweep-steps", type=int, default=0,
                     help="cap on the timed calls per sweep entry (for counter runs)")
+    ap.add_argument("--sweep-no-graph", action="store_true",
+                    help="with --sweep: leave out the timing inside a HIP graph (for counter runs)")
     ap.add_argument("--sweep-splits", action="store_true",
                     help="with --sweep: time every fan-out split count, not only the automatic one")
-    ap.add_argument("--mode", choices=["main", "copy", "read", "sweep"], default="main",
+    ap.add_argument("--mode", choices=["main", "copy", "read", "read-small", "sweep"],
+                    default="main",
                     help="main: the large-batch line (plus --sweep if given); sweep: only the "
                          "--sweep workloads; read / copy: bandwidth references and counter "
-                         "calibration")
+                         "calibration; read-small: pure reads of small batches' windows over "
+                         "launch shapes, beside the entry points")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the C128 compress-store path shards by request "
@@ -730,6 +828,8 @@ def main():
         copy_line(args)
     elif args.mode == "read":
         read_line(args)
+    elif args.mode == "read-small":
+        read_small_line(args)
     elif args.mode == "sweep":
         if not args.sweep:
             sys.exit("--mode sweep needs --sweep PATH")

@@ -29,6 +29,10 @@ def lib():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.probe_stream_read.argtypes = [vp, i64, vp, ci, ci, ci, vp]
         L.probe_stream_read.restype = ci
+        L.probe_stream_chunks.argtypes = [vp, i64, vp, ci, ci, ci, ci, vp]
+        L.probe_stream_chunks.restype = ci
+        L.probe_window_read_split.argtypes = [vp, i64, vp, ci, ci, ci, ci, vp, vp]
+        L.probe_window_read_split.restype = ci
         L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, ci, vp]
         L.probe_block_gather_read.restype = ci
         _lib = L

@@ -46,6 +46,26 @@ __global__ void __launch_bounds__(512) stream_read(const float4* __restrict__ p,
   if (threadIdx.x == 0 || acc == 1234.5f) out[blockIdx.x] = acc;
 }
 
+// Sequential read in contiguous chunks: workgroup w reads chunks w, w + G, ... of U * blockDim.x
+// 16-byte vectors each (U loads per lane, all issued before any is summed).  Consecutive lanes
+// read consecutive vectors, so every wave-wide load is 1 KiB contiguous and a chunk is one
+// contiguous range (32 KiB to 128 KiB).  n4 is a multiple of the chunk size (checked on the host).
+template <int U, bool kNt>
+__global__ void __launch_bounds__(512) stream_chunks(const float4* __restrict__ p, int64_t n4,
+                                                     float* __restrict__ out) {
+  const int64_t chunk4 = static_cast<int64_t>(U) * blockDim.x;
+  float acc = 0.0f;
+  for (int64_t c = blockIdx.x; (c + 1) * chunk4 <= n4; c += gridDim.x) {
+    const float4* base = p + c * chunk4 + threadIdx.x;
+    float4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = ld<kNt>(base + k * blockDim.x);
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  }
+  if (threadIdx.x == 0 || acc == 1234.5f) out[blockIdx.x] = acc;
+}
+
 // 512 lanes: lane l of wave w covers 16-byte vector (w % 2) * 64 + l of each 4 KiB row
 // half pair ... here simply: the workgroup sweeps each 32 KiB block with 512 x 16 B per step.
 template <bool kNt>
@@ -74,7 +94,62 @@ __global__ void __launch_bounds__(512) block_gather_read(const float* __restrict
   if (threadIdx.x == 0 || acc == 1234.5f) out[blockIdx.x] = acc;
 }
 
+// The window gather of small batches, split: token t's window is 16 blocks x 8 rows x 4
+// quarter-rows of 1 KiB (kv left / right, score left / right) = 512 pieces.  Workgroup (t, s)
+// of S per token has W waves; wave w reads a contiguous range of 512 / (S * W) pieces, L one-KiB
+// wave loads in flight at a time (non-temporal, as the compress kernels load).
+template <int L>
+__global__ void __launch_bounds__(1024) window_read_split(const float* __restrict__ pool,
+                                                          int64_t stride0,
+                                                          const int32_t* __restrict__ ids,
+                                                          int S, int W, float* __restrict__ out) {
+  const int t = blockIdx.x, s = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = 512 / (S * W);
+  const int p0 = s * (512 / S) + wave * n;
+  const int32_t* my = ids + static_cast<int64_t>(t) * 16;
+  float acc = 0.0f;
+  for (int k = 0; k < n; k += L) {
+    float4 v[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int p = p0 + k + j;
+      const int b = p >> 5, q = p & 31, r = q >> 2, part = q & 3;
+      const float* a = pool + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(my[b])) * stride0 +
+                       r * 1024 + (part >> 1) * 512 + (part & 1) * 256 + lane * 4;
+      v[j] = ld<true>(reinterpret_cast<const float4*>(a));
+    }
+#pragma unroll
+    for (int j = 0; j < L; ++j) acc += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  }
+  if (threadIdx.x == 0 || acc == 1234.5f) out[t * S + s] = acc;
+}
+
 }  // namespace
+
+// Split window gather of `n_windows` windows (ids: 16 block ids each; pool blocks of 8 rows of
+// 1024 floats at stride0 >= 8192 floats): S in {1, 2, 4, 8} workgroups per window, W in {4, 8, 16}
+// waves, L in {4, 8, 16, 32} loads in flight with L dividing 512 / (S * W); out holds
+// n_windows * S floats.
+extern "C" int probe_window_read_split(const float* pool, int64_t stride0, const int32_t* ids,
+                                       int n_windows, int S, int W, int L, float* out,
+                                       void* stream) {
+  if (!pool || !ids || !out || n_windows < 1 || stride0 < 8192) return -1;
+  if ((S != 1 && S != 2 && S != 4 && S != 8) || (W != 4 && W != 8 && W != 16)) return -1;
+  const int n = 512 / (S * W);
+  if (L > n || n % L) return -1;
+  const dim3 grid(n_windows, S), block(64 * W);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (L) {
+    case 4: window_read_split<4><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
+    case 8: window_read_split<8><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
+    case 16: window_read_split<16><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
+    case 32: window_read_split<32><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
 
 extern "C" int probe_stream_read(const void* p, int64_t bytes, float* out, int blocks,
                                  int threads, int nt, void* stream) {
@@ -98,4 +173,32 @@ extern "C" int probe_block_gather_read(const float* pool, int64_t stride0, const
     block_gather_read<false><<<n_windows, 512, 0, static_cast<hipStream_t>(stream)>>>(
         pool, stride0, ids, out);
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+namespace {
+template <int U>
+int launch_chunks(const void* p, int64_t n4, float* out, int blocks, int threads, int nt,
+                  hipStream_t stream) {
+  if (nt)
+    stream_chunks<U, true><<<blocks, threads, 0, stream>>>(static_cast<const float4*>(p), n4, out);
+  else
+    stream_chunks<U, false><<<blocks, threads, 0, stream>>>(static_cast<const float4*>(p), n4, out);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+}  // namespace
+
+// Sequential chunked read of `bytes` (a multiple of loads * threads * 16) by `blocks`
+// workgroups of `threads` lanes, `loads` 16-byte loads per lane per chunk (4, 8 or 16).
+extern "C" int probe_stream_chunks(const void* p, int64_t bytes, float* out, int blocks,
+                                   int threads, int loads, int nt, void* stream) {
+  if (!p || !out || blocks < 1 || threads < 64 || threads > 512 || threads % 64) return -1;
+  const int64_t chunk = static_cast<int64_t>(loads) * threads * 16;
+  if (bytes < chunk || bytes % chunk) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (loads) {
+    case 4: return launch_chunks<4>(p, bytes / 16, out, blocks, threads, nt, s);
+    case 8: return launch_chunks<8>(p, bytes / 16, out, blocks, threads, nt, s);
+    case 16: return launch_chunks<16>(p, bytes / 16, out, blocks, threads, nt, s);
+    default: return -1;
+  }
 }

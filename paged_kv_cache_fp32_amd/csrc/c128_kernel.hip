@@ -62,12 +62,14 @@ c128_compress_store_kernel(const C128Params p) {
   const int half = wave & 1;
   const int rg = wave >> 1;
 
-  // ---- gate (all values wave-uniform; the whole workgroup takes one path)
+  // ---- gate (all values wave-uniform; the whole workgroup takes one path).  The request id
+  // does not depend on the gate, so it is loaded with the position and the slot: one dependent
+  // round trip less before the block ids.
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
+  const int32_t req = p.token_to_req[t];
   if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
-  const int32_t req = p.token_to_req[t];
   if (req < 0 || req >= p.bt_rows ||
       static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
     return;

@@ -48,9 +48,9 @@ __device__ __forceinline__ Window gate_and_window(const C128Params& p, int32_t t
   Window w{false, 0, nullptr};
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
+  const int32_t req = p.token_to_req[t];  // with the gate's loads: one round trip less
   if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return w;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
-  const int32_t req = p.token_to_req[t];
   if (req < 0 || req >= p.bt_rows || static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
     return w;
   w.rope_row = win * kRatio;
@@ -771,9 +771,11 @@ c128_staged_kernel(const C128Params p, int32_t block_tokens, int32_t nblocks) {
       if (k < n) {
         int32_t rope = -1, id = -1;
         const int32_t t = lds_tok[k];
-        if (t >= 0 && t < T && gate_open(p, t)) {
-          const int32_t win = p.positions[t] >> 7;  // window rows 128*win .. 128*win + 127
-          const int32_t req = p.token_to_req[t];
+        const int32_t tc = t >= 0 && t < T ? t : 0;  // position, slot and request in one round trip
+        const int32_t pos = p.positions[tc], slot = p.slot_mapping[tc];
+        const int32_t req = p.token_to_req[tc];
+        if (t >= 0 && t < T && gate_of(pos, slot)) {
+          const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
           if (req >= 0 && req < p.bt_rows &&
               static_cast<int64_t>(win + 1) * kWindowBlocks <= p.bt_cols &&
               win * kRatio < p.cs_rows) {
