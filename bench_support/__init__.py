@@ -17,6 +17,18 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+class IdxProbe(ctypes.Structure):
+    """The probe_indexer_window_read arguments (struct IdxProbe in stream_probe.hip)."""
+    _fields_ = [("pool", ctypes.c_void_p), ("s0", ctypes.c_int64), ("s1", ctypes.c_int64),
+                ("positions", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+                ("req", ctypes.c_void_p), ("bt", ctypes.c_void_p), ("bt_stride", ctypes.c_int64),
+                ("bt_rows", ctypes.c_int32), ("bt_cols", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int32), ("offs", ctypes.c_void_p),
+                ("cs", ctypes.c_void_p), ("cs_stride", ctypes.c_int64),
+                ("cs_rows", ctypes.c_int32), ("T", ctypes.c_int32), ("kpw", ctypes.c_int32),
+                ("nb_mask", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -35,5 +47,7 @@ def lib():
         L.probe_window_read_split.restype = ci
         L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, ci, vp]
         L.probe_block_gather_read.restype = ci
+        L.probe_indexer_window_read.argtypes = [ctypes.POINTER(IdxProbe), ci, vp, vp]
+        L.probe_indexer_window_read.restype = ci
         _lib = L
     return _lib

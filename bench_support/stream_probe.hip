@@ -6,15 +6,36 @@
 //    ids[16w .. 16w+15] (32 KiB each when stride0 = 8192 floats) with the same
 //    lane-to-16-byte-vector mapping as the compress kernel, summing them: the
 //    compress kernel's exact HBM access pattern without its arithmetic.
-// Each comes with plain loads and with the non-temporal hint the compress kernels use.
-// Both write one float per workgroup so the loads cannot be removed.
+//  * stream_chunks: a sequential read in contiguous chunks per workgroup.
+//  * window_read_split: small batches' windows read with S workgroups per window.
+//  * idx_window_read: the indexer compressor's reads (metadata, 8 half-rows, RoPE row).
+// The first three come with plain loads and with the non-temporal hint the compress kernels
+// use. Each writes one float per workgroup or wave so the loads cannot be removed.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct IdxProbe {
+  const float* pool;
+  int64_t s0, s1;  // floats per pool block, per row
+  const int32_t* positions;
+  const int32_t* slot;
+  const int32_t* req;
+  const int32_t* bt;
+  int64_t bt_stride;
+  int32_t bt_rows, bt_cols, n_blocks;
+  const int64_t* offs;  // mode 1: [T][8] row offsets in floats, -1 for a row not read
+  const float* cs;
+  int64_t cs_stride;
+  int32_t cs_rows;
+  int32_t T, kpw;
+  uint32_t nb_mask;     // mode 2: pool blocks - 1 (a power of two minus one)
+};
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <bool kNt>
 __device__ __forceinline__ float4 ld(const float4* p) {
@@ -126,6 +147,80 @@ __global__ void __launch_bounds__(1024) window_read_split(const float* __restric
   if (threadIdx.x == 0 || acc == 1234.5f) out[t * S + s] = acc;
 }
 
+
+// The indexer compressor's reads without its arithmetic or its record stores.  A wave takes
+// kpw consecutive tokens; lane (k, i) = (lane / 8, lane % 8) resolves window row i of token k;
+// per token the wave loads the 8 half-rows (512 B of kv and 512 B of score each, lane l the
+// 8 bytes at column 2l) and the RoPE row, non-temporal, and sums them.
+//  mode 0: gate, request and block ids read as the compressor reads them (positions,
+//          slot_mapping, token_to_req, then the block table: two dependent round trips);
+//  mode 1: the row offsets precomputed on the host (one round trip: offs and positions);
+//  mode 2: no metadata: token t reads rows 0..7 of pool block (t * 2654435761) & nb_mask.
+
+template <int kMode>
+__global__ void __launch_bounds__(256) idx_window_read(const IdxProbe p, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t tbase = wid * p.kpw;
+  const int mk = lane >> 3, mi = lane & 7;
+  const int64_t mt = tbase + mk;
+  int64_t moff = -1;
+  int32_t mrow = -1;  // RoPE row
+  if (mk < p.kpw && mt < p.T) {
+    if constexpr (kMode == 0) {
+      const int32_t pos = p.positions[mt], s = p.slot[mt], r = p.req[mt];
+      if (s >= 0 && pos >= 0 && (pos & 3) == 3 && r >= 0 && r < p.bt_rows) {
+        const int32_t q = pos - 7 + mi;
+        if (q >= 0 && (q >> 3) < p.bt_cols) {
+          const int32_t b = p.bt[static_cast<int64_t>(r) * p.bt_stride + (q >> 3)];
+          if (static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_blocks))
+            moff = b * p.s0 + (q & 7) * p.s1 + (mi >= 4 ? 128 : 0);
+        }
+        mrow = pos & ~3;
+      }
+    } else if constexpr (kMode == 1) {
+      moff = p.offs[mt * 8 + mi];
+      mrow = p.positions[mt] & ~3;
+    } else {
+      const uint32_t b = static_cast<uint32_t>(mt * 2654435761ull) & p.nb_mask;
+      moff = b * p.s0 + mi * p.s1 + (mi >= 4 ? 128 : 0);
+      mrow = static_cast<int32_t>(mt & 1023) * 4;
+    }
+    if (mrow >= p.cs_rows) mrow = -1;
+  }
+  const int col = 2 * lane;
+  float acc = 0.0f;
+  for (int k = 0; k < p.kpw; ++k) {
+    float2 v[17];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(moff), 8 * k + i);
+      const uint32_t hi = __builtin_amdgcn_readlane(
+          static_cast<uint32_t>(static_cast<uint64_t>(moff) >> 32), 8 * k + i);
+      const int64_t off = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+      if (off >= 0) {
+        const f32x2 a = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x2*>(p.pool + off + col));
+        const f32x2 b = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x2*>(p.pool + off + 256 + col));
+        v[2 * i] = make_float2(a.x, a.y);
+        v[2 * i + 1] = make_float2(b.x, b.y);
+      } else {
+        v[2 * i] = v[2 * i + 1] = make_float2(0.f, 0.f);
+      }
+    }
+    const int32_t row = __builtin_amdgcn_readlane(mrow, 8 * k);
+    v[16] = make_float2(0.f, 0.f);
+    if (row >= 0 && lane >= 32) {
+      const float* c = p.cs + static_cast<int64_t>(row) * p.cs_stride;
+      v[16] = make_float2(c[lane - 32], c[lane]);
+    }
+#pragma unroll
+    for (int j = 0; j < 17; ++j) acc += v[j].x + v[j].y;
+  }
+  if (lane == 0 || acc == 1234.5f) out[wid] = acc;
+}
 }  // namespace
 
 // Split window gather of `n_windows` windows (ids: 16 block ids each; pool blocks of 8 rows of
@@ -201,4 +296,23 @@ extern "C" int probe_stream_chunks(const void* p, int64_t bytes, float* out, int
     case 16: return launch_chunks<16>(p, bytes / 16, out, blocks, threads, nt, s);
     default: return -1;
   }
+}
+
+// Indexer window reads (idx_window_read above) of p.T tokens, p.kpw (1..8) per wave, 4 waves a
+// workgroup; out holds one float per wave.
+extern "C" int probe_indexer_window_read(const IdxProbe* p, int mode, float* out, void* stream) {
+  if (!p || !out || !p->pool || p->T < 1 || p->kpw < 1 || p->kpw > 8 || !p->cs) return -1;
+  if (mode == 0 && (!p->positions || !p->slot || !p->req || !p->bt)) return -1;
+  if (mode == 1 && (!p->offs || !p->positions)) return -1;
+  if (mode == 2 && ((p->nb_mask + 1u) & p->nb_mask) != 0) return -1;
+  const int64_t waves = (static_cast<int64_t>(p->T) + p->kpw - 1) / p->kpw;
+  const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: idx_window_read<0><<<grid, block, 0, st>>>(*p, out); break;
+    case 1: idx_window_read<1><<<grid, block, 0, st>>>(*p, out); break;
+    case 2: idx_window_read<2><<<grid, block, 0, st>>>(*p, out); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
