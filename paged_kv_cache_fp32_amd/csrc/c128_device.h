@@ -44,17 +44,43 @@ __device__ __forceinline__ float bf16_round(float x) {
   return __uint_as_float(bf16_bits(x) << 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Wave reductions with DPP lane moves instead of LDS-crossbar shuffles (ds_bpermute).  Lanes
+// i ^ 1 and i ^ 2 are quad permutes; after them every quad holds one value, so the mirror within
+// 8 lanes pairs each quad with its neighbour, and then the mirror within 16 lanes pairs the two
+// half-rows.  The four 16-lane rows are combined through readlane.  Every lane gets the result;
+// the whole wave must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
 }
 
-// Max over the 16-lane group holding one 64-column quantisation block.
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the wave: quads, half-rows and rows by DPP, then (row0 + row1) + (row2 + row3).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// Max over each 16-lane row (a 64-column quantisation block of 4 columns a lane, or a 32-dim
+// MXFP4 block of 2 a lane); exact in any order.
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = __builtin_fmaxf(v, dpp_move<0xb1>(v));
+  v = __builtin_fmaxf(v, dpp_move<0x4e>(v));
+  v = __builtin_fmaxf(v, dpp_move<0x141>(v));
+  return __builtin_fmaxf(v, dpp_move<0x140>(v));
+}
+
+// Max over the wave.
+__device__ __forceinline__ float wave_max(float v) {
+  v = group16_max(v);
+  return __builtin_fmaxf(__builtin_fmaxf(lane_value(v, 0), lane_value(v, 16)),
+                         __builtin_fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -60,12 +60,6 @@ __device__ __forceinline__ float2 load_stream2(const float* p) {
   return make_float2(v.x, v.y);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
 // E2M1 code of x in the low nibble: the nearest of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6,
 // ties to the even code, beyond 6 saturating to 6; bit 3 is the sign of x.  Each comparison
 // is one midpoint between neighbouring magnitudes: strict where the code below it is the even

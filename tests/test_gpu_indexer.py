@@ -174,3 +174,32 @@ def test_indexer_extreme_scores(score_std):
     wl = idx_batch(300, 950 + int(score_std), score_std=score_std)
     rep, *_ = check(wl, f"indexer scores std {score_std:g}")
     assert rep["written"] == 300
+
+
+@pytest.mark.parametrize("T", [8193, 20001])
+def test_indexer_pipelined_mixed_batch(T):
+    """Beyond 8192 tokens a wave takes several tokens and keeps the next token's loads in flight
+    while it reduces the current one.  Every kind of token in one batch there: a seeded 30% with
+    state slot -1, 10% moved off the window boundary, windows at position 3, 5% with no kv slot
+    and five request ids out of range; T leaves a ragged last wave."""
+    wl = idx_batch(T, 1300 + T, k_max=40)
+    rng = np.random.default_rng(1300 + T)
+    wl.slot_mapping[rng.random(T) < 0.3] = -1
+    wl.positions[rng.random(T) < 0.1] -= 1
+    wl.kv_slot_mapping[rng.random(T) < 0.05] = -1
+    bad = rng.choice(T, 5, replace=False)
+    wl.token_to_req[bad] = wl.block_table.shape[0]
+    assert (wl.positions == 3).any()
+    announce(f"indexer pipelined mixed batch T={T}")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    gate = (wl.slot_mapping >= 0) & (wl.positions % 4 == 3)
+    assert (orc.status[~gate] == 0).all() and (orc.status[bad[gate[bad]]] == -1).all()
+    computed = gate & (wl.token_to_req < wl.block_table.shape[0])
+    assert np.isfinite(comp[computed]).all() and np.isnan(comp[~computed]).all()
+    wl.kv_slot_mapping[orc.status == -1] = -1
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == int((orc.status == 1).sum()) > T // 2
