@@ -138,10 +138,13 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
   int64_t moff = 0;
   bool mok = false;
   if (mk < tokens_per_wave && mt < p.num_tokens) {
+    // the request id and the kv slot are loaded with the gate's position and slot: the block
+    // ids then wait for one round trip, not two
     mpos = p.positions[mt];
     const int32_t slot = p.slot_mapping[mt];
+    const int32_t req = p.token_to_req[mt];
+    const int32_t kvs = mi == 0 ? p.kv_slot_mapping[mt] : -1;
     if (slot >= 0 && mpos >= 0 && (mpos & (kC4Ratio - 1)) == kC4Ratio - 1) {
-      const int32_t req = p.token_to_req[mt];
       mok = req >= 0 && req < p.bt_rows && mpos / state_bs < p.bt_cols &&
             (mpos & ~(kC4Ratio - 1)) < p.cs_rows;
       const int32_t q = mpos - (kC4Rows - 1) + mi;
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
         moff = static_cast<int64_t>(b) * p.s0 + static_cast<int64_t>(boff) * p.s1 +
                (mi >= kC4Ratio ? kHead : 0);
       }
-      if (mi == 0) mkv = p.kv_slot_mapping[mt];
+      mkv = kvs;
     }
   }
   const uint64_t good = __builtin_amdgcn_ballot_w64(mok);
