@@ -26,8 +26,9 @@ single-token, decode-batch and varlen-prefill workloads on every entry point
 large-batch line).  ``--mode copy`` times a plain device-to-device copy (the
 counter-calibration kernel for rocprofv3); ``--mode read`` times streaming and
 window-gather reads, with plain and non-temporal loads (the attainable-bandwidth
-reference lines); ``--mode read-small`` and ``--mode read-idx`` time pure reads of the
-small decode batches' windows and of the indexer's access pattern beside the kernels.
+reference lines); ``--mode read-small``, ``--mode read-idx`` and ``--mode read-c4`` time pure
+reads of the small decode batches' windows and of the indexer's and the C4 compressor's access
+patterns beside the kernels.
 """
 
 from __future__ import annotations
@@ -773,14 +774,15 @@ def read_small_line(args):
         del dws, ids
 
 
-def read_idx_line(args):
-    """The indexer compressor's 16384-token decode batch beside read-only probes of its access
-    pattern (bench_support idx_window_read, no arithmetic and no record stores): block ids
-    resolved through the block table as the kernel resolves them (mode 0), row offsets
-    precomputed on the host (mode 1: one dependent round trip less), and no metadata at all
-    (mode 2: token t reads a whole hashed pool block), each at 1, 2, 4 and 8 tokens per wave;
-    and a sequential read of 128 MiB, about the batch's state bytes, in contiguous chunks.
-    Cold (a 1 GiB read before each call) and warm medians of the per-call event times."""
+def read_pattern_line(args, c4: bool):
+    """A neighbouring compressor's 16384-token decode batch (the indexer's, or with ``c4`` the C4
+    compressor's) beside read-only probes of its access pattern (bench_support idx_window_read,
+    no arithmetic and no record stores): block ids resolved through the block table as the
+    kernel resolves them (mode 0), row offsets precomputed on the host (mode 1: one dependent
+    round trip less), and no metadata at all (mode 2: token t reads a whole hashed pool block),
+    each at 1, 2, 4 and 8 tokens per wave; and a sequential read of about the batch's state bytes
+    in contiguous chunks.  Cold (a 1 GiB read before each call) and warm medians of the per-call
+    event times."""
     import ctypes
 
     import torch
@@ -803,26 +805,34 @@ def read_idx_line(args):
                             flush=(lambda: torch.sum(scratch, dim=0, out=sink)) if cold else None)
         return round(float(np.median(per)) * 1e3, 2)
 
-    wl = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024,
-                                    512, kv_bs=64, kv_blocks=256, cs_rows=4096)
+    if c4:
+        wl = synth.c4_decode_batch("c4 decode T=16384", 1005, 16384, 16384 * 2, 1024, 512,
+                                   kv_bs=64, kv_blocks=256, cs_rows=4096)
+        half, kernel, probe_fn = 512, c128.c4_compress_store, L.probe_c4_window_read
+    else:
+        wl = synth.indexer_decode_batch("indexer decode T=16384", 1006, 16384, 16384 * 2, 1024,
+                                        512, kv_bs=64, kv_blocks=256, cs_rows=4096)
+        half, kernel, probe_fn = 128, c128.indexer_compress_store, L.probe_indexer_window_read
     d = DeviceWorkload(wl, device=dev)
     st = d.state
     T = wl.num_tokens
     s0, s1 = st.stride(0), st.stride(1)
     nb = st.shape[0]
-    if st.shape[1] != 8 or s1 < 512 or not np.array_equal(wl.token_to_req, np.arange(T)):
-        raise RuntimeError("the indexer probe expects 8-row state blocks and one token a request")
+    if st.shape[1] != 8 or s1 < 4 * half or not np.array_equal(wl.token_to_req, np.arange(T)):
+        raise RuntimeError("the window-read probe expects 8-row state blocks and one token a "
+                           "request")
     pos = wl.positions.astype(np.int64)
     q = pos[:, None] - 7 + np.arange(8)[None, :]
     blk = wl.block_table[np.arange(T)[:, None], np.maximum(q, 0) // 8].astype(np.int64)
-    offs = np.where(q >= 0, blk * s0 + (q % 8) * s1 + np.where(np.arange(8) >= 4, 128, 0), -1)
-    span = (nb - 1) * s0 + 7 * s1 + 512
-    if offs.max() + 384 > span or blk.min() < 0 or blk.max() >= nb or pos.max() >= 4096:
-        raise RuntimeError("indexer probe offsets out of range")
+    offs = np.where(q >= 0, blk * s0 + (q % 8) * s1 + np.where(np.arange(8) >= 4, half, 0), -1)
+    span = (nb - 1) * s0 + 7 * s1 + 4 * half
+    if offs.max() + 3 * half > span or blk.min() < 0 or blk.max() >= nb or pos.max() >= 4096:
+        raise RuntimeError("window-read probe offsets out of range")
     offs_dev = torch.from_numpy(np.ascontiguousarray(offs)).to(dev)
     nb_mask = (1 << (nb.bit_length() - 1)) - 1
     nbytes = algorithmic_bytes(wl)
-    seq = torch.ones(1 << 25, dtype=torch.float32, device=dev)  # 128 MiB
+    seq_floats = (1 << 27) if c4 else (1 << 25)  # 512 MiB / 128 MiB
+    seq = torch.ones(seq_floats, dtype=torch.float32, device=dev)
 
     def probe(kpw):
         return bench_support.IdxProbe(
@@ -831,19 +841,18 @@ def read_idx_line(args):
             d.block_table.shape[0], d.block_table.shape[1], nb, offs_dev.data_ptr(),
             d.cos_sin.data_ptr(), d.cos_sin.stride(0), d.cos_sin.shape[0], T, kpw, nb_mask)
 
-    rec = {"mode": "read-idx", "tokens": T, "algorithmic_bytes": nbytes,
-           "probe_state_bytes": int((offs >= 0).sum()) * 1024, "seq_bytes": 4 * seq.numel()}
+    rec = {"mode": "read-c4" if c4 else "read-idx", "tokens": T, "algorithmic_bytes": nbytes,
+           "probe_state_bytes": int((offs >= 0).sum()) * 8 * half,
+           "seq_bytes": 4 * seq.numel()}
     for cold in (False, True):
         tag = "cold" if cold else "warm"
-        rec[f"kernel_{tag}_us"] = med([lambda: c128.indexer_compress_store(*d.args(),
-                                                                           stream=sid)], cold)
+        rec[f"kernel_{tag}_us"] = med([lambda: kernel(*d.args(), stream=sid)], cold)
         for mode in (0, 1, 2):
             for kpw in (1, 2, 4, 8):
                 prm = probe(kpw)
 
                 def call(prm=prm, mode=mode):
-                    assert L.probe_indexer_window_read(ctypes.byref(prm), mode, out.data_ptr(),
-                                                       sid) == 0
+                    assert probe_fn(ctypes.byref(prm), mode, out.data_ptr(), sid) == 0
                 rec[f"probe{mode}_{tag}_us_kpw{kpw}"] = med([call], cold)
         for blocks, threads, loads in ((256, 256, 8), (512, 256, 4), (1024, 256, 8),
                                        (2048, 256, 4)):
@@ -851,7 +860,7 @@ def read_idx_line(args):
                 assert L.probe_stream_chunks(seq.data_ptr(), 4 * seq.numel(), out.data_ptr(),
                                              b, t, u, 1, sid) == 0
             rec[f"seq_{tag}_us_{blocks}x{threads}x{loads}"] = med([call], cold)
-        log(f"[read-idx] {tag} done")
+        log(f"[{rec['mode']}] {tag} done")
     print(json.dumps(rec), flush=True)
 
 
@@ -893,7 +902,8 @@ def main():
                     help="with --sweep: leave out the timing inside a HIP graph (for counter runs)")
     ap.add_argument("--sweep-splits", action="store_true",
                     help="with --sweep: time every fan-out split count, not only the automatic one")
-    ap.add_argument("--mode", choices=["main", "copy", "read", "read-small", "read-idx", "sweep"],
+    ap.add_argument("--mode", choices=["main", "copy", "read", "read-small", "read-idx", "read-c4",
+                                          "sweep"],
                     default="main",
                     help="main: the large-batch line (plus --sweep if given); sweep: only the "
                          "--sweep workloads; read / copy: bandwidth references and counter "
@@ -913,8 +923,8 @@ def main():
         read_line(args)
     elif args.mode == "read-small":
         read_small_line(args)
-    elif args.mode == "read-idx":
-        read_idx_line(args)
+    elif args.mode in ("read-idx", "read-c4"):
+        read_pattern_line(args, args.mode == "read-c4")
     elif args.mode == "sweep":
         if not args.sweep:
             sys.exit("--mode sweep needs --sweep PATH")

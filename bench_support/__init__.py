@@ -18,7 +18,8 @@ def build(force: bool = True) -> str:
 
 
 class IdxProbe(ctypes.Structure):
-    """The probe_indexer_window_read arguments (struct IdxProbe in stream_probe.hip)."""
+    """The probe_indexer_window_read / probe_c4_window_read arguments (struct IdxProbe in
+    stream_probe.hip)."""
     _fields_ = [("pool", ctypes.c_void_p), ("s0", ctypes.c_int64), ("s1", ctypes.c_int64),
                 ("positions", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("req", ctypes.c_void_p), ("bt", ctypes.c_void_p), ("bt_stride", ctypes.c_int64),
@@ -49,5 +50,7 @@ def lib():
         L.probe_block_gather_read.restype = ci
         L.probe_indexer_window_read.argtypes = [ctypes.POINTER(IdxProbe), ci, vp, vp]
         L.probe_indexer_window_read.restype = ci
+        L.probe_c4_window_read.argtypes = [ctypes.POINTER(IdxProbe), ci, vp, vp]
+        L.probe_c4_window_read.restype = ci
         _lib = L
     return _lib

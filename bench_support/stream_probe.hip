@@ -8,7 +8,7 @@
 //    compress kernel's exact HBM access pattern without its arithmetic.
 //  * stream_chunks: a sequential read in contiguous chunks per workgroup.
 //  * window_read_split: small batches' windows read with S workgroups per window.
-//  * idx_window_read: the indexer compressor's reads (metadata, 8 half-rows, RoPE row).
+//  * idx_window_read: the indexer and C4 compressors' reads (metadata, 8 half-rows, RoPE row).
 // The first three come with plain loads and with the non-temporal hint the compress kernels
 // use. Each writes one float per workgroup or wave so the loads cannot be removed.
 
@@ -148,17 +148,22 @@ __global__ void __launch_bounds__(1024) window_read_split(const float* __restric
 }
 
 
-// The indexer compressor's reads without its arithmetic or its record stores.  A wave takes
-// kpw consecutive tokens; lane (k, i) = (lane / 8, lane % 8) resolves window row i of token k;
-// per token the wave loads the 8 half-rows (512 B of kv and 512 B of score each, lane l the
-// 8 bytes at column 2l) and the RoPE row, non-temporal, and sums them.
+// The indexer or C4 compressor's reads without its arithmetic or its record stores.  A wave
+// takes kpw consecutive tokens; lane (k, i) = (lane / 8, lane % 8) resolves window row i of
+// token k; per token the wave loads the 8 half-rows (indexer: 512 B of kv and 512 B of score
+// each; C4: 2 KiB of each) and the RoPE row, non-temporal, and sums them.
 //  mode 0: gate, request and block ids read as the compressor reads them (positions,
 //          slot_mapping, token_to_req, then the block table: two dependent round trips);
 //  mode 1: the row offsets precomputed on the host (one round trip: offs and positions);
 //  mode 2: no metadata: token t reads rows 0..7 of pool block (t * 2654435761) & nb_mask.
 
-template <int kMode>
+template <int kMode, bool kC4>
 __global__ void __launch_bounds__(256) idx_window_read(const IdxProbe p, float* __restrict__ out) {
+  // head 128 (indexer): a row is kv 2 x 128 | score 2 x 128, lane l loads 8 bytes at column 2l
+  // of each half-row; head 512 (C4): kv 2 x 512 | score 2 x 512, lane l loads 16 bytes at
+  // columns 4l and 256 + 4l of each half-row
+  constexpr int kHalf = kC4 ? 512 : 128;      // floats in the kv (or score) half of a row
+  constexpr int kScore = 2 * kHalf;           // score part of a row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -175,7 +180,7 @@ __global__ void __launch_bounds__(256) idx_window_read(const IdxProbe p, float* 
         if (q >= 0 && (q >> 3) < p.bt_cols) {
           const int32_t b = p.bt[static_cast<int64_t>(r) * p.bt_stride + (q >> 3)];
           if (static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_blocks))
-            moff = b * p.s0 + (q & 7) * p.s1 + (mi >= 4 ? 128 : 0);
+            moff = b * p.s0 + (q & 7) * p.s1 + (mi >= 4 ? kHalf : 0);
         }
         mrow = pos & ~3;
       }
@@ -184,40 +189,70 @@ __global__ void __launch_bounds__(256) idx_window_read(const IdxProbe p, float* 
       mrow = p.positions[mt] & ~3;
     } else {
       const uint32_t b = static_cast<uint32_t>(mt * 2654435761ull) & p.nb_mask;
-      moff = b * p.s0 + mi * p.s1 + (mi >= 4 ? 128 : 0);
+      moff = b * p.s0 + mi * p.s1 + (mi >= 4 ? kHalf : 0);
       mrow = static_cast<int32_t>(mt & 1023) * 4;
     }
     if (mrow >= p.cs_rows) mrow = -1;
   }
-  const int col = 2 * lane;
   float acc = 0.0f;
   for (int k = 0; k < p.kpw; ++k) {
-    float2 v[17];
+    int64_t off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(moff), 8 * k + i);
       const uint32_t hi = __builtin_amdgcn_readlane(
           static_cast<uint32_t>(static_cast<uint64_t>(moff) >> 32), 8 * k + i);
-      const int64_t off = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-      if (off >= 0) {
-        const f32x2 a = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x2*>(p.pool + off + col));
-        const f32x2 b = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x2*>(p.pool + off + 256 + col));
-        v[2 * i] = make_float2(a.x, a.y);
-        v[2 * i + 1] = make_float2(b.x, b.y);
-      } else {
-        v[2 * i] = v[2 * i + 1] = make_float2(0.f, 0.f);
-      }
+      off[i] = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
     }
     const int32_t row = __builtin_amdgcn_readlane(mrow, 8 * k);
-    v[16] = make_float2(0.f, 0.f);
-    if (row >= 0 && lane >= 32) {
-      const float* c = p.cs + static_cast<int64_t>(row) * p.cs_stride;
-      v[16] = make_float2(c[lane - 32], c[lane]);
-    }
+    if constexpr (kC4) {
+      float4 v[8][4];
 #pragma unroll
-    for (int j = 0; j < 17; ++j) acc += v[j].x + v[j].y;
+      for (int i = 0; i < 8; ++i) {
+        if (off[i] >= 0) {
+          const float* r = p.pool + off[i] + 4 * lane;
+          v[i][0] = ld<true>(reinterpret_cast<const float4*>(r));
+          v[i][1] = ld<true>(reinterpret_cast<const float4*>(r + 256));
+          v[i][2] = ld<true>(reinterpret_cast<const float4*>(r + kScore));
+          v[i][3] = ld<true>(reinterpret_cast<const float4*>(r + kScore + 256));
+        } else {
+          v[i][0] = v[i][1] = v[i][2] = v[i][3] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row >= 0) {
+        const float* cs = p.cs + static_cast<int64_t>(row) * p.cs_stride;
+        const int j = lane & 15;
+        c = make_float4(cs[2 * j], cs[2 * j + 1], cs[32 + 2 * j], cs[33 + 2 * j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc += (v[i][h].x + v[i][h].y) + (v[i][h].z + v[i][h].w);
+      acc += (c.x + c.y) + (c.z + c.w);
+    } else {
+      float2 v[17];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (off[i] >= 0) {
+          const f32x2 a = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x2*>(p.pool + off[i] + 2 * lane));
+          const f32x2 b = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x2*>(p.pool + off[i] + kScore + 2 * lane));
+          v[2 * i] = make_float2(a.x, a.y);
+          v[2 * i + 1] = make_float2(b.x, b.y);
+        } else {
+          v[2 * i] = v[2 * i + 1] = make_float2(0.f, 0.f);
+        }
+      }
+      v[16] = make_float2(0.f, 0.f);
+      if (row >= 0 && lane >= 32) {
+        const float* c = p.cs + static_cast<int64_t>(row) * p.cs_stride;
+        v[16] = make_float2(c[lane - 32], c[lane]);
+      }
+#pragma unroll
+      for (int j = 0; j < 17; ++j) acc += v[j].x + v[j].y;
+    }
   }
   if (lane == 0 || acc == 1234.5f) out[wid] = acc;
 }
@@ -298,9 +333,12 @@ extern "C" int probe_stream_chunks(const void* p, int64_t bytes, float* out, int
   }
 }
 
-// Indexer window reads (idx_window_read above) of p.T tokens, p.kpw (1..8) per wave, 4 waves a
-// workgroup; out holds one float per wave.
-extern "C" int probe_indexer_window_read(const IdxProbe* p, int mode, float* out, void* stream) {
+// Window reads of the indexer compressor (head 128) or of the C4 compressor (head 512) with
+// the kernel's lane mapping (idx_window_read above): p.T tokens, p.kpw (1..8) per wave, 4 waves
+// a workgroup; out holds one float per wave.
+namespace {
+template <bool kC4>
+int launch_window_read(const IdxProbe* p, int mode, float* out, void* stream) {
   if (!p || !out || !p->pool || p->T < 1 || p->kpw < 1 || p->kpw > 8 || !p->cs) return -1;
   if (mode == 0 && (!p->positions || !p->slot || !p->req || !p->bt)) return -1;
   if (mode == 1 && (!p->offs || !p->positions)) return -1;
@@ -309,10 +347,19 @@ extern "C" int probe_indexer_window_read(const IdxProbe* p, int mode, float* out
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (mode) {
-    case 0: idx_window_read<0><<<grid, block, 0, st>>>(*p, out); break;
-    case 1: idx_window_read<1><<<grid, block, 0, st>>>(*p, out); break;
-    case 2: idx_window_read<2><<<grid, block, 0, st>>>(*p, out); break;
+    case 0: idx_window_read<0, kC4><<<grid, block, 0, st>>>(*p, out); break;
+    case 1: idx_window_read<1, kC4><<<grid, block, 0, st>>>(*p, out); break;
+    case 2: idx_window_read<2, kC4><<<grid, block, 0, st>>>(*p, out); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+}  // namespace
+
+extern "C" int probe_indexer_window_read(const IdxProbe* p, int mode, float* out, void* stream) {
+  return launch_window_read<false>(p, mode, out, stream);
+}
+
+extern "C" int probe_c4_window_read(const IdxProbe* p, int mode, float* out, void* stream) {
+  return launch_window_read<true>(p, mode, out, stream);
 }

@@ -65,6 +65,9 @@ constexpr int64_t kStaticCompactedMaxTokens = int64_t(1) << 20;
 hipError_t launch_c128_compacted_static(const C128Params& p, hipStream_t stream);
 // C4 compressor (ratio 4, overlapping 8-row window), one wave per token: c4_kernel.hip.
 // state_bs is the state cache's rows per block.
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream);
 // Indexer FP8 compressor (head 128, ratio 4, overlapping window): indexer_kernel.hip.
 hipError_t launch_indexer_compress_store(const C128Params& p, int32_t state_bs,

@@ -992,11 +992,9 @@ hipError_t launch_c128_compacted_static(const C128Params& p, hipStream_t stream)
   return launch_c128_compacted(p, ws, stream);
 }
 
-namespace {
-
-// Compute units of the current device (the staged grid is sized in whole rounds of one
-// workgroup per CU); looked up once per device, 256 on MI355X.
-int staged_cu_count() {
+// Compute units of the current device (the staged grid, and the C4 kernel's wide shape, are
+// sized in whole rounds of one workgroup per CU); looked up once per device, 256 on MI355X.
+int device_cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1010,13 +1008,11 @@ int staged_cu_count() {
   return n;
 }
 
-}  // namespace
-
 hipError_t launch_c128_staged(const C128Params& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
   // One round: a workgroup per CU (the LDS stage allows no second one).  Count blocks of 256
   // tokens, doubled until at most kStagedCountBlocks of them cover the batch.
-  const int64_t groups = staged_cu_count();
+  const int64_t groups = device_cu_count();
   int64_t block_tokens = 256;
   while ((p.num_tokens + block_tokens - 1) / block_tokens > kStagedCountBlocks) block_tokens *= 2;
   const int32_t nblocks = static_cast<int32_t>((p.num_tokens + block_tokens - 1) / block_tokens);

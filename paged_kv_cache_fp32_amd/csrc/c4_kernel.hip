@@ -15,15 +15,20 @@
 //    is a 1 KiB contiguous segment of a row.  All loads of a window (up to 8 rows x 4 vectors,
 //    non-temporal) are issued before any arithmetic; the per-column softmax is a plain max /
 //    exp2-sum over registers.  No barrier anywhere: waves are independent.
-//  * A wave takes 1 to 8 consecutive tokens (enough waves for 2 per SIMD first).  Their
-//    metadata is resolved up front with one lane per (token, window row): gate, request, block
-//    column, block id and range checks in two rounds of loads, so the token loop only moves row
+//  * A wave takes 1 to 8 tokens (enough waves for 2 per SIMD first).  Their metadata is
+//    resolved up front with one lane per (token, window row): gate, request, block column,
+//    block id and range checks in two rounds of loads, so the token loop only moves row
 //    offsets from lanes to scalars and streams.
+//  * Small batches run 4-wave workgroups, each wave on consecutive tokens.  From 8192 tokens,
+//    while one round covers the batch, a workgroup is 12 waves (one per CU, 3 per SIMD); it
+//    gates all of its tokens first and deals the passing ones out to its waves in turn.
 //  * Epilogue within the wave: RMSNorm by one wave reduction; a 64-column quant block is 16
 //    lanes of v0 (blocks 0..3) or of v1 (blocks 4..6); lanes 48..63 hold the RoPE dims in v1.
-//    Records go to the wave's LDS stage and reach the k_cache after the wave's last state
-//    read: measured on MI355X, the same 584-byte records stored token by token cost about 12%
-//    of the call, because the writes land in the middle of the HBM read stream.
+//    Records go to the wave's LDS stage and reach the k_cache after the last state read of
+//    every wave of the workgroup: measured on MI355X, the same 584-byte records stored token by
+//    token cost about 12% of the call, and stored at the end of each wave about 8% (16384
+//    tokens), because the writes land in the middle of the HBM read stream.  Holding a whole
+//    CU's records to the end of its reads takes most of that back.
 //
 // HBM-bound gather-reduce again (about 0.6 flop per byte): no MFMA.
 
@@ -36,9 +41,12 @@ namespace {
 constexpr int kC4Ratio = 4;
 constexpr int kC4Rows = 2 * kC4Ratio;       // previous window + current window
 constexpr int kC4ScoreOffset = 2 * kHead;   // score part of a row: 2 x 512 columns in
-constexpr int kC4WavesPerGroup = 4;         // waves per workgroup
+constexpr int kC4NarrowWaves = 4;           // waves per workgroup, small batches
+constexpr int kC4WideWaves = 12;            // waves per workgroup from kC4WideMinTokens on
+constexpr int kC4WideMinTokens = 8192;
 constexpr int kC4MaxTokensPerWave = 8;      // 8 tokens x 8 window rows = the 64 lanes
 constexpr int kC4TargetWaves = 2048;        // 2 waves per SIMD on 256 CUs
+constexpr int kC4WideTargetWaves = 3072;    // 3 per SIMD: one 12-wave workgroup per CU
 constexpr int kC4WavesPerSimd = 3;          // room for all 32 window loads in flight
 
 // Per-column softmax-weighted sum over NR rows held in registers (scores scaled to log2).
@@ -112,52 +120,104 @@ __device__ __forceinline__ uint8_t scale_byte(int e) {
   return static_cast<uint8_t>(b < 0 ? 0 : (b > 255 ? 255 : b));
 }
 
-template <bool kDebug, int WPE>
-__global__ void __launch_bounds__(64 * kC4WavesPerGroup)
+template <bool kDebug, int WPE, int NW>
+__global__ void __launch_bounds__(64 * NW)
     __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     c4_compress_store_kernel(const C128Params p, int32_t state_bs, int32_t state_bs_log2,
                              int32_t tokens_per_wave) {
-  __shared__ __align__(16) uint8_t stage_all[kC4WavesPerGroup][kC4MaxTokensPerWave * kSlotBytes];
-  __shared__ int32_t slot_all[kC4WavesPerGroup][kC4MaxTokensPerWave];
+  __shared__ __align__(16) uint8_t stage_all[NW][kC4MaxTokensPerWave * kSlotBytes];
+  __shared__ int32_t slot_all[NW][kC4MaxTokensPerWave];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all[wave];
   int32_t* slot_of = slot_all[wave];
-  const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * kC4WavesPerGroup + wave) *
-                        tokens_per_wave;
+  const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * NW + wave) * tokens_per_wave;
   if (lane < kC4MaxTokensPerWave) slot_of[lane] = -1;
 
+  // ---- wide workgroups deal their tokens out: one lane per token of the workgroup's range
+  // loads its gate, request id and kv slot; the tokens that pass are listed in LDS and wave w
+  // takes list entries w, w + NW, w + 2 NW, ..., so that every wave reads about as many
+  // windows before the workgroup's barrier.  Narrow workgroups keep each wave's consecutive
+  // tokens.
+  constexpr bool kDeal = NW > kC4NarrowWaves;
+  constexpr int kDealMax = kDeal ? NW * kC4MaxTokensPerWave : 1;
+  static_assert(!kDeal || kDealMax <= 128, "the dealt range must fit the first two waves");
+  __shared__ int32_t deal_tok[kDealMax];
+  __shared__ int32_t deal_meta[kDealMax][3];  // position, request, kv slot
+  __shared__ int32_t deal_count[2];
+  const int64_t gbase = static_cast<int64_t>(blockIdx.x) * NW * tokens_per_wave;
+  int32_t my_tokens = tokens_per_wave;
+  if constexpr (kDeal) {
+    const int tid = static_cast<int>(threadIdx.x);
+    bool pass = false;
+    int32_t pos = -1, req = -1, kvs = -1;
+    if (tid < NW * tokens_per_wave && gbase + tid < p.num_tokens) {
+      const int64_t t = gbase + tid;
+      pos = p.positions[t];
+      const int32_t slot = p.slot_mapping[t];
+      req = p.token_to_req[t];
+      kvs = p.kv_slot_mapping[t];
+      pass = slot >= 0 && pos >= 0 && (pos & (kC4Ratio - 1)) == kC4Ratio - 1;
+    }
+    const uint64_t passing = __builtin_amdgcn_ballot_w64(pass);
+    if (wave < 2 && lane == 0) deal_count[wave] = __popcll(passing);
+    __syncthreads();
+    if (pass) {
+      const int e = (wave == 1 ? deal_count[0] : 0) +
+                    static_cast<int>(__popcll(passing & ((1ull << lane) - 1)));
+      deal_tok[e] = tid;
+      deal_meta[e][0] = pos;
+      deal_meta[e][1] = req;
+      deal_meta[e][2] = kvs;
+    }
+    const int n = deal_count[0] + deal_count[1];
+    __syncthreads();
+    my_tokens = n > wave ? (n - wave + NW - 1) / NW : 0;
+  }
+
   // ---- metadata of the wave's tokens, one lane per (token k, window row i): gate, request,
-  // block column, block id and their range checks, all in two rounds of loads.  A token goes
-  // on only if every one of its 8 lanes passes.  Rows before position 0 (pos 3, i < 4) are not
+  // block column, block id and their range checks.  The request id and the kv slot come with
+  // the gate's position and slot, so the block ids wait for one round trip.  A token goes on
+  // only if every one of its 8 lanes passes.  Rows before position 0 (pos 3, i < 4) are not
   // read and need no block.
   const int mk = lane >> 3, mi = lane & 7;
-  const int64_t mt = tbase + mk;
   int32_t mpos = -1, mkv = -1;
   int64_t moff = 0;
   bool mok = false;
-  if (mk < tokens_per_wave && mt < p.num_tokens) {
-    // the request id and the kv slot are loaded with the gate's position and slot: the block
-    // ids then wait for one round trip, not two
-    mpos = p.positions[mt];
-    const int32_t slot = p.slot_mapping[mt];
-    const int32_t req = p.token_to_req[mt];
-    const int32_t kvs = mi == 0 ? p.kv_slot_mapping[mt] : -1;
-    if (slot >= 0 && mpos >= 0 && (mpos & (kC4Ratio - 1)) == kC4Ratio - 1) {
-      mok = req >= 0 && req < p.bt_rows && mpos / state_bs < p.bt_cols &&
-            (mpos & ~(kC4Ratio - 1)) < p.cs_rows;
-      const int32_t q = mpos - (kC4Rows - 1) + mi;
-      if (mok && q >= 0) {
-        const int32_t bcol = state_bs_log2 >= 0 ? q >> state_bs_log2 : q / state_bs;
-        const int32_t boff = q - bcol * state_bs;
-        const int32_t b = p.block_table[static_cast<int64_t>(req) * p.bt_stride + bcol];
-        mok = static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks);
-        moff = static_cast<int64_t>(b) * p.s0 + static_cast<int64_t>(boff) * p.s1 +
-               (mi >= kC4Ratio ? kHead : 0);
-      }
-      mkv = kvs;
+  bool gate = false;
+  int32_t req = -1, kvs = -1;
+  if constexpr (kDeal) {
+    if (mk < my_tokens) {
+      const int e = wave + NW * mk;
+      mpos = deal_meta[e][0];
+      req = deal_meta[e][1];
+      kvs = deal_meta[e][2];
+      gate = true;
     }
+  } else {
+    const int64_t mt = tbase + mk;
+    if (mk < tokens_per_wave && mt < p.num_tokens) {
+      mpos = p.positions[mt];
+      const int32_t slot = p.slot_mapping[mt];
+      req = p.token_to_req[mt];
+      kvs = mi == 0 ? p.kv_slot_mapping[mt] : -1;
+      gate = slot >= 0 && mpos >= 0 && (mpos & (kC4Ratio - 1)) == kC4Ratio - 1;
+    }
+  }
+  if (gate) {
+    mok = req >= 0 && req < p.bt_rows && mpos / state_bs < p.bt_cols &&
+          (mpos & ~(kC4Ratio - 1)) < p.cs_rows;
+    const int32_t q = mpos - (kC4Rows - 1) + mi;
+    if (mok && q >= 0) {
+      const int32_t bcol = state_bs_log2 >= 0 ? q >> state_bs_log2 : q / state_bs;
+      const int32_t boff = q - bcol * state_bs;
+      const int32_t b = p.block_table[static_cast<int64_t>(req) * p.bt_stride + bcol];
+      mok = static_cast<uint32_t>(b) < static_cast<uint32_t>(p.n_state_blocks);
+      moff = static_cast<int64_t>(b) * p.s0 + static_cast<int64_t>(boff) * p.s1 +
+             (mi >= kC4Ratio ? kHead : 0);
+    }
+    mkv = kvs;
   }
   const uint64_t good = __builtin_amdgcn_ballot_w64(mok);
 
@@ -166,7 +226,7 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
   const float4 w1 = *reinterpret_cast<const float4*>(p.rms_w + 256 + col);
   const int j = lane & 15;  // RoPE pair index of lanes 48..63
 
-  for (int k = 0; k < tokens_per_wave; ++k) {
+  for (int k = 0; k < my_tokens; ++k) {
     if (((good >> (8 * k)) & 0xffu) != 0xffu) continue;  // inactive or an index out of range
     const int32_t pos = __builtin_amdgcn_readlane(mpos, 8 * k);
     const int32_t kv_slot = __builtin_amdgcn_readlane(mkv, 8 * k);
@@ -203,7 +263,8 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
                         c[3] * rrms * w0.w, c[4] * rrms * w1.x, c[5] * rrms * w1.y,
                         c[6] * rrms * w1.z, c[7] * rrms * w1.w};
     if constexpr (kDebug) {
-      float* out = p.compressed_out + (tbase + k) * kHead;
+      const int64_t t = kDeal ? gbase + deal_tok[wave + NW * k] : tbase + k;
+      float* out = p.compressed_out + t * kHead;
       *reinterpret_cast<float4*>(out + col) = make_float4(c[0], c[1], c[2], c[3]);
       *reinterpret_cast<float4*>(out + 256 + col) = make_float4(c[4], c[5], c[6], c[7]);
     }
@@ -246,9 +307,10 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
     if (lane == 0) slot_of[k] = kv_slot;
   }
 
-  // ---- paged insert of every staged record, after the wave's last state read: the k_cache
-  // writes reach HBM in bursts instead of interleaved with the read stream (8-byte stores;
-  // records and scale groups are 8-byte aligned)
+  // ---- paged insert of every staged record, after the last state read of every wave of the
+  // workgroup: the k_cache writes reach HBM in bursts instead of interleaved with the read
+  // stream (8-byte stores; records and scale groups are 8-byte aligned)
+  __syncthreads();
   for (int k = 0; k < tokens_per_wave; ++k) {
     const int32_t kv_slot = slot_of[k];
     if (kv_slot < 0) continue;
@@ -268,28 +330,44 @@ __global__ void __launch_bounds__(64 * kC4WavesPerGroup)
   }
 }
 
-int c4_tokens_per_wave(int64_t num_tokens) {
-  // Enough waves for 2 per SIMD (2048 on 256 CUs x 4 SIMDs) before a wave takes more than
-  // one token; at most kC4MaxTokensPerWave (its LDS stage).
-  int64_t k = (num_tokens + kC4TargetWaves - 1) / kC4TargetWaves;
+// Tokens per wave: enough waves for the target (2 per SIMD for the narrow shape, 3 for the wide
+// one) before a wave takes more than one token; at most kC4MaxTokensPerWave (its LDS stage).
+int c4_tokens_per_wave(int64_t num_tokens, int64_t target_waves) {
+  const int64_t k = (num_tokens + target_waves - 1) / target_waves;
   return static_cast<int>(k < 1 ? 1 : (k > kC4MaxTokensPerWave ? kC4MaxTokensPerWave : k));
+}
+
+template <int NW>
+hipError_t launch_c4_as(const C128Params& p, int32_t state_bs, int64_t target_waves,
+                        hipStream_t stream) {
+  const int32_t kpw = c4_tokens_per_wave(p.num_tokens, target_waves);
+  const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
+  const dim3 grid(static_cast<unsigned>((waves + NW - 1) / NW));
+  const dim3 block(64 * NW);
+  const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
+  if (p.compressed_out)
+    return launch_kernel(c4_compress_store_kernel<true, kC4WavesPerSimd, NW>, grid, block, stream,
+                         p, state_bs, lg, kpw);
+  return launch_kernel(c4_compress_store_kernel<false, kC4WavesPerSimd, NW>, grid, block, stream,
+                       p, state_bs, lg, kpw);
 }
 
 }  // namespace
 
+// Small batches take 4-wave workgroups, spread over as many CUs as possible.  From
+// kC4WideMinTokens on, while one round of them covers the batch, a workgroup is 12 waves (one
+// per CU), so that the records of a whole CU wait in LDS until all of its waves have read their
+// windows: the record writes then meet far less of the read stream.  Beyond one round the
+// narrow shape stays, as a second round of wide workgroups would run as a tail.
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  const int32_t kpw = c4_tokens_per_wave(p.num_tokens);
-  const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
-  const int64_t groups = (waves + kC4WavesPerGroup - 1) / kC4WavesPerGroup;
-  const dim3 grid(static_cast<unsigned>(groups));
-  const dim3 block(64 * kC4WavesPerGroup);
-  const int32_t lg = (state_bs & (state_bs - 1)) == 0 ? __builtin_ctz(state_bs) : -1;
-  if (p.compressed_out)
-    return launch_kernel(c4_compress_store_kernel<true, kC4WavesPerSimd>, grid, block, stream, p,
-                         state_bs, lg, kpw);
-  return launch_kernel(c4_compress_store_kernel<false, kC4WavesPerSimd>, grid, block, stream, p,
-                       state_bs, lg, kpw);
+  if (p.num_tokens >= kC4WideMinTokens) {
+    const int64_t kpw = c4_tokens_per_wave(p.num_tokens, kC4WideTargetWaves);
+    const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
+    if ((waves + kC4WideWaves - 1) / kC4WideWaves <= device_cu_count())
+      return launch_c4_as<kC4WideWaves>(p, state_bs, kC4WideTargetWaves, stream);
+  }
+  return launch_c4_as<kC4NarrowWaves>(p, state_bs, kC4TargetWaves, stream);
 }
 
 }  // namespace dsv4

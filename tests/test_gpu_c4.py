@@ -219,3 +219,43 @@ def test_c4_extreme_scores(score_std):
     wl = c4_batch(300, 900 + int(score_std), score_std=score_std)
     rep, *_ = check(wl, f"c4 scores std {score_std:g}")
     assert rep["written"] == 300
+
+
+@pytest.mark.parametrize("T", [8192, 13001])
+def test_c4_wide_workgroups_mixed_batch(T):
+    """From 8192 tokens, while one round of 12-wave workgroups (one per CU) covers the batch, a
+    workgroup gates all of its tokens first and deals the passing ones out to its waves.  Every
+    kind of token in one such batch: a seeded 30% with state slot -1, 10% moved off the window
+    boundary, windows at position 3, 5% with no kv slot and five request ids out of range; T
+    leaves a ragged last workgroup."""
+    wl = c4_batch(T, 1500 + T, k_max=40)
+    rng = np.random.default_rng(1500 + T)
+    wl.slot_mapping[rng.random(T) < 0.3] = -1
+    wl.positions[rng.random(T) < 0.1] -= 1
+    wl.kv_slot_mapping[rng.random(T) < 0.05] = -1
+    bad = rng.choice(T, 5, replace=False)
+    wl.token_to_req[bad] = wl.block_table.shape[0]
+    assert (wl.positions == 3).any()
+    announce(f"c4 wide workgroups, mixed batch T={T}")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    gate = (wl.slot_mapping >= 0) & (wl.positions % 4 == 3)
+    assert (orc.status[~gate] == 0).all() and (orc.status[bad[gate[bad]]] == -1).all()
+    computed = gate & (wl.token_to_req < wl.block_table.shape[0])
+    assert np.isfinite(comp[computed]).all() and np.isnan(comp[~computed]).all()
+    wl.kv_slot_mapping[orc.status == -1] = -1
+    rep = compare(wl, body, orc, gpu_compressed=comp)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == int((orc.status == 1).sum()) > T // 2
+
+
+def test_c4_wide_workgroups_sparse_prefill():
+    """A chunked prefill of about 14k tokens (one wide round; about a quarter of them close a
+    window, and 10% of the slots are dropped)."""
+    wl = synth.c4_varlen_prefill("c4 varlen prefill 32 req", 1203, 32, 1024, 4096, kv_bs=64,
+                                 cs_rows=8192)
+    assert 8192 <= wl.num_tokens <= 24576
+    rep, *_ = check(wl, f"c4 sparse prefill T={wl.num_tokens}")
+    assert rep["written"] == int(wl.written_mask().sum()) > 2000
