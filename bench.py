@@ -574,14 +574,17 @@ def c4_slices(wl, T, n_sets):
 
 
 def indexer_sweep(want, measure, dev, fp4=False):
-    """Indexer compressor: decode batches cut from one 16384-token batch (512 MiB pool); fp4:
-    the same inputs into the MXFP4 cache."""
+    """Indexer compressor: decode batches cut from one 16384-token batch (512 MiB pool), and that
+    batch with its kv slots in token order; fp4: the same inputs into the MXFP4 cache."""
+    import dataclasses
+
     import synth
     from synth.device import DeviceWorkload
     sizes = (1, 128, 1024, 4096, 16384)
     kind = "indexer mxfp4" if fp4 else "indexer"
     names = [f"{kind} decode T={T}" for T in sizes]
-    if not any(want(n) for n in names):
+    seq_name = f"{kind} decode T=16384 seq slots"
+    if not any(want(n) for n in names + [seq_name]):
         return
     big = synth.indexer_decode_batch(f"{kind} decode T=16384", 1006, 16384, 16384 * 2, 1024,
                                      512, kv_bs=64, kv_blocks=256, cs_rows=4096, fp4=fp4)
@@ -596,6 +599,11 @@ def indexer_sweep(want, measure, dev, fp4=False):
             dws.append(d)
         measure(name, dws, 1000 if T <= 4096 else 400)
         del dws
+    if not fp4 and want(seq_name):
+        # the same batch with kv slots in token order (token t -> slot t): a cache block's
+        # records, and their scales, then come from neighbouring waves
+        wl = dataclasses.replace(big, kv_slot_mapping=np.arange(16384, dtype=np.int32))
+        measure(seq_name, [DeviceWorkload(wl, device=dev, state=pool_dev)], 400)
 
 
 def c4_sweep(want, measure, dev):
