@@ -94,3 +94,18 @@ def test_graph_c4_and_indexer():
     d = DeviceWorkload(fx)
     announce("graph: indexer mxfp4")
     capture_and_replay(d, lambda: c128.indexer_mxfp4_compress_store(*d.args()))
+
+
+def test_graph_c4_wide_workgroups_and_indexer_runs():
+    """9000 tokens: C4 takes its 12-wave workgroups that gate and deal their tokens, and the
+    indexer's waves take two tokens each."""
+    c4 = synth.c4_decode_batch("graph c4 wide", 1306, 9000, 18008, 16, 16, kv_bs=16,
+                               kv_blocks=1125, cs_rows=128)
+    d = DeviceWorkload(c4)
+    announce("graph: c4 wide workgroups (9000 tokens)")
+    capture_and_replay(d, lambda: c128.c4_compress_store(*d.args()))
+    ix = synth.indexer_decode_batch("graph indexer 9000", 1307, 9000, 18008, 16, 16, kv_bs=16,
+                                    kv_blocks=1125, cs_rows=128)
+    d = DeviceWorkload(ix)
+    announce("graph: indexer (9000 tokens)")
+    capture_and_replay(d, lambda: c128.indexer_compress_store(*d.args()))
