@@ -221,13 +221,14 @@ def test_c4_extreme_scores(score_std):
     assert rep["written"] == 300
 
 
-@pytest.mark.parametrize("T", [8192, 13001])
+@pytest.mark.parametrize("T", [8192, 13001, 30001])
 def test_c4_wide_workgroups_mixed_batch(T):
     """From 8192 tokens, while one round of 12-wave workgroups (one per CU) covers the batch, a
-    workgroup gates all of its tokens first and deals the passing ones out to its waves.  Every
-    kind of token in one such batch: a seeded 30% with state slot -1, 10% moved off the window
-    boundary, windows at position 3, 5% with no kv slot and five request ids out of range; T
-    leaves a ragged last workgroup."""
+    workgroup gates all of its tokens first and deals the passing ones out to its waves (up to 16
+    tokens a wave, resolved 8 at a time: 30001 tokens take 10).  Every kind of token in one such
+    batch: a seeded 30% with state slot -1, 10% moved off the window boundary, windows at
+    position 3, 5% with no kv slot and five request ids out of range; T leaves a ragged last
+    workgroup."""
     wl = c4_batch(T, 1500 + T, k_max=40)
     rng = np.random.default_rng(1500 + T)
     wl.slot_mapping[rng.random(T) < 0.3] = -1
@@ -251,11 +252,12 @@ def test_c4_wide_workgroups_mixed_batch(T):
     assert rep["written"] == int((orc.status == 1).sum()) > T // 2
 
 
-def test_c4_wide_workgroups_sparse_prefill():
-    """A chunked prefill of about 14k tokens (one wide round; about a quarter of them close a
-    window, and 10% of the slots are dropped)."""
-    wl = synth.c4_varlen_prefill("c4 varlen prefill 32 req", 1203, 32, 1024, 4096, kv_bs=64,
-                                 cs_rows=8192)
-    assert 8192 <= wl.num_tokens <= 24576
+@pytest.mark.parametrize("nreq,seed", [(32, 1203), (64, 1202)])
+def test_c4_wide_workgroups_sparse_prefill(nreq, seed):
+    """Chunked prefills of about 14k and 32k tokens (one wide round, one or two batches a wave;
+    about a quarter of the tokens close a window, and 10% of the slots are dropped)."""
+    wl = synth.c4_varlen_prefill(f"c4 varlen prefill {nreq} req", seed, nreq, 1024, 4096,
+                                 kv_bs=64, cs_rows=8192)
+    assert 8192 <= wl.num_tokens <= 49152
     rep, *_ = check(wl, f"c4 sparse prefill T={wl.num_tokens}")
     assert rep["written"] == int(wl.written_mask().sum()) > 2000
