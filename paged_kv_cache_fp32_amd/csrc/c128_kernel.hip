@@ -64,11 +64,13 @@ c128_compress_store_kernel(const C128Params p) {
 
   // ---- gate (all values wave-uniform; the whole workgroup takes one path).  The request id
   // does not depend on the gate, so it is loaded with the position and the slot: one dependent
-  // round trip less before the block ids.
+  // round trip less before the block ids.  Its sign test joins the gate's own tests in one
+  // branch; with the gate branching first, the compiler sinks the request load below it, into
+  // a round trip of its own.
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
   const int32_t req = p.token_to_req[t];
-  if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return;
+  if ((slot < 0) | (pos < 0) | ((pos & (kRatio - 1)) != kRatio - 1) | (req < 0)) return;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
   if (req < 0 || req >= p.bt_rows ||
       static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)

@@ -48,8 +48,11 @@ __device__ __forceinline__ Window gate_and_window(const C128Params& p, int32_t t
   Window w{false, 0, nullptr};
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
-  const int32_t req = p.token_to_req[t];  // with the gate's loads: one round trip less
-  if (slot < 0 || pos < 0 || (pos & (kRatio - 1)) != kRatio - 1) return w;
+  // The request id is loaded with the gate's loads (one dependent round trip less before the
+  // block ids), and its sign test joins the gate's tests in one branch: with the gate
+  // branching first, the compiler sinks the request load below it, into a round trip of its own.
+  const int32_t req = p.token_to_req[t];
+  if ((slot < 0) | (pos < 0) | ((pos & (kRatio - 1)) != kRatio - 1) | (req < 0)) return w;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
   if (req < 0 || req >= p.bt_rows || static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
     return w;
