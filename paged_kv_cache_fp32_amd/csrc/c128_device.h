@@ -85,6 +85,21 @@ __device__ __forceinline__ float wave_max(float v) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Loads that write LDS directly (global_load_lds_dword / _dwordx4): each active lane reads 4
+// bytes, or 16 from a 16-byte aligned address, at g, and lane i's bytes land at lds + 4 * i or
+// lds + 16 * i (lds wave-uniform).  No register holds the data, so inputs that are needed only
+// at the end of a kernel can be fetched at its start at no register cost.  The compiler counts
+// these loads like any other and waits for them before LDS reads of the same memory.
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void load_to_lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_void*)(const_cast<void*>(g)), (lds_void*)(lds), 4, 0, 0);
+}
+__device__ __forceinline__ void load_to_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_void*)(const_cast<void*>(g)), (lds_void*)(lds), 16, 0,
+                                   0);
+}
+
 // State rows are read exactly once per call: load them with the non-temporal hint
 // (global_load_dwordx4 ... nt) so the stream does not allocate in L2 / MALL.  On the
 // 16-block window gather this lifts the attainable read rate from about 6.2 to 7.0 TB/s.

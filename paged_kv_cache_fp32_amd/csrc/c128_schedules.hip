@@ -134,19 +134,42 @@ __device__ __forceinline__ void merge_row_groups(float4 (&lds_ml)[RG][2][64],
   }
 }
 
+// LDS copies of the epilogue's inputs besides the pooled state: the two column halves of rms_w,
+// the token's cos/sin row and, for each epilogue wave, the kv slot.
+struct EpilogueInputs {
+  float4 w[2][64];
+  float cs[kRope];
+  int32_t kv[2];
+};
+
+// Fetch them with loads that write LDS directly: every lane of both epilogue waves (column
+// half `half`).  A kernel issues this early, where the round trip overlaps other waiting, and
+// waits for the loads (vmcnt) before any of its waves can exit.  The compiler treats these
+// loads as writes to any memory, so the kernel issues them after its last block-id read.
+__device__ __forceinline__ void fetch_epilogue_inputs(const C128Params& p, int32_t t,
+                                                      int32_t rope_row, int half, int lane,
+                                                      EpilogueInputs& e) {
+  load_to_lds16(p.rms_w + half * 256 + lane * 4, &e.w[half][0]);
+  if (half == 1)
+    load_to_lds4(p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride + lane, e.cs);
+  if (lane == 0) load_to_lds4(p.kv_slot_mapping + t, &e.kv[half]);
+}
+
 // Fused epilogue of token t on 128 lanes (2 waves, one per column half; 4 columns per lane):
 // RMSNorm, bf16 round trip, per-64 absmax -> UE8M0 exponent -> E4M3FN codes, GPT-J RoPE ->
 // bf16, paged insert.  sumsq is the sum of squares of all 512 pooled values.  The 584-byte
 // record goes to the token's k_cache slot, or with kStage to `stage` (an LDS record: 576 data
 // bytes, then the 8 scale bytes) for a later insert.  Returns the kv slot, or -1 when the token
-// has none (nothing is written then).
+// has none (nothing is written then).  With `in`, rms_w, the kv slot and the cos/sin row come
+// from its LDS copies (fetch_epilogue_inputs) instead of global memory.
 template <bool kDebug, bool kStage = false>
 __device__ __forceinline__ int32_t epilogue(const C128Params& p, int32_t t, int32_t rope_row,
                                             const float (&c)[4], int half, int lane, int col,
-                                            float sumsq, uint8_t* stage = nullptr) {
+                                            float sumsq, uint8_t* stage = nullptr,
+                                            const EpilogueInputs* in = nullptr) {
   const float var = sumsq * (1.0f / kHead);
   const float rrms = 1.0f / __builtin_sqrtf(var + p.eps);
-  const float4 w = *reinterpret_cast<const float4*>(p.rms_w + col);
+  const float4 w = in ? in->w[half][lane] : *reinterpret_cast<const float4*>(p.rms_w + col);
   float n[4] = {c[0] * rrms * w.x, c[1] * rrms * w.y, c[2] * rrms * w.z, c[3] * rrms * w.w};
 
   if constexpr (kDebug)
@@ -161,7 +184,7 @@ __device__ __forceinline__ int32_t epilogue(const C128Params& p, int32_t t, int3
                                __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
   amax = group16_max(amax);
 
-  const int32_t kv_slot = p.kv_slot_mapping[t];
+  const int32_t kv_slot = in ? in->kv[half] : p.kv_slot_mapping[t];
   if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return -1;
   uint8_t* rec;
   uint8_t* scl;
@@ -194,7 +217,7 @@ __device__ __forceinline__ int32_t epilogue(const C128Params& p, int32_t t, int3
   } else {
     // GPT-J RoPE: this lane holds pairs m0 = 2j and m0 + 1 (dims 448 + 4j .. + 3)
     const int j = lane - 48;
-    const float* cs = p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
+    const float* cs = in ? in->cs : p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
     const float c0 = cs[2 * j], c1 = cs[2 * j + 1];
     const float s0r = cs[kRope / 2 + 2 * j], s1r = cs[kRope / 2 + 2 * j + 1];
     const float x0 = n[0] * c0 - n[1] * s0r;
@@ -216,7 +239,8 @@ template <bool kDebug, bool kStage = false>
 __device__ __forceinline__ int32_t finish_token(const C128Params& p, int32_t t, int32_t rope_row,
                                                 bool epilogue_wave, int half, int lane, int col,
                                                 const float (&l)[4], const float (&acc)[4],
-                                                float* lds_ss, uint8_t* stage = nullptr) {
+                                                float* lds_ss, uint8_t* stage = nullptr,
+                                                const EpilogueInputs* in = nullptr) {
   float c[4] = {0.f, 0.f, 0.f, 0.f};
   if (epilogue_wave) {
 #pragma unroll
@@ -228,7 +252,7 @@ __device__ __forceinline__ int32_t finish_token(const C128Params& p, int32_t t, 
   __syncthreads();
   if (!epilogue_wave) return -1;
   return epilogue<kDebug, kStage>(p, t, rope_row, c, half, lane, col, lds_ss[0] + lds_ss[1],
-                                  stage);
+                                  stage, in);
 }
 
 // 16 bytes as two 8-byte agent-scope atomic accesses (relaxed): coherent across the XCDs
@@ -284,6 +308,7 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_kernel(const C128Params 
   __shared__ float4 lds_acc[RG][2][64];
   __shared__ float lds_ss[2];
   __shared__ uint32_t lds_last;
+  __shared__ EpilogueInputs lds_in;
 
   const int32_t t = blockIdx.x;
   const int s = blockIdx.y;
@@ -303,8 +328,11 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_kernel(const C128Params 
                          ml, l, acc);
   merge_row_groups<RG>(lds_ml, lds_l, lds_acc, rg, half, lane, ml, l, acc);
 
+  // Any workgroup of the token may turn out to be the last, so each fetches the epilogue's
+  // inputs; their round trip overlaps the handoff's, and the wait below covers them.
   float* base = partials + static_cast<int64_t>(t) * S * (3 * kHead) + col;
   if (rg == 0) {
+    fetch_epilogue_inputs(p, t, win.rope_row, half, lane, lds_in);
     float* out = base + s * (3 * kHead);
     store_agent4(out, ml[0], ml[1], ml[2], ml[3]);
     store_agent4(out + kHead, l[0], l[1], l[2], l[3]);
@@ -338,7 +366,8 @@ __global__ void __launch_bounds__(128 * RG) c128_fanout_kernel(const C128Params 
       fold(ml, l, acc, load_agent4(in), load_agent4(in + kHead), load_agent4(in + 2 * kHead));
     }
   }
-  finish_token<kDebug>(p, t, win.rope_row, rg == 0, half, lane, col, l, acc, lds_ss);
+  finish_token<kDebug>(p, t, win.rope_row, rg == 0, half, lane, col, l, acc, lds_ss, nullptr,
+                       &lds_in);
 }
 
 // ---------------------------------------------------------------------------------------------
