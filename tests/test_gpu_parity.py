@@ -701,6 +701,37 @@ def test_padded_strides_other_schedules(mode):
         check_varlen(wl, label)
 
 
+@pytest.mark.parametrize("mode", ["single", "fanout2", "fanout8", "fanout16", "varlen", "staged"])
+def test_cos_sin_rows_67_floats_apart(mode):
+    """A cos/sin table whose rows are 67 floats apart (so most rows are only 4-byte aligned),
+    NaN in the 3 padding floats: every schedule reads its token's row at rope_row * stride and
+    only its first 64 columns (a stray read shows up as NaN codes).  The fan-out fetches the
+    row into LDS with one 4-byte load per lane."""
+    if mode == "staged":
+        wl = synth.shared_pool_batch("cos/sin stride 67 (staged)", 5700, 2048, 2048, 8, 64, 34,
+                                     1024)
+    else:
+        wl = small(T=12, seed=23)
+    announce(f"cos/sin row stride 67 ({mode})")
+    d = DeviceWorkload(wl)
+    rows = d.cos_sin.shape[0]
+    padded = torch.full((rows, 67), float("nan"), dtype=torch.float32, device=d.state.device)
+    padded[:, :64] = d.cos_sin
+    d.cos_sin = padded[:, :64]
+    assert d.cos_sin.stride() == (67, 1)
+    if mode.startswith("fanout"):
+        comp = d.run(debug=True, splits=int(mode[6:]))
+    else:
+        comp = d.run(debug=True, varlen=(mode == "varlen"))
+    body, guards_ok = d.k_cache_bytes()
+    assert guards_ok, "k_cache guard bands were written"
+    orc = oracle.run(wl, THREADS)
+    rep = compare(wl, body, orc, gpu_compressed=comp.cpu().numpy())
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == wl.num_tokens
+
+
 @pytest.mark.parametrize("mode", ["single", "fanout", "varlen"])
 def test_largest_position_is_skipped(mode):
     """A boundary token at position 2^31 - 1 needs block-table column 2^28 - 1: no table is that
