@@ -252,6 +252,19 @@ def test_c4_wide_workgroups_mixed_batch(T):
     assert rep["written"] == int((orc.status == 1).sum()) > T // 2
 
 
+@pytest.mark.parametrize("nreq,seed", [(160, 1210), (210, 1213)])
+def test_c4_prefill_beyond_one_wide_round(nreq, seed):
+    """Chunked prefills of 87,880 and 109,751 tokens (about a fifth of them writing): more than
+    one round of wide workgroups holds (49,152 tokens on 256 CUs), so they take the narrow
+    shape, about 11,000 and 13,700 waves of 8 tokens."""
+    announce(f"c4 prefill beyond one wide round: generating {nreq} requests")
+    wl = synth.c4_varlen_prefill(f"c4 varlen prefill {nreq} req", seed, nreq, 1024, 512,
+                                 kv_bs=64, cs_rows=2048)
+    assert wl.num_tokens > 49152
+    rep, *_ = check(wl, f"c4 prefill beyond one wide round T={wl.num_tokens}")
+    assert rep["written"] == int(wl.written_mask().sum()) > 15000
+
+
 @pytest.mark.parametrize("nreq,seed", [(32, 1203), (64, 1202)])
 def test_c4_wide_workgroups_sparse_prefill(nreq, seed):
     """Chunked prefills of about 14k and 32k tokens (one wide round, one or two batches a wave;
