@@ -70,7 +70,12 @@ c128_compress_store_kernel(const C128Params p) {
   const int32_t pos = p.positions[t];
   const int32_t slot = p.slot_mapping[t];
   const int32_t req = p.token_to_req[t];
-  if ((slot < 0) | (pos < 0) | ((pos & (kRatio - 1)) != kRatio - 1) | (req < 0)) return;
+  // Without the pooled-vector output a token with no kv slot writes nothing, so its kv slot is
+  // loaded here too and joins the gate: no work for such a token, and no round trip for the
+  // slot (and the kernel-argument line that holds its pointer) before the insert.
+  const int32_t kv_slot = kDebug ? 0 : p.kv_slot_mapping[t];
+  if ((slot < 0) | (pos < 0) | ((pos & (kRatio - 1)) != kRatio - 1) | (req < 0) | (kv_slot < 0))
+    return;
   const int32_t win = pos >> 7;  // window rows 128*win .. 128*win + 127
   if (req < 0 || req >= p.bt_rows ||
       static_cast<int64_t>(win + 1) * kWindowBlocks > p.bt_cols)
@@ -156,6 +161,15 @@ c128_compress_store_kernel(const C128Params p) {
   const float var = (lds_ss[0] + lds_ss[1]) * (1.0f / kHead);
   const float rrms = 1.0f / __builtin_sqrtf(var + p.eps);
   const float4 w = *reinterpret_cast<const float4*>(p.rms_w + col);
+  // The RoPE lanes' cos/sin pairs go out with rms_w (one round trip for both); every lane loads
+  // a valid pair (lane & 15) and only lanes 48..63 of the second wave use it.  The empty asm
+  // consumes them here: the compiler would otherwise sink the loads into the RoPE branch, which
+  // runs after the quantised stores, into a round trip of their own.
+  const int j = lane & 15;
+  const float* cs = p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
+  const float c0 = cs[2 * j], c1 = cs[2 * j + 1];
+  const float s0r = cs[kRope / 2 + 2 * j], s1r = cs[kRope / 2 + 2 * j + 1];
+  asm volatile("" ::"v"(c0), "v"(c1), "v"(s0r), "v"(s1r));
   float n[4] = {c[0] * rrms * w.x, c[1] * rrms * w.y, c[2] * rrms * w.z, c[3] * rrms * w.w};
 
   if constexpr (kDebug)
@@ -170,10 +184,10 @@ c128_compress_store_kernel(const C128Params p) {
                                __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
   amax = group16_max(amax);
 
-  const int32_t kv_slot = p.kv_slot_mapping[t];
-  if (kv_slot < 0 || kv_slot >= p.n_kv_slots) return;
-  const int32_t kb = kv_slot / p.kv_bs;
-  const int32_t ko = kv_slot - kb * p.kv_bs;
+  const int32_t kv = kDebug ? p.kv_slot_mapping[t] : kv_slot;
+  if (kv < 0 || kv >= p.n_kv_slots) return;
+  const int32_t kb = kv / p.kv_bs;
+  const int32_t ko = kv - kb * p.kv_bs;
   uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
   uint8_t* rec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
   uint8_t* scl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
@@ -194,11 +208,7 @@ c128_compress_store_kernel(const C128Params p) {
       scl[col >> 6] = static_cast<uint8_t>(byte < 0 ? 0 : (byte > 255 ? 255 : byte));
     }
   } else {
-    // GPT-J RoPE: this lane holds pairs m0 = 2j and m0 + 1 (dims 448 + 4j .. + 3)
-    const int j = lane - 48;
-    const float* cs = p.cos_sin + static_cast<int64_t>(rope_row) * p.cs_stride;
-    const float c0 = cs[2 * j], c1 = cs[2 * j + 1];
-    const float s0r = cs[kRope / 2 + 2 * j], s1r = cs[kRope / 2 + 2 * j + 1];
+    // GPT-J RoPE: this lane (j = lane - 48) holds pairs m0 = 2j and m0 + 1 (dims 448 + 4j .. + 3)
     const float x0 = n[0] * c0 - n[1] * s0r;
     const float y0 = n[1] * c0 + n[0] * s0r;
     const float x1 = n[2] * c1 - n[3] * s1r;

@@ -168,6 +168,28 @@ def test_non_boundary_and_negative_slots():
     assert np.isfinite(comp[5]).all() and np.isnan(comp[4]).all() and np.isnan(comp[0]).all()
 
 
+@pytest.mark.parametrize("mode", ["single", "fanout", "varlen"])
+def test_kv_slot_edges_without_pooled_output(mode):
+    """Without the pooled-vector output the single pass drops a token with a negative kv slot
+    at its gate: kv slots -1, -7 and one past the last slot (each on a boundary token) write
+    nothing and every other boundary token is inserted, on the plain entry point, the fan-out
+    and the compacted schedule alike."""
+    wl = small(T=10, seed=29)
+    n_slots = wl.k_cache.shape[0] * wl.k_cache.shape[1]
+    wl.kv_slot_mapping[[1, 4, 8]] = np.array([-1, -7, n_slots], np.int32)
+    announce(f"kv slot edges, no pooled output ({mode})")
+    kw = {"splits": 4} if mode == "fanout" else ({"varlen": True} if mode == "varlen" else {})
+    body, _, guards_ok = run_gpu(wl, debug=False, **kw)
+    assert guards_ok
+    orc = oracle.run(wl, 2)
+    assert list(orc.status) == [1, 2, 1, 1, 2, 1, 1, 1, -1, 1]
+    wl.kv_slot_mapping[8] = -1
+    rep = compare(wl, body, orc)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep["written"] == 7
+
+
 def test_all_zero_window():
     wl = small(T=2, seed=9)
     wl.state[:, :, :512] = 0.0
