@@ -144,6 +144,11 @@ __global__ void __launch_bounds__(64 * NW)
   __shared__ __align__(16) uint8_t stage_all[NW][kMaxTok * kSlotBytes];
   __shared__ int32_t slot_all[NW][kMaxTok];
 
+  // The token count per wave and the kv-slot pointer sit in another 64-byte line of the kernel
+  // arguments than the other pointers; the empty asm makes all of them arrive in one round trip
+  // (the compiler otherwise requests that line only after its first wait).
+  asm volatile("" ::"s"(tokens_per_wave), "s"(p.kv_slot_mapping), "s"(p.positions),
+               "s"(p.rms_w));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* stage = stage_all[wave];
