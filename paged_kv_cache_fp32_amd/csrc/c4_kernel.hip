@@ -48,7 +48,8 @@ constexpr int kC4WideMinTokens = 8192;
 constexpr int kC4MaxTokensPerWave = 8;      // 8 tokens x 8 window rows = the 64 lanes
 constexpr int kC4TargetWaves = 2048;        // 2 waves per SIMD on 256 CUs
 constexpr int kC4WideTargetWaves = 3072;    // 3 per SIMD: one 12-wave workgroup per CU
-constexpr int kC4WideMaxTokensPerWave = 16;  // wide waves: two batches of 8
+constexpr int kC4WideMaxGatedPerWave = 64;   // wide waves gate up to 64 tokens (a lane each of the
+                                             // workgroup's threads) and stage 16 records a round
 constexpr int kC4WavesPerSimd = 3;          // room for all 32 window loads in flight
 
 // Per-column softmax-weighted sum over NR rows held in registers (scores scaled to log2).
@@ -136,8 +137,8 @@ __global__ void __launch_bounds__(64 * NW)
     __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     c4_compress_store_kernel(const C128Params p, int32_t state_bs, int32_t state_bs_log2,
                              int32_t tokens_per_wave) {
-  // A wave takes up to 8 * NB tokens, resolved in NB batches of 8 (its 64 metadata lanes: 8
-  // tokens x 8 window rows); NB = 2 only for wide workgroups.
+  // A wave takes up to 8 * NB tokens a round, resolved in NB batches of 8 (its 64 metadata lanes:
+  // 8 tokens x 8 window rows); NB = 2 only for wide workgroups.
   constexpr bool kDeal = NW > kC4NarrowWaves;
   static_assert(NB == 1 || (NB == 2 && kDeal), "two batches only in wide workgroups");
   constexpr int kMaxTok = kC4MaxTokensPerWave * NB;
@@ -156,18 +157,20 @@ __global__ void __launch_bounds__(64 * NW)
   const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * NW + wave) * tokens_per_wave;
   if (lane < kMaxTok) slot_of[lane] = -1;
 
-  // ---- wide workgroups deal their tokens out: one lane per token of the workgroup's range
-  // loads its gate, request id and kv slot; the tokens that pass are listed in LDS and wave w
-  // takes list entries w, w + NW, w + 2 NW, ..., so that every wave reads about as many
-  // windows before the workgroup's barrier.  Narrow workgroups keep each wave's consecutive
-  // tokens.
-  constexpr int kDealMax = kDeal ? NW * kMaxTok : 1;
+  // ---- wide workgroups deal their tokens out: one lane per token of the workgroup's range (up
+  // to 64 tokens a wave) loads its gate, request id and kv slot; the tokens that pass are listed
+  // in LDS and wave w takes list entries w, w + NW, w + 2 NW, ..., so that every wave reads about
+  // as many windows before the workgroup's barrier.  A wave's stage holds kMaxTok records, so a
+  // wave dealt more tokens than that takes them in rounds, each ending in the workgroup's
+  // insert.  Narrow workgroups keep each wave's consecutive tokens, one round.
+  constexpr int kDealMax = kDeal ? 64 * NW : 1;
   static_assert(!kDeal || kDealMax <= 64 * NW, "one lane per dealt token");
   __shared__ int32_t deal_tok[kDealMax];
   __shared__ int32_t deal_meta[kDealMax][3];  // position, request, kv slot
   __shared__ int32_t deal_count[NW];
   const int64_t gbase = static_cast<int64_t>(blockIdx.x) * NW * tokens_per_wave;
   int32_t my_tokens = tokens_per_wave;
+  int rounds = 1;  // workgroup-uniform
   if constexpr (kDeal) {
     const int tid = static_cast<int>(threadIdx.x);
     bool pass = false;
@@ -199,13 +202,16 @@ __global__ void __launch_bounds__(64 * NW)
     }
     __syncthreads();
     my_tokens = n > wave ? (n - wave + NW - 1) / NW : 0;
+    // a single-batch wide kernel is launched with at most 8 tokens a wave: one round
+    if constexpr (NB > 1) rounds = ((n + NW - 1) / NW + kMaxTok - 1) / kMaxTok;
   }
 
-  // One batch of up to 8 tokens, the wave's stage slots b0 .. b0 + nb - 1.  With two batches
+  // One batch of up to 8 tokens of round `base` (the wave's dealt tokens base + b0 ..), into the
+  // wave's stage slots b0 .. b0 + nb - 1.  With two batches
   // the lane index is counted afresh in each, and the state block size is made opaque, so that
   // the loop keeps neither the work-item id, per-lane addresses nor division constants live (and
   // spilled) from one batch to the next.
-  const auto batch = [&](const int b0, const int nb) {
+  const auto batch = [&](const int base, const int b0, const int nb) {
     int ln = lane, sbs = state_bs;
     if constexpr (NB > 1) {
       ln = lane_index();
@@ -229,7 +235,7 @@ __global__ void __launch_bounds__(64 * NW)
     int32_t req = -1, kvs = -1;
     if constexpr (kDeal) {
       if (mk < nb) {
-        const int e = wave + NW * (b0 + mk);
+        const int e = wave + NW * (base + b0 + mk);
         mpos = deal_meta[e][0];
         req = deal_meta[e][1];
         kvs = deal_meta[e][2];
@@ -299,7 +305,7 @@ __global__ void __launch_bounds__(64 * NW)
                           c[3] * rrms * w0.w, c[4] * rrms * w1.x, c[5] * rrms * w1.y,
                           c[6] * rrms * w1.z, c[7] * rrms * w1.w};
       if constexpr (kDebug) {
-        const int64_t t = kDeal ? gbase + deal_tok[wave + NW * slot_k] : tbase + k;
+        const int64_t t = kDeal ? gbase + deal_tok[wave + NW * (base + slot_k)] : tbase + k;
         float* out = p.compressed_out + t * kHead;
         *reinterpret_cast<float4*>(out + col) = make_float4(c[0], c[1], c[2], c[3]);
         *reinterpret_cast<float4*>(out + 256 + col) = make_float4(c[4], c[5], c[6], c[7]);
@@ -343,49 +349,53 @@ __global__ void __launch_bounds__(64 * NW)
       if (ln == 0) slot_of[slot_k] = kv_slot;
     }
   };
-  if constexpr (NB > 1) {
-    for (int b0 = 0; b0 < my_tokens; b0 += 8) batch(b0, my_tokens - b0 < 8 ? my_tokens - b0 : 8);
-  } else {
-    batch(0, my_tokens);
-  }
+  for (int r = 0; r < (NB > 1 ? rounds : 1); ++r) {
+    const int base = r * kMaxTok;
+    const int left = my_tokens - base;
+    const int mine = left < 0 ? 0 : (left < kMaxTok ? left : kMaxTok);
+    if constexpr (NB > 1) {
+      for (int b0 = 0; b0 < mine; b0 += 8) batch(base, b0, mine - b0 < 8 ? mine - b0 : 8);
+    } else {
+      batch(base, 0, mine);
+    }
 
-  // ---- paged insert of every staged record, after the last state read of every wave of the
-  // workgroup: the k_cache writes reach HBM in bursts instead of interleaved with the read
-  // stream (8-byte stores; records and scale groups are 8-byte aligned)
-  __syncthreads();
-  const int fl = NB > 1 ? lane_index() : lane;
-  for (int k = 0; k < tokens_per_wave; ++k) {
-    const int32_t kv_slot = slot_of[k];
-    if (kv_slot < 0) continue;
-    const int32_t kb = kv_slot / p.kv_bs;
-    const int32_t ko = kv_slot - kb * p.kv_bs;
-    uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
-    uint8_t* grec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
-    uint8_t* gscl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
-                    static_cast<int64_t>(ko) * kScaleBytes;
-    const uint8_t* rec = stage + k * kSlotBytes;
-    *reinterpret_cast<uint2*>(grec + 8 * fl) = *reinterpret_cast<const uint2*>(rec + 8 * fl);
-    if (fl < 8)
-      *reinterpret_cast<uint2*>(grec + 512 + 8 * fl) =
-          *reinterpret_cast<const uint2*>(rec + 512 + 8 * fl);
-    else if (fl == 8)
-      *reinterpret_cast<uint2*>(gscl) = *reinterpret_cast<const uint2*>(rec + kRecordBytes);
+    // ---- paged insert of every staged record, after the last state read of every wave of the
+    // workgroup: the k_cache writes reach HBM in bursts instead of interleaved with the read
+    // stream (8-byte stores; records and scale groups are 8-byte aligned).  A wave's stage and
+    // slot list are its own, so the next round may refill them without a further barrier.
+    __syncthreads();
+    const int fl = NB > 1 ? lane_index() : lane;
+    for (int k = 0; k < (kDeal ? kMaxTok : tokens_per_wave); ++k) {
+      const int32_t kv_slot = slot_of[k];
+      if (kv_slot < 0) continue;
+      const int32_t kb = kv_slot / p.kv_bs;
+      const int32_t ko = kv_slot - kb * p.kv_bs;
+      uint8_t* blockp = p.k_cache + static_cast<int64_t>(kb) * p.kc_stride0;
+      uint8_t* grec = blockp + static_cast<int64_t>(ko) * kRecordBytes;
+      uint8_t* gscl = blockp + static_cast<int64_t>(p.kv_bs) * kRecordBytes +
+                      static_cast<int64_t>(ko) * kScaleBytes;
+      const uint8_t* rec = stage + k * kSlotBytes;
+      *reinterpret_cast<uint2*>(grec + 8 * fl) = *reinterpret_cast<const uint2*>(rec + 8 * fl);
+      if (fl < 8)
+        *reinterpret_cast<uint2*>(grec + 512 + 8 * fl) =
+            *reinterpret_cast<const uint2*>(rec + 512 + 8 * fl);
+      else if (fl == 8)
+        *reinterpret_cast<uint2*>(gscl) = *reinterpret_cast<const uint2*>(rec + kRecordBytes);
+    }
+    if (r + 1 < rounds && fl < kMaxTok) slot_of[fl] = -1;
   }
 }
 
 // Tokens per wave: enough waves for the target (2 per SIMD for the narrow shape, 3 for the wide
-// one) before a wave takes more than one token; at most max_tokens (the wave's LDS stage: 8
-// narrow, 16 wide).
+// one) before a wave takes more than one token; at most max_tokens (8 for a narrow wave, the
+// 64 lanes of its metadata; 64 for a wide wave, which gates one token a thread).
 int c4_tokens_per_wave(int64_t num_tokens, int64_t target_waves, int64_t max_tokens) {
   const int64_t k = (num_tokens + target_waves - 1) / target_waves;
   return static_cast<int>(k < 1 ? 1 : (k > max_tokens ? max_tokens : k));
 }
 
 template <int NW, int NB>
-hipError_t launch_c4_as(const C128Params& p, int32_t state_bs, int64_t target_waves,
-                        hipStream_t stream) {
-  const int32_t kpw =
-      c4_tokens_per_wave(p.num_tokens, target_waves, int64_t{kC4MaxTokensPerWave} * NB);
+hipError_t launch_c4_as(const C128Params& p, int32_t state_bs, int32_t kpw, hipStream_t stream) {
   const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
   const dim3 grid(static_cast<unsigned>((waves + NW - 1) / NW));
   const dim3 block(64 * NW);
@@ -402,23 +412,28 @@ hipError_t launch_c4_as(const C128Params& p, int32_t state_bs, int64_t target_wa
 // Small batches take 4-wave workgroups, spread over as many CUs as possible.  From
 // kC4WideMinTokens on, while one round of them covers the batch, a workgroup is 12 waves (one
 // per CU), so that the records of a whole CU wait in LDS until all of its waves have read their
-// windows: the record writes then meet far less of the read stream.  Beyond one round the
-// narrow shape stays, as a second round of wide workgroups would run as a tail.
+// windows: the record writes then meet far less of the read stream.  A wide wave gates up to 64
+// tokens (cu_count * 768 tokens in one round of workgroups) and stages 16 records at a time: a
+// chunked prefill, where about one token in four writes, stays at one insert per workgroup up to
+// about 200k tokens, and a denser batch beyond 49,152 tokens inserts after every 16 records a
+// wave.  Beyond one round the narrow shape stays, as a second round of wide workgroups would run
+// as a tail.
 hipError_t launch_c4_compress_store(const C128Params& p, int32_t state_bs, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
   if (p.num_tokens >= kC4WideMinTokens) {
-    const int64_t kpw =
-        c4_tokens_per_wave(p.num_tokens, kC4WideTargetWaves, kC4WideMaxTokensPerWave);
+    const int32_t kpw =
+        c4_tokens_per_wave(p.num_tokens, kC4WideTargetWaves, kC4WideMaxGatedPerWave);
     const int64_t waves = (static_cast<int64_t>(p.num_tokens) + kpw - 1) / kpw;
     if ((waves + kC4WideWaves - 1) / kC4WideWaves <= device_cu_count()) {
       // one batch of metadata per wave while 8 tokens a wave suffice: the single-batch kernel
       // keeps half the LDS stage and fewer registers
       if (kpw <= kC4MaxTokensPerWave)
-        return launch_c4_as<kC4WideWaves, 1>(p, state_bs, kC4WideTargetWaves, stream);
-      return launch_c4_as<kC4WideWaves, 2>(p, state_bs, kC4WideTargetWaves, stream);
+        return launch_c4_as<kC4WideWaves, 1>(p, state_bs, kpw, stream);
+      return launch_c4_as<kC4WideWaves, 2>(p, state_bs, kpw, stream);
     }
   }
-  return launch_c4_as<kC4NarrowWaves, 1>(p, state_bs, kC4TargetWaves, stream);
+  return launch_c4_as<kC4NarrowWaves, 1>(
+      p, state_bs, c4_tokens_per_wave(p.num_tokens, kC4TargetWaves, kC4MaxTokensPerWave), stream);
 }
 
 }  // namespace dsv4

@@ -252,11 +252,29 @@ def test_c4_wide_workgroups_mixed_batch(T):
     assert rep["written"] == int((orc.status == 1).sum()) > T // 2
 
 
+def test_c4_wide_rounds_on_dense_workgroups():
+    """A 60,000-token batch: 20,000 decode tokens that all write, then 40,000 that do not close a
+    window.  One round of wide workgroups holds it at 20 tokens a wave, so every workgroup over
+    the dense part deals 20 writing tokens to each wave, more than its 16-record stage: it
+    inserts twice (16 records a wave, then 4); the workgroups over the rest insert nothing."""
+    wl = c4_batch(20000, 1530, k_max=40)
+    extra = 40000
+    rng = np.random.default_rng(1531)
+    wl.positions = np.concatenate(
+        [wl.positions, (4 * rng.integers(1, 40, extra) + 1).astype(np.int32)])
+    wl.slot_mapping = np.concatenate([wl.slot_mapping, np.zeros(extra, np.int32)])
+    wl.token_to_req = np.concatenate([wl.token_to_req, np.zeros(extra, np.int32)])
+    wl.kv_slot_mapping = np.concatenate([wl.kv_slot_mapping, np.full(extra, -1, np.int32)])
+    assert wl.num_tokens == 60000
+    rep, *_ = check(wl, "c4 dense workgroups in two rounds, T=60000")
+    assert rep["written"] == 20000
+
+
 @pytest.mark.parametrize("nreq,seed", [(160, 1210), (210, 1213)])
 def test_c4_prefill_beyond_one_wide_round(nreq, seed):
-    """Chunked prefills of 87,880 and 109,751 tokens (about a fifth of them writing): more than
-    one round of wide workgroups holds (49,152 tokens on 256 CUs), so they take the narrow
-    shape, about 11,000 and 13,700 waves of 8 tokens."""
+    """Chunked prefills of 87,880 and 109,751 tokens (about a fifth of them writing), beyond the
+    49,152 tokens that 16 tokens a wave cover: wide waves gate 29 and 36 tokens each and deal the
+    writing ones, about 7 and 8 a wave, into their stages."""
     announce(f"c4 prefill beyond one wide round: generating {nreq} requests")
     wl = synth.c4_varlen_prefill(f"c4 varlen prefill {nreq} req", seed, nreq, 1024, 512,
                                  kv_bs=64, cs_rows=2048)
