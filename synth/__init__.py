@@ -527,6 +527,42 @@ def indexer_decode_batch(name: str, seed: int, num_tokens: int, n_blocks: int, k
     return wl
 
 
+def indexer_varlen_prefill(name: str, seed: int, num_reqs: int, max_chunk: int,
+                           max_start: int, kv_bs: int, cs_rows: int, state_bs: int = 8,
+                           drop_frac: float = 0.1, score_std: float = math.sqrt(2.0),
+                           threads: int | None = None, fp4: bool = False) -> Workload:
+    """The indexer's compressor on a chunked prefill, laid out as ``c4_varlen_prefill`` (request
+    r holds positions start_r .. start_r + L_r - 1, L ~ U{1..max_chunk}, start ~ U{0..max_start};
+    every fourth position closes a window; a seeded ``drop_frac`` of slot_mapping is -1; every
+    token gets a distinct kv slot), with head-128 state rows and the indexer cache (``fp4``: the
+    MXFP4 one)."""
+    L = randint(num_reqs, 1, max_chunk, seed, 70)
+    start = randint(num_reqs, 0, max_start, seed, 71)
+    cols = int(-(-(max_start + max_chunk) // state_bs))
+    n_blocks = num_reqs * cols
+    bt = permutation(n_blocks, seed, 72).reshape(num_reqs, cols).astype(np.int32)
+    token_to_req = np.concatenate([np.full(int(L[r]), r, np.int32) for r in range(num_reqs)])
+    positions = np.concatenate(
+        [np.arange(int(start[r]), int(start[r] + L[r]), dtype=np.int64) for r in range(num_reqs)])
+    T = positions.shape[0]
+    blk = bt[token_to_req, positions // state_bs].astype(np.int64)
+    slot_mapping = blk * state_bs + positions % state_bs
+    slot_mapping[uniform(T, seed, 73) < drop_frac] = -1
+    kv_blocks = int(-(-T // kv_bs))
+    kv_slots = permutation(kv_blocks * kv_bs, seed, 74)[:T].astype(np.int32)
+    state_base, state = alloc_state(n_blocks, row_width=INDEXER_ROW, rows_per_block=state_bs)
+    fill_state(state, seed, 1.0, score_std, threads=threads, width=2 * INDEXER_HEAD)
+    kc_base, kc = alloc_indexer_cache(kv_blocks, kv_bs, fp4=fp4)
+    w = (1.0 + 0.1 * normal(INDEXER_HEAD, seed, 3).astype(np.float64)).astype(np.float32)
+    wl = Workload(name, state, bt, token_to_req, positions.astype(np.int32),
+                  slot_mapping.astype(np.int32), w, 1e-6, rope_table(cs_rows), kc, kv_slots,
+                  seed, state_base, kc_base, compress_ratio=C4_RATIO, overlap=1, indexer=True,
+                  indexer_fp4=fp4)
+    wl.info = {"kind": "indexer varlen", "tokens": T, "requests": num_reqs,
+               "pool_blocks": n_blocks, "state_bs": state_bs}
+    return wl
+
+
 def config0() -> Workload:
     """Single request, one boundary token at position 127; 16-block pool; KV block size 2,
     kv slot 3; kv ~ N(0,1), score ~ N(0,2); 4096 RoPE rows."""

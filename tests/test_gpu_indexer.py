@@ -203,3 +203,13 @@ def test_indexer_pipelined_mixed_batch(T):
     print(rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
     assert rep["written"] == int((orc.status == 1).sum()) > T // 2
+
+
+@pytest.mark.parametrize("nreq,seed,max_start", [(64, 1402, 4096), (210, 1413, 512)])
+def test_indexer_chunked_prefill(nreq, seed, max_start):
+    """Chunked prefills of 33,908 and 107,030 tokens: contiguous positions per request, about one
+    token in four closing a window, 10% of the state slots dropped, a distinct kv slot each."""
+    wl = synth.indexer_varlen_prefill(f"indexer prefill {nreq} req", seed, nreq, 1024,
+                                      max_start, kv_bs=64, cs_rows=8192, fp4=False)
+    rep, *_ = check(wl, f"indexer prefill T={wl.num_tokens}")
+    assert rep["written"] == int(wl.written_mask().sum()) > 7000
