@@ -920,7 +920,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the C128 compress-store path shards by request "
-              "with no exchange between GPUs, and this build runs on a single MI355X. "
+              "with no exchange between GPUs, so one GPU's throughput is the figure. "
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
