@@ -28,7 +28,8 @@ counter-calibration kernel for rocprofv3); ``--mode read`` times streaming and
 window-gather reads, with plain and non-temporal loads (the attainable-bandwidth
 reference lines); ``--mode read-small``, ``--mode read-idx`` and ``--mode read-c4`` time pure
 reads of the small decode batches' windows and of the indexer's and the C4 compressor's access
-patterns beside the kernels.
+patterns beside the kernels; ``--mode read-gather`` times the large batch's window gather over
+id orders and launch shapes.
 """
 
 from __future__ import annotations
@@ -706,6 +707,71 @@ def read_line(args):
     print(json.dumps(rec), flush=True)
 
 
+def read_gather_line(args):
+    """The large batch's window gather without arithmetic (the 16384-token workload's 8.59 GB
+    pool, non-temporal loads; bench_support probes): the probe with the compress kernel's launch
+    shape on the windows' own random block ids, on consecutive ids in pool order and on windows
+    of 16 consecutive blocks in random window order; then a persistent grid over 12 launch
+    shapes (workgroups x waves x loads in flight per lane) on the windows' own ids.  One JSON
+    line per probe: where the gather's ceiling lies, and whether it depends on the ids or on
+    the launch shape."""
+    import numpy as np
+    import torch
+
+    import bench_support
+    import synth
+    from synth.device import DeviceWorkload
+
+    L = bench_support.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+    wl = synth.config4()
+    d = DeviceWorkload(wl, device=dev)
+    T = wl.num_tokens
+    nb = d.state.shape[0]
+    s0 = d.state.stride(0)
+    pos = wl.positions.astype(np.int64)
+    cols = (pos // 128)[:, None] * 16 + np.arange(16)[None, :]
+    own = np.ascontiguousarray(wl.block_table[np.arange(T)[:, None], cols]).astype(np.int32)
+    order = np.random.default_rng(wl.seed).permutation(T).astype(np.int32)
+    orders = (("windows' own ids (random)", own),
+              ("consecutive ids in pool order", np.arange(T * 16, dtype=np.int32).reshape(T, 16)),
+              ("16 consecutive blocks a window, random window order",
+               (order[:, None] * 16 + np.arange(16, dtype=np.int32)[None, :]).astype(np.int32)))
+    out = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+    nbytes = T * 128 * 4096
+
+    def timed(fn):
+        _, per = time_calls(torch, stream, [fn], args.steps, args.warmup)
+        ms = float(np.median(per))
+        return round(ms * 1e3, 1), round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    ids_dev = {}
+    for name, ids in orders:
+        assert ids.min() >= 0 and ids.max() < nb
+        ids_dev[name] = torch.from_numpy(np.ascontiguousarray(ids)).to(dev)
+
+        def kernel_shape(i=ids_dev[name]):
+            assert L.probe_block_gather_read(d.state.data_ptr(), s0, i.data_ptr(), T,
+                                             out.data_ptr(), 1, sid) == 0
+        us, gbs = timed(kernel_shape)
+        print(json.dumps({"mode": "read-gather", "probe": "kernel shape", "ids": name,
+                          "us": us, "GBps": gbs}), flush=True)
+    i = ids_dev[orders[0][0]]
+    for G, W, Ld in ((256, 16, 16), (256, 16, 8), (256, 8, 16), (256, 8, 8), (256, 4, 16),
+                     (256, 4, 8), (256, 4, 4), (512, 4, 8), (512, 8, 8), (256, 2, 16),
+                     (512, 2, 16), (1024, 4, 8)):
+        def persistent(G=G, W=W, Ld=Ld):
+            assert L.probe_window_read_persistent(d.state.data_ptr(), s0, i.data_ptr(), T, G, W,
+                                                  Ld, out.data_ptr(), sid) == 0
+        us, gbs = timed(persistent)
+        print(json.dumps({"mode": "read-gather", "probe": "persistent", "ids": orders[0][0],
+                          "workgroups": G, "waves": W, "loads_in_flight": Ld,
+                          "kib_in_flight_per_workgroup": W * Ld, "us": us, "GBps": gbs}),
+              flush=True)
+
+
 def read_small_line(args):
     """Small decode batches (1, 32, 128 and 256 tokens on the decode sweep's pool): the time of a
     pure read of exactly their windows over every launch shape of the split window-gather probe
@@ -911,12 +977,13 @@ def main():
     ap.add_argument("--sweep-splits", action="store_true",
                     help="with --sweep: time every fan-out split count, not only the automatic one")
     ap.add_argument("--mode", choices=["main", "copy", "read", "read-small", "read-idx", "read-c4",
-                                          "sweep"],
+                                          "read-gather", "sweep"],
                     default="main",
                     help="main: the large-batch line (plus --sweep if given); sweep: only the "
                          "--sweep workloads; read / copy: bandwidth references and counter "
                          "calibration; read-small: pure reads of small batches' windows over "
-                         "launch shapes, beside the entry points")
+                         "launch shapes, beside the entry points; read-gather: the large "
+                         "batch's window gather over id orders and launch shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the C128 compress-store path shards by request "
@@ -933,6 +1000,8 @@ def main():
         read_small_line(args)
     elif args.mode in ("read-idx", "read-c4"):
         read_pattern_line(args, args.mode == "read-c4")
+    elif args.mode == "read-gather":
+        read_gather_line(args)
     elif args.mode == "sweep":
         if not args.sweep:
             sys.exit("--mode sweep needs --sweep PATH")

@@ -46,6 +46,8 @@ def lib():
         L.probe_stream_chunks.restype = ci
         L.probe_window_read_split.argtypes = [vp, i64, vp, ci, ci, ci, ci, vp, vp]
         L.probe_window_read_split.restype = ci
+        L.probe_window_read_persistent.argtypes = [vp, i64, vp, ci, ci, ci, ci, vp, vp]
+        L.probe_window_read_persistent.restype = ci
         L.probe_block_gather_read.argtypes = [vp, i64, vp, ci, vp, ci, vp]
         L.probe_block_gather_read.restype = ci
         L.probe_indexer_window_read.argtypes = [ctypes.POINTER(IdxProbe), ci, vp, vp]

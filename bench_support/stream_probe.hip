@@ -9,6 +9,7 @@
 //  * stream_chunks: a sequential read in contiguous chunks per workgroup.
 //  * window_read_split: small batches' windows read with S workgroups per window.
 //  * idx_window_read: the indexer and C4 compressors' reads (metadata, 8 half-rows, RoPE row).
+//  * window_read_persistent: large batches' windows read by a persistent grid of any shape.
 // The first three come with plain loads and with the non-temporal hint the compress kernels
 // use. Each writes one float per workgroup or wave so the loads cannot be removed.
 
@@ -148,6 +149,41 @@ __global__ void __launch_bounds__(1024) window_read_split(const float* __restric
 }
 
 
+// The window gather of large batches by a persistent grid: workgroup g reads windows g, g + G,
+// ...; a window is 16 blocks x 8 rows x 4 quarter-rows of 1 KiB = 512 pieces, split evenly over
+// the workgroup's W waves, each keeping L one-KiB wave loads in flight (non-temporal, as the
+// compress kernels load).  Its launch shape is free, unlike the compress kernels'.
+template <int L>
+__global__ void __launch_bounds__(1024) window_read_persistent(const float* __restrict__ pool,
+                                                               int64_t stride0,
+                                                               const int32_t* __restrict__ ids,
+                                                               int n_windows, int W,
+                                                               float* __restrict__ out) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = 512 / W;
+  float acc = 0.0f;
+  for (int w = blockIdx.x; w < n_windows; w += gridDim.x) {
+    const int32_t* my = ids + static_cast<int64_t>(w) * 16;
+    for (int k = 0; k < n; k += L) {
+      float4 v[L];
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const int p = wave * n + k + j;
+        const int b = p >> 5, q = p & 31;  // block; row q >> 2, quarter q & 3
+        const float* a = pool +
+                         static_cast<int64_t>(__builtin_amdgcn_readfirstlane(my[b])) * stride0 +
+                         q * 256 + lane * 4;
+        v[j] = ld<true>(reinterpret_cast<const float4*>(a));
+      }
+#pragma unroll
+      for (int j = 0; j < L; ++j) acc += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    }
+  }
+  if (threadIdx.x == 0 || acc == 1234.5f) out[blockIdx.x] = acc;
+}
+
+
 // The indexer or C4 compressor's reads without its arithmetic or its record stores.  A wave
 // takes kpw consecutive tokens; lane (k, i) = (lane / 8, lane % 8) resolves window row i of
 // token k; per token the wave loads the 8 half-rows (indexer: 512 B of kv and 512 B of score
@@ -277,6 +313,30 @@ extern "C" int probe_window_read_split(const float* pool, int64_t stride0, const
     case 16: window_read_split<16><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
     case 32: window_read_split<32><<<grid, block, 0, st>>>(pool, stride0, ids, S, W, out); break;
     default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// Persistent window gather of `n_windows` windows (ids: 16 block ids each; pool blocks of 8 rows of
+// 1024 floats at stride0 >= 8192 floats) by G workgroups of W in {2, 4, 8, 16} waves, L in
+// {4, 8, 16} loads in flight per lane with L dividing 512 / W; out holds G floats.
+extern "C" int probe_window_read_persistent(const float* pool, int64_t stride0,
+                                            const int32_t* ids, int n_windows, int G, int W,
+                                            int L, float* out, void* stream) {
+  if (!pool || !ids || !out || n_windows < 1 || G < 1 || stride0 < 8192) return -1;
+  if (W != 2 && W != 4 && W != 8 && W != 16) return -1;
+  if ((L != 4 && L != 8 && L != 16) || (512 / W) % L) return -1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(G), block(64 * W);
+  switch (L) {
+    case 4:
+      window_read_persistent<4><<<grid, block, 0, st>>>(pool, stride0, ids, n_windows, W, out);
+      break;
+    case 8:
+      window_read_persistent<8><<<grid, block, 0, st>>>(pool, stride0, ids, n_windows, W, out);
+      break;
+    default:
+      window_read_persistent<16><<<grid, block, 0, st>>>(pool, stride0, ids, n_windows, W, out);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
