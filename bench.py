@@ -532,6 +532,11 @@ def sweep(args, path):
         measure("scattered positions T=262400", [d5], 200)
         measure("scattered positions T=262400", [d5], 200, varlen=True)
         del d5
+    if want("large chunked prefill T=246933"):
+        d6 = DeviceWorkload(synth.large_prefill(), device=dev)
+        measure("large chunked prefill T=246933", [d6], 200)
+        measure("large chunked prefill T=246933", [d6], 200, varlen=True)
+        del d6
     pool = pool_dev = None
     for T in [1 << i for i in range(13)]:
         if not want(f"cfg3 decode sweep T={T}"):

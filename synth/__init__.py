@@ -592,6 +592,14 @@ def config2() -> Workload:
                           kv_bs=64, cs_rows=8192)
 
 
+def large_prefill(threads: int | None = None) -> Workload:
+    """A large chunked prefill: 32 requests, chunks of up to 16384 tokens starting at positions
+    up to 16384 (246,933 tokens, 1,730 of them close a window with a state slot), distinct
+    windows in a 131072-block (4.3 GB) pool."""
+    return varlen_prefill("large chunked prefill", SEED_BASE + 6, 32, 16384, 16384, 131072,
+                          kv_bs=64, cs_rows=32768, threads=threads)
+
+
 def config3_pool(threads: int | None = None):
     """The shared 65536-block pool of the decode sweep (scores ~ N(0,4))."""
     base, state = alloc_state(65536)

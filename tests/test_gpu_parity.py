@@ -528,6 +528,26 @@ def test_staged_gates_and_bad_indices():
     assert np.isnan(comp[bad[:10]]).all() and np.isnan(comp[bad[20:30]]).all()
 
 
+def test_staged_gate_density_regions():
+    """160,000 tokens in four regions of gate density, with a fifth of the state slots negative
+    throughout: one position in 128 closes a window (a chunked prefill), then one in eight, then
+    every position (10,000 tokens), then one in 128 again.  The staged schedule's workgroups
+    start their count pass at different chunks and keep all 625 chunks' gate masks; every
+    workgroup must derive the same ranks from them, so each passing token is written once, by
+    one workgroup: every record agrees with the oracle and nothing else is written."""
+    T = 160000
+    wl = synth.shared_pool_batch("gate density regions", 5700, T, 2048, 8, 64, T // 64 + 1, 1024)
+    rng = np.random.default_rng(5700)
+    t = np.arange(T)
+    u = rng.random(T)
+    keep = np.where(t < 40000, u < 1 / 128, np.where(t < 120000, u < 1 / 8,
+                                                     np.where(t < 130000, True, u < 1 / 128)))
+    wl.positions[~keep] -= rng.integers(1, 128, int((~keep).sum())).astype(np.int32)
+    wl.slot_mapping[rng.random(T) < 0.2] = -1
+    rep, *_ = check(wl, label="staged gate density regions T=160000")
+    assert rep["written"] == int(wl.written_mask().sum()) > 10000
+
+
 # ---------------------------------------------------------------- compacted schedule (varlen)
 
 def check_varlen(wl, label, debug=True):
@@ -604,6 +624,30 @@ def test_plain_entry_point_on_the_scattered_batch():
     print(rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
     assert rep["written"] == int(wl.written_mask().sum()) > 1500
+
+
+def test_large_chunked_prefill_both_schedules():
+    """A 32-request chunked prefill of 246,933 tokens, 1,730 of them closing a window, with
+    distinct windows in a 4.3 GB pool: the plain entry point (the staged schedule, 965 chunks of
+    gate masks) and the compacted schedule write the same records, and the oracle, run on the
+    tokens that close a window, fixes every record and every byte that must stay untouched."""
+    import dataclasses
+    wl = synth.large_prefill()
+    announce("large chunked prefill T=246933 (plain entry point)")
+    plain, _, ok_plain = run_gpu(wl, debug=False)
+    announce("large chunked prefill T=246933 (compacted schedule)")
+    body, _, ok_varlen = run_gpu(wl, debug=False, varlen=True)
+    assert ok_plain and ok_varlen
+    act = np.nonzero(wl.active_mask())[0]
+    sub = dataclasses.replace(wl, token_to_req=wl.token_to_req[act], positions=wl.positions[act],
+                              slot_mapping=wl.slot_mapping[act],
+                              kv_slot_mapping=wl.kv_slot_mapping[act])
+    orc = oracle.run(sub, THREADS)
+    for got in (plain, body):
+        rep = compare(sub, got, orc)
+        print(rep.summary(), flush=True)
+        assert rep.ok(), rep.summary()
+        assert rep["written"] == int(wl.written_mask().sum()) > 1500
 
 
 def compare_token_range(wl, body, lo, hi):
