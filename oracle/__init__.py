@@ -49,11 +49,14 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle library.  ``DSV4_ORACLE_LIB`` names another build of the same source
+    (the mutation tests load deliberately broken copies through it)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("DSV4_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         i64, vp, dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
         L.oracle_c128_compress_store.argtypes = [
             vp, i64, i64, i64, i64,          # state, n blocks, state bs, s0, s1

@@ -26,6 +26,23 @@ def build_handworked():
                           kc_base)
 
 
+DOUBLE_ROUNDING_W = 1.0 + 2.0 ** -4 + 2.0 ** -10  # exact in fp32
+
+
+def build_double_rounding():
+    """The hand-worked input with every rms weight 1 except the first quantisation block, where
+    w = 1 + 2^-4 + 2^-10.  Every kv row is +-1 and eps is 0, so the normalised values are
+    exactly +-w.  In the first block bf16 rounds w to 1.0625, the block's UE8M0 exponent is -8
+    (absmax 1.0625 over 448 lies in (2^-9, 2^-8]) and 1.0625 * 2^8 = 272 falls midway between the
+    E4M3 neighbours 256 and 288: ties go to the even code, 256 (0x78, 0xF8 negative).  Coded from
+    the fp32 value without the bf16 step, 272.25 would round to 288 (0x79)."""
+    wl = build_handworked()
+    w = np.ones(512, np.float32)
+    w[:64] = DOUBLE_ROUNDING_W
+    wl.rms_w = w
+    return wl
+
+
 def expected_record():
     scales, codes, rope = [], [], []
     for line in open(os.path.join(HERE, "c128_handworked.txt")):

@@ -453,6 +453,22 @@ def test_fanout_gate_and_bad_indices():
     assert np.isnan(comp[:2]).all() and np.isnan(comp[4]).all() and np.isfinite(comp[2]).all()
 
 
+def test_quant_rounds_through_bf16_first():
+    """The kernel codes the bf16 value of each normalised value, as the oracle does: on
+    build_double_rounding's input (tests/golden/handworked.py) the first quantisation block's
+    values are exactly +-(1 + 2^-4 + 2^-10), whose bf16 value lands on an E4M3 midpoint after the
+    block's scale; the codes are the even neighbour, 0x78 / 0xF8."""
+    from tests.golden.handworked import build_double_rounding
+    wl = build_double_rounding()
+    announce("bf16 before the E4M3 codes")
+    body, comp, guards_ok = run_gpu(wl, debug=True)
+    assert guards_ok
+    rep = compare(wl, body, oracle.run(wl, 1), gpu_compressed=comp)
+    assert rep.ok(), rep.summary()
+    rec = body[:448]  # kv slot 0 of the first block
+    assert np.array_equal(rec, np.where(np.arange(448) % 3 == 0, 0x78, 0xF8).astype(np.uint8))
+
+
 # ---------------------------------------------------------------- staged schedule (large batches)
 
 def shared(T, seed):

@@ -474,6 +474,22 @@ def test_negative_kv_slot_writes_nothing():
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
+def test_quant_rounds_through_bf16_first():
+    """The quantiser takes the bf16 value of each normalised fp32 value before the block's
+    absmax and codes (the API page, FP8 UE8M0 quant block).  On the input of
+    tests/golden/handworked.py's build_double_rounding the first block's values are exactly
+    +-(1 + 2^-4 + 2^-10): through bf16 they code to 256 * sign (0x78 / 0xF8, the even neighbour
+    of the midpoint 272), with scale byte 127 - 8.  The other blocks (w = 1) give the same codes
+    and exponent."""
+    from tests.golden.handworked import build_double_rounding
+    wl = build_double_rounding()
+    r = oracle.run(wl, 1)
+    codes, sc, _ = decode_record(r.k_cache, int(wl.kv_slot_mapping[0]))
+    sign = np.arange(448) % 3 == 0
+    assert np.array_equal(codes, np.where(sign, 0x78, 0xF8).astype(np.uint8))
+    assert list(sc[:7]) == [119] * 7
+
+
 def test_handworked_golden_record():
     """Hand-derived record (tests/golden/c128_handworked.txt): kv = +-1 per column, w a power of
     two per quant block, eps = 0, position 127."""
