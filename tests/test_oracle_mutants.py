@@ -70,6 +70,9 @@ MUTANTS = [
     M("eps added outside the square root",
       [("1.0 / sqrt(ss / H + a->eps)", "1.0 / (sqrt(ss / H) + a->eps)")],
       [f"{PINS}::test_rmsnorm_weight_and_eps"]),
+    M("RMSNorm divides by the mean square, not its root",
+      [("double rrms = 1.0 / sqrt(ss / H + a->eps);", "double rrms = 1.0 / (ss / H + a->eps);")],
+      [f"{PINS}::test_record_invariant_under_power_of_two_kv_scaling"]),
     M("RMSNorm weight not applied",
       [("n[j] = c[j] * rrms * (double)a->rms_w[j];", "n[j] = c[j] * rrms;")],
       [f"{PINS}::test_rmsnorm_weight_and_eps"]),
@@ -78,6 +81,10 @@ MUTANTS = [
       [("for (int j = 0; j < NOPE; ++j) u[j] = oracle_bf16_value(oracle_bf16_bits((double)(float)n[j]));",
         "for (int j = 0; j < NOPE; ++j) u[j] = (double)(float)n[j];")],
       [f"{PINS}::test_quant_rounds_through_bf16_first"]),
+    M("absmax without the absolute value",
+      [("    for (int j = g * QBLOCK; j < (g + 1) * QBLOCK; ++j)\n      if (fabs(u[j]) > amax) amax = fabs(u[j]);",
+        "    for (int j = g * QBLOCK; j < (g + 1) * QBLOCK; ++j)\n      if (u[j] > amax) amax = u[j];")],
+      [f"{PINS}::test_quant_invariants_on_random_windows"]),
     M("floor(log2) instead of ceil(log2)",
       [("return (f == 0.5) ? k - 1 : k;", "return k - 1;")],
       [f"{PINS}::test_ue8m0_exponent_exact_for_every_bf16_absmax"]),

@@ -265,6 +265,57 @@ def test_shift_invariance_of_the_pool():
 
 # ---------------------------------------------------------------- addressing
 
+def test_pool_is_a_convex_combination_of_the_window():
+    """Every pooled value lies between the smallest and the largest kv value of its column over
+    the window's 128 rows (the softmax weights are positive and sum to one), with score spreads
+    from near-uniform (std 0.01) to near one-hot (std 100)."""
+    for seed, std in ((31, 0.01), (32, 1.0), (33, 100.0)):
+        wl = small_decode(T=3, seed=seed, score_std=std)
+        r = oracle.run(wl, 1)
+        for t in range(wl.num_tokens):
+            assert r.status[t] == 1
+            kv = window_rows(wl, t)[:, :512].astype(np.float64)
+            lo, hi = kv.min(0), kv.max(0)
+            slack = 1e-12 * np.maximum(np.abs(lo), np.abs(hi))
+            c = r.compressed[t]
+            assert np.all(c >= lo - slack) and np.all(c <= hi + slack)
+            assert np.any(c > lo + 1e-6) and np.any(c < hi - 1e-6)  # not a corner row
+
+
+def test_record_invariant_under_power_of_two_kv_scaling():
+    """With eps = 0, multiplying every kv value by 2^k multiplies the pooled values by exactly
+    2^k, and RMSNorm divides it out again (every step is exact under power-of-two scaling): the
+    records are byte-identical for k from -20 to 20."""
+    def run(k):
+        wl = small_decode(T=4, seed=41)
+        wl.eps = 0.0
+        wl.state[:, :, :512] *= np.float32(2.0 ** k)
+        return oracle.run(wl, 1)
+    base = run(0)
+    assert (base.status == 1).all()
+    for k in (-20, -3, 1, 7, 20):
+        assert np.array_equal(run(k).k_cache_base, base.k_cache_base), k
+
+
+def test_pool_invariant_under_permuting_window_rows():
+    """Moving whole state rows (kv with its score) to other places inside a token's own window
+    blocks leaves every record unchanged: the pooling is a sum over the window's rows, in any
+    order (fp64 sums in another order differ in the last bits, far below any rounding of the
+    record)."""
+    wl = small_decode(T=3, seed=51)
+    r0 = oracle.run(wl, 1)
+    for t in range(wl.num_tokens):
+        pos, req = int(wl.positions[t]), int(wl.token_to_req[t])
+        slots = [(int(wl.block_table[req, q // 8]), q % 8) for q in range(pos - 127, pos + 1)]
+        rows = np.stack([wl.state[b, i].copy() for b, i in slots])
+        perm = synth.permutation(128, 52, t)
+        for (b, i), src in zip(slots, perm):
+            wl.state[b, i] = rows[src]
+    r1 = oracle.run(wl, 1)
+    assert np.array_equal(r1.k_cache_base, r0.k_cache_base)
+    np.testing.assert_allclose(r1.compressed, r0.compressed, rtol=0, atol=1e-13)  # |kv| <= ~5
+
+
 def test_physical_relocation_invariance():
     """Permuting the pool's physical blocks and remapping the block table gives identical
     k_cache bytes."""
