@@ -159,7 +159,17 @@ MUTANTS = [
       [("r[IDX_NOPE + 2 * m] = x * C - y * S;", "r[IDX_NOPE + 2 * m] = x * C + y * S;", 0),
        ("r[IDX_NOPE + 2 * m + 1] = y * C + x * S;", "r[IDX_NOPE + 2 * m + 1] = y * C - x * S;", 0)],
       [f"{PINS_IDX}::test_indexer_rope_against_complex_multiply"]),
+    M("indexer records and scales interleaved per token",
+      [("uint8_t* data = blockp + koff * IDX_RECORD;",
+        "uint8_t* data = blockp + koff * (IDX_RECORD + IDX_SCALE);"),
+       ("uint8_t* scale = blockp + a->kv_bs * IDX_RECORD + koff * IDX_SCALE;",
+        "uint8_t* scale = blockp + koff * (IDX_RECORD + IDX_SCALE) + IDX_RECORD;")],
+      [f"{PINS_IDX}::test_indexer_insert_byte_offsets"]),
     # indexer MXFP4
+    M("MXFP4 one exponent for all 128 dims",
+      [("    for (int j = g * FP4_BLOCK; j < (g + 1) * FP4_BLOCK; ++j)\n      if (fabs(u[j]) > amax)",
+        "    for (int j = 0; j < IDX_HEAD; ++j)\n      if (fabs(u[j]) > amax)")],
+      [f"{PINS_FP4}::test_mxfp4_one_hot_record"]),
     M("MXFP4 odd dim in the low nibble",
       [("data[j / 2] = (uint8_t)(lo | (hi << 4));", "data[j / 2] = (uint8_t)(hi | (lo << 4));")],
       [f"{PINS_FP4}::test_mxfp4_one_hot_record"]),
