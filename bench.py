@@ -315,9 +315,10 @@ def cpu_baseline(wl, gpu_body, nbytes, gpu_compressed=None):
 def range_sweep(args):
     """The metric's token range in the bench line: cold calls (a 1 GiB read before each one
     evicts the L2s and the MALL) of decode batches of 1, 128 and 1024 tokens on the decode
-    sweep's 65536-block pool and of the varlen prefill workload, each on the plain entry point
-    and on the fastest entry point for that batch; median over the calls, per-call event time
-    on the launch stream."""
+    sweep's 65536-block pool, of a 1024-request decode step in which one token in 128 closes a
+    window, and of the varlen prefill workload, each on the plain entry point and on the fastest
+    entry point for that batch; median over the calls, per-call event time on the launch
+    stream."""
     import torch
 
     import paged_kv_cache_fp32_amd as c128
@@ -334,9 +335,10 @@ def range_sweep(args):
         torch.sum(scratch, dim=0, out=sink)
 
     def entry(dws, kind):
-        if kind == "fan-out":
-            wss = [c128.fanout_workspace(d.wl.num_tokens, 0, dev) for d in dws]
-            return [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w, splits=0,
+        if kind.startswith("fan-out"):  # "fan-out": automatic split count, "fan-out N": N
+            sp = int(kind.split()[1]) if " " in kind else 0
+            wss = [c128.fanout_workspace(d.wl.num_tokens, sp, dev) for d in dws]
+            return [(lambda d=d, w=w: c128.compress_store_ex(*d.args(), workspace=w, splits=sp,
                                                              stream=sid))
                     for d, w in zip(dws, wss)]
         if kind == "compacted":
@@ -375,6 +377,14 @@ def range_sweep(args):
             dws.append(d)
         measure(f"decode T={T}", dws, ["plain"] + ([best] if best else []))
         del dws
+    dws = []
+    for s in range(4):
+        d = DeviceWorkload(synth.decode_step(1024, state=pool, window_set=s), device=dev,
+                           state=pool_dev)
+        pool_dev = (d.state_buf, d.state)
+        dws.append(d)
+    measure("decode step T=1024, 1 in 128 active", dws, ["plain", "fan-out 4"])
+    del dws
     del pool, pool_dev
     torch.cuda.empty_cache()
     d2 = DeviceWorkload(synth.config2(), device=dev)
@@ -969,8 +979,8 @@ def main():
     ap.add_argument("--sweep", default=None, help="write per-workload JSONL to this path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-range", action="store_true",
-                    help="leave out the cold token-range points (decode 1/128/1024 tokens, "
-                         "varlen prefill) of the bench line")
+                    help="leave out the cold token-range points (decode 1/128/1024 tokens, a "
+                         "1024-request decode step, varlen prefill) of the bench line")
     ap.add_argument("--range-steps", type=int, default=30,
                     help="cold calls per token-range point")
     ap.add_argument("--sweep-filter", default=None,

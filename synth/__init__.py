@@ -616,6 +616,20 @@ def config3(num_tokens: int, state=None, window_set: int = 0) -> Workload:
                         window_set=window_set, pool_seed=SEED_BASE + 3)
 
 
+def decode_step(num_tokens: int, state=None, window_set: int = 0) -> Workload:
+    """A decode step as a serving loop sees it: the decode sweep's batch of ``num_tokens``
+    requests, of which about one in 128 (a seeded draw, at least one) has its new token close a
+    window; every other token sits one position before its window's end."""
+    wl = config3(num_tokens, state=state, window_set=window_set)
+    T = num_tokens
+    pick = permutation(T, SEED_BASE + 7 + window_set, 0)[:max(1, T // 128)]
+    keep = np.zeros(T, bool)
+    keep[pick] = True
+    wl.positions[~keep] -= 1
+    wl.name = f"decode step T={T}"
+    return wl
+
+
 def config4(threads: int | None = None) -> Workload:
     """16384 boundary tokens over a 262144-block (8.59 GB) pool; every block read once;
     score windows mix N(0,1) and near-constant; KV block size 64, 256 blocks."""

@@ -28,3 +28,20 @@ def test_world_size_above_one_is_refused():
 def test_steps_must_be_positive():
     out = run("--steps", "0")
     assert out.returncode != 0 and "--steps" in out.stderr
+
+
+def test_decode_step_workload():
+    """The decode step of the bench line: max(1, T // 128) tokens close a window, every other
+    token sits one position before its window's end, and the batch is the decode sweep's."""
+    import numpy as np
+
+    import synth
+    _, pool = synth.config3_pool()
+    for T in (1, 100, 1024):
+        wl = synth.decode_step(T, state=pool)
+        full = synth.config3(T, state=pool)
+        act = wl.active_mask()
+        assert int(act.sum()) == max(1, T // 128)
+        assert np.array_equal(wl.positions[act], full.positions[act])
+        assert np.array_equal(wl.positions[~act], full.positions[~act] - 1)
+        assert np.all(wl.positions[~act] % 128 == 126)
