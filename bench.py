@@ -567,6 +567,22 @@ def sweep(args, path):
             for sp in ([0, 2, 4, 8, 16] if args.sweep_splits else [0]):
                 measure(f"cfg3 decode sweep T={T}", dws, 1000, splits=sp)
         del dws
+    for T in (128, 256, 1024, 2048, 4096):
+        if not want(f"decode step T={T}"):
+            continue
+        if pool is None:
+            _, pool = synth.config3_pool()
+        dws = []
+        for s in range(min(4, 65536 // (16 * T))):
+            d = DeviceWorkload(synth.decode_step(T, state=pool, window_set=s), device=dev,
+                               state=pool_dev)
+            pool_dev = (d.state_buf, d.state)
+            dws.append(d)
+        measure(f"decode step T={T}", dws, 300)
+        for sp in (2, 4, 8):
+            measure(f"decode step T={T}", dws, 300, splits=sp)
+        measure(f"decode step T={T}", dws, 300, varlen=True)
+        del dws
     del pool, pool_dev
     torch.cuda.empty_cache()
     c4_sweep(want, measure, dev)
