@@ -107,3 +107,47 @@ def test_noalloc_rejects_more_tokens_than_its_scratch_holds():
     assert e.value.code == -8 and "at most 1048576" in str(e.value)
     torch.cuda.synchronize()
     assert torch.equal(before, d.kc_buf)
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free call captured into a HIP graph: each replay, with an eager call on
+    another batch run between replays (it rewrites the shared scratch with other counts and
+    another token list), gives the bytes of the eager call.  The scratch address is looked up
+    by an eager call before capture, as the header asks."""
+    import paged_kv_cache_fp32_amd as c128
+    a = DeviceWorkload(synth.varlen_prefill("no-alloc graph", 1208, 8, 600, 1024, 8 * 208,
+                                            kv_bs=64, cs_rows=2048))
+    b_wl = synth.varlen_prefill("no-alloc graph, other batch", 1209, 16, 700, 2048, 8192,
+                                kv_bs=16, cs_rows=4096)
+    b = DeviceWorkload(b_wl)
+    b_initial = b.kc_buf.clone()
+    c128.compress_store_varlen_noalloc(*b.args())
+    torch.cuda.synchronize()
+    b_eager = b.kc_buf.clone()
+    announce("no-alloc under graph capture")
+
+    a_initial = a.kc_buf.clone()
+    c128.compress_store_varlen_noalloc(*a.args())
+    torch.cuda.synchronize()
+    a_eager = a.kc_buf.clone()
+    assert not torch.equal(a_eager, a_initial)
+    a.kc_buf.copy_(a_initial)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        c128.compress_store_varlen_noalloc(*a.args())  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c128.compress_store_varlen_noalloc(*a.args())
+    for i in range(3):
+        b.kc_buf.copy_(b_initial)
+        c128.compress_store_varlen_noalloc(*b.args())
+        torch.cuda.synchronize()
+        assert torch.equal(b.kc_buf, b_eager), f"eager call {i} on the other batch differs"
+        a.kc_buf.copy_(a_initial)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a.kc_buf, a_eager), f"replay {i} differs from the eager call"
