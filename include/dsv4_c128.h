@@ -55,7 +55,10 @@
  *   kv_slot_mapping i32 [T]            contiguous
  *
  * Calls are stream-ordered and asynchronous: no host synchronisation and no
- * device-to-host reads.  T == 0 is a valid no-op.
+ * device-to-host reads.  T == 0 is a valid no-op.  Calls keep no device state
+ * of the library's own between calls (except dsv4_c128_compress_store_varlen_noalloc,
+ * below), so calls on different streams may overlap when they share no output
+ * and no workspace.
  *
  * Errors.  Entry points return DSV4_OK (0) or a negative DSV4_ERR_* code.  On
  * any validation error nothing is launched and k_cache is untouched;
